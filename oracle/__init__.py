@@ -1,0 +1,11 @@
+"""CPU oracle of the streaming decode step.
+
+TEST INFRASTRUCTURE ONLY: a plain, slow, float32 NumPy implementation written from the pages'
+definitions.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it; the HIP path never does, and this package imports nothing from it.
+"""
+from .step import (  # noqa: F401
+    F32, INVALID_POS, NORM_LAYER, NORM_RMS, ROPE_HALF, ROPE_INTERLEAVED, FFN_GELU, FFN_SWIGLU,
+    OracleDecoder, apply_rope, attend, gelu_erf, gemv, layer_norm, rms_norm, rope_cos_sin,
+    rope_pairs, seq_sum, silu_mul, valid_slots,
+)
