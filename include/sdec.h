@@ -1,0 +1,182 @@
+/*
+ * sdec — one autoregressive decode step of a streaming transformer on MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; every device pointer is a HIP device address, every
+ * stream a hipStream_t passed as void*.  The method these calls implement is the one the
+ * docs.rs inferencelayer pages describe:
+ *   [talker] inferencelayer 0.2.8, src/qwen3tts_gpu.rs — TalkerGpu::load / new_state / step
+ *            and the build_step_plan pass list (RMSNorm, q/k/v GEMVs, per-head qk-RMSNorm,
+ *            rotate_half rope, KV append, GQA causal attention, o GEMV + residual, RMSNorm,
+ *            SwiGLU FFN, down GEMV + residual, final RMSNorm);
+ *   [mimi]   inferencelayer 0.2.1, src/mimi_gpu.rs — TrShape, Builder::transformer_shaped
+ *            (LayerNorm, packed qkv GEMV, rope fused with the KV-ring push, windowed ring
+ *            attention, GEMVs with LayerScale folded into the residual, GELU), reset;
+ *   [pocket] inferencelayer 0.2.4, src/pocket_tts_gpu.rs — PocketBackboneGpu::load_voice
+ *            (importing a K/V cache into the rings), step (ring capacity check), reset.
+ *
+ * Errors: every int-returning call returns SDEC_OK (0) or a negative code; the message of the
+ * last failure on the calling thread is in sdec_last_error().  All argument checks run on the
+ * host before anything is enqueued; on error no GPU work is enqueued and the handle's state is
+ * unchanged.
+ */
+#ifndef SDEC_H
+#define SDEC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SDEC_OK = 0,
+  SDEC_E_ARG = -1,      /* null pointer, bad configuration, misaligned pointer, bad m */
+  SDEC_E_POS = -2,      /* pos is not the next position while first == 0 ([talker] step:
+                           positions must be contiguous) */
+  SDEC_E_CAPACITY = -3, /* an unbounded stack got a position past its ring ([talker] step:
+                           cache length past max_pos; [pocket] PocketBackboneGpu::step) */
+  SDEC_E_HIP = -4,      /* a HIP runtime call failed; the message carries hipGetErrorString */
+  SDEC_E_NOMEM = -5     /* device allocation failed */
+};
+
+enum { SDEC_NORM_RMS = 0, SDEC_NORM_LAYER = 1 };
+enum { SDEC_ROPE_HALF = 0, SDEC_ROPE_INTERLEAVED = 1 };
+enum { SDEC_FFN_SWIGLU = 0, SDEC_FFN_GELU_ERF = 1 };
+
+/* sdec_config.flags */
+#define SDEC_FLAG_EAGER 1u /* launch kernels one by one per step instead of replaying a graph */
+#define SDEC_FLAG_TAPS 2u  /* keep per-layer branch outputs readable through sdec_tap_view */
+
+/* Geometry and options of one decoder stack ([talker] Dims; [mimi] TrShape). */
+typedef struct sdec_config {
+  uint32_t n_layers;
+  uint32_t d_model;     /* hidden width; multiple of 4 */
+  uint32_t n_q_heads;
+  uint32_t n_kv_heads;  /* divides n_q_heads; q-head h reads kv head h / (n_q_heads/n_kv_heads) */
+  uint32_t head_dim;    /* 64 or 128 ([talker] load: head_dim <= 128) */
+  uint32_t d_ff;        /* FFN width; multiple of 4 */
+  uint32_t m;           /* independent streams stepped in lockstep, 1..8 */
+  uint32_t norm;        /* SDEC_NORM_RMS (x/sqrt(mean x^2+eps)*g) or SDEC_NORM_LAYER (two-pass) */
+  float norm_eps;
+  uint32_t qk_norm;     /* nonzero: per-head RMSNorm of q and k before rope ([talker] QK_NORM_SRC) */
+  float qk_norm_eps;
+  uint32_t rope;        /* SDEC_ROPE_HALF: pairs (j, j+hd/2); SDEC_ROPE_INTERLEAVED: (2j, 2j+1) */
+  double rope_theta;    /* angle of pair j at position p: p * theta^(-2j/head_dim) */
+  uint32_t ffn;         /* SDEC_FFN_SWIGLU (silu(Wg n) * (Wu n)) or SDEC_FFN_GELU_ERF (gelu(W1 n)) */
+  uint32_t layer_scale; /* nonzero: residual adds are x += ls (*) branch ([mimi] MV_LS) */
+  uint32_t final_norm;  /* nonzero: the output is norm(x) with the final weights, else x itself */
+  uint32_t window;      /* a key at position p is legal for the query at pos iff
+                           p <= pos and pos - p < window ([mimi] attn_src); 1 <= window <= ring */
+  uint32_t unbounded;   /* nonzero: the stack refuses pos >= ring_slots instead of wrapping
+                           (the talker's cache and the FlowLM ring); requires window == ring */
+  uint32_t flags;       /* SDEC_FLAG_* */
+} sdec_config;
+
+/* One layer's parameters: device pointers, float32, borrowed (the caller keeps them alive and
+ * unchanged until sdec_destroy; the library never copies or frees them).  Matrices are
+ * row-major [n_out, k] ([talker] MATVEC_SRC: W stored [n,k], no transpose), 16-byte aligned.
+ * A field the configuration does not use may be NULL. */
+typedef struct sdec_layer_weights {
+  const float* attn_norm_w; /* [d_model] pre-attention norm gain */
+  const float* attn_norm_b; /* [d_model] LayerNorm bias (NORM_LAYER only) */
+  const float* wq;          /* [n_q_heads*head_dim, d_model] */
+  const float* wk;          /* [n_kv_heads*head_dim, d_model] */
+  const float* wv;          /* [n_kv_heads*head_dim, d_model]; a packed in_proj [q;k;v] passes
+                               in_proj, in_proj + qw*d, in_proj + (qw+kw)*d ([mimi] rope_push_src) */
+  const float* wo;          /* [d_model, n_q_heads*head_dim] */
+  const float* q_norm;      /* [head_dim] (qk_norm only) */
+  const float* k_norm;      /* [head_dim] (qk_norm only) */
+  const float* ls1;         /* [d_model] LayerScale of the attention branch (layer_scale only) */
+  const float* ffn_norm_w;  /* [d_model] */
+  const float* ffn_norm_b;  /* [d_model] (NORM_LAYER only) */
+  const float* w_gate;      /* [d_ff, d_model] (SwiGLU only) */
+  const float* w_up;        /* [d_ff, d_model]: SwiGLU up projection, or the GELU FFN's W1 */
+  const float* w_down;      /* [d_model, d_ff] */
+  const float* ls2;         /* [d_model] LayerScale of the FFN branch (layer_scale only) */
+} sdec_layer_weights;
+
+typedef struct sdec_final_weights {
+  const float* norm_w; /* [d_model] (final_norm only) */
+  const float* norm_b; /* [d_model] (final_norm with NORM_LAYER only) */
+} sdec_final_weights;
+
+typedef struct sdec_handle sdec_handle;
+
+/* Build a stack: validate the configuration, allocate the K/V rings ([m][n_layers][ring_slots]
+ * [n_kv_heads][head_dim] float32 each, zeroed), one position ring per stream ([m][ring_slots]
+ * uint32, every slot 0xFFFFFFFF = empty, [mimi] INVALID_POS), the scratch buffers, and record
+ * the per-token launch sequence as a hipGraph.  `layers` points to n_layers structs (host
+ * memory, read during the call).  Synchronous; *out is set only on success. */
+int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
+                const sdec_final_weights* final_weights, uint32_t ring_slots,
+                sdec_handle** out);
+
+/* One decode step of every stream at position `pos` ([talker] TalkerGpu::step; [mimi] the
+ * per-frame (pos, first) uniform).  x: device [m][d_model] float32, read as the step's input
+ * rows and overwritten in place with the output rows (the final-norm hidden state, or the
+ * residual stream when the stack has no final norm).  first != 0 starts fresh streams: every
+ * position ring is invalidated before the step.  With first == 0, pos must equal the previous
+ * step's pos + 1 (or the position set by sdec_set_next_position).  Asynchronous: enqueues on
+ * `stream` and returns; x must stay valid until the work completes. */
+int sdec_step(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stream);
+
+/* Fresh session on `stream`: zero the K/V rings, set every position-ring slot to empty and
+ * forget the next position ([mimi] MimiGpu::reset; [pocket] PocketCodecGpu::reset). */
+int sdec_reset(sdec_handle* h, void* stream);
+
+/* Release every buffer the library owns and the graph.  Synchronizes the device first.
+ * NULL is accepted. */
+void sdec_destroy(sdec_handle* h);
+
+/* Message of the last failed call on this thread ("" if none).  Valid until the next call. */
+const char* sdec_last_error(void);
+
+/* Device pointers of stream `stream_idx`'s rings for `layer`: *k and *v are [ring_slots]
+ * [n_kv_heads][head_dim] float32 (keys already roped), *pos_ring is [ring_slots] uint32 and is
+ * shared by every layer of the stream.  Writing them imports a cache ([pocket] load_voice: the
+ * [positions][heads][head_dim] cache layout is the ring's slot-major layout); follow with
+ * sdec_set_next_position.  Any output pointer may be NULL. */
+int sdec_kv_view(sdec_handle* h, uint32_t stream_idx, uint32_t layer, float** k, float** v,
+                 uint32_t** pos_ring);
+
+/* Declare the position the next step (with first == 0) must carry, after an import through
+ * sdec_kv_view ([pocket] load_voice sets the clock to the imported length). */
+int sdec_set_next_position(sdec_handle* h, uint32_t next_pos);
+
+/* With SDEC_FLAG_TAPS: device pointer of a per-layer branch output of the latest step,
+ * [m][width] float32.  which = 0: attention output before the o projection (width
+ * n_q_heads*head_dim); 1: o projection output before LayerScale and the residual add;
+ * 2: FFN down projection output before LayerScale and the residual add (width d_model). */
+int sdec_tap_view(sdec_handle* h, uint32_t layer, uint32_t which, float** ptr);
+
+/* Per-kernel timing of one eager step: runs the step like sdec_step (same checks, same state
+ * update) with a hipEvent pair around every launch, waits for it, and adds each launch's
+ * milliseconds into ms[kind] and 1 into calls[kind] (kind = SDEC_K_*; arrays of SDEC_K_COUNT). */
+enum {
+  SDEC_K_BEGIN = 0, SDEC_K_QKV = 1, SDEC_K_QK_ROPE_PUSH = 2, SDEC_K_ATTENTION = 3, SDEC_K_O = 4,
+  SDEC_K_FFN_UP = 5, SDEC_K_FFN_DOWN = 6, SDEC_K_END = 7, SDEC_K_COUNT = 8
+};
+int sdec_step_profile(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stream,
+                      double* ms, uint32_t* calls);
+
+/* One-shot GEMV, the step's weight-streaming kernel on its own ([talker] MATVEC_SRC):
+ * y[r][i] = sum_j x[r][j] * w[i][j] for r < m (1..8), i < n, with w row-major [n][k]
+ * (k a multiple of 4, w and x 16-byte aligned), x [m][k], y [m][n]; all device float32. */
+int sdec_gemv(const float* w, const float* x, float* y, uint32_t n, uint32_t k, uint32_t m,
+              void* stream);
+
+/* One-shot ring attention ([mimi] attn_src with [talker] GQA_ATTN_SRC's head mapping) for m
+ * streams at query position pos: q [m][n_q_heads*head_dim]; k_ring, v_ring [m][ring_slots]
+ * [n_kv_heads][head_dim]; pos_ring [m][ring_slots]; out [m][n_q_heads*head_dim].  Slot j is
+ * legal iff pos_ring[j] != 0xFFFFFFFF, pos_ring[j] <= pos and pos - pos_ring[j] < window; a
+ * head with no legal slot gets zeros.  head_dim is 64 or 128; all device memory. */
+int sdec_ring_attention(const float* q, const float* k_ring, const float* v_ring,
+                        const uint32_t* pos_ring, float* out, uint32_t m, uint32_t n_q_heads,
+                        uint32_t n_kv_heads, uint32_t head_dim, uint32_t ring_slots,
+                        uint32_t window, uint32_t pos, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDEC_H */

@@ -1,0 +1,119 @@
+// Internal interface between the C-ABI host code (sdec.cpp) and the HIP kernels (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdec {
+
+constexpr uint32_t kInvalidPos = 0xFFFFFFFFu;
+constexpr int kMaxM = 8;
+constexpr int kWgThreads = 256;  // four wave64s
+
+// Per-step device state written by the step-begin kernel and read by the layer kernels, so a
+// recorded graph stays valid for every position.
+struct DevState {
+  uint32_t pos;
+  uint32_t slot;
+};
+
+enum GemvPrologue : int { PRO_NONE = 0, PRO_RMS = 1, PRO_LN = 2 };
+enum GemvEpilogue : int { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2, EPI_GELU = 3 };
+
+// y = x . W^T over up to three row segments (q, k, v share one launch).  With EPI_SWIGLU the
+// launch covers `n_rows` FFN indices, reading rows of w[0] (gate) and w[1] (up).
+struct GemvArgs {
+  const float* w[3];
+  uint32_t seg_end[3];  // cumulative row counts of the segments
+  uint32_t n_rows;
+  uint32_t k;
+  uint32_t m;            // valid input rows (streams)
+  const float* x;        // [m][x_stride]
+  uint32_t x_stride;
+  const float* norm_w;   // prologue gain
+  const float* norm_b;   // prologue bias (LayerNorm)
+  float eps;
+  float* y;              // EPI_STORE / EPI_SWIGLU / EPI_GELU output, [m][y_stride]
+  uint32_t y_stride;
+  float* res;            // EPI_RESIDUAL target, [m][res_stride], updated in place
+  uint32_t res_stride;
+  const float* ls;       // LayerScale or null
+  float* tap;            // optional copy of the raw branch, [m][tap_stride]
+  uint32_t tap_stride;
+};
+
+struct GemvLaunch {
+  int prologue;
+  int epilogue;
+  int rows_per_wave;  // R: rows one wave reduces together
+  int waves_per_wg;
+  uint32_t grid;      // workgroups
+};
+
+hipError_t launch_gemv(const GemvArgs& a, const GemvLaunch& l, hipStream_t s);
+// A launch shape for this GEMV on this device (grid sized to the row tiles).
+GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, uint32_t m);
+
+struct QkRopeArgs {
+  const float* qkv;      // [m][qkv_stride]: q (Hq*hd), k (Hkv*hd), v (Hkv*hd)
+  uint32_t qkv_stride;
+  float* q_out;          // [m][Hq*hd] normed + roped queries
+  float* k_ring;         // this layer's K ring of stream 0: [R][Hkv][hd]
+  float* v_ring;
+  uint64_t ring_stream_stride;  // floats between consecutive streams' rings
+  uint32_t n_q_heads, n_kv_heads, head_dim, m;
+  const float* q_norm;   // null: no qk-norm
+  const float* k_norm;
+  float eps;
+  int rope_style;        // 0 rotate_half, 1 interleaved
+  const float* cs;       // [hd/2] cos then [hd/2] sin for this step's position
+  const DevState* st;
+};
+hipError_t launch_qk_rope_push(const QkRopeArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const float* q;        // [m][Hq*hd]
+  const float* k_ring;   // stream 0 of this layer: [R][Hkv][hd]
+  const float* v_ring;
+  uint64_t ring_stream_stride;
+  const uint32_t* pos_ring;  // [m][R]
+  uint32_t pos_stream_stride;
+  float* out;            // [m][Hq*hd]
+  float* part;           // [m][Hq][n_chunks][hd + 2] chunk partials
+  uint32_t* counters;    // [m][Hkv], zero between launches (the last chunk resets it)
+  uint32_t m, n_q_heads, n_kv_heads, head_dim, ring, window, chunk, n_chunks;
+  const DevState* st;    // position source; null: use `pos`
+  uint32_t pos;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+uint32_t attention_chunk(uint32_t head_dim);
+
+struct BeginArgs {
+  const float* x_in;     // caller rows [m][d]
+  float* xres;           // residual stream [m][d]
+  uint32_t md;           // m*d
+  uint32_t* pos_rings;   // [m][R]
+  uint32_t m, ring;
+  uint32_t pos, first;
+  float* cs;             // [hd/2] cos, [hd/2] sin
+  uint32_t head_dim;
+  double theta;
+  DevState* st;
+};
+hipError_t launch_begin(const BeginArgs& a, hipStream_t s);
+
+struct EndArgs {
+  const float* xres;     // [m][d]
+  float* x_out;          // [m][d]
+  uint32_t m, d;
+  int norm;              // -1: copy, PRO_RMS or PRO_LN
+  const float* w;
+  const float* b;
+  float eps;
+};
+hipError_t launch_end(const EndArgs& a, hipStream_t s);
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, uint64_t n, hipStream_t s);
+hipError_t launch_fill_f32(float* p, float value, uint64_t n, hipStream_t s);
+
+}  // namespace sdec

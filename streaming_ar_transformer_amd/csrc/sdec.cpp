@@ -1,0 +1,592 @@
+// Host side of the sdec C ABI: argument checks, device buffers, the per-token launch sequence
+// and its hipGraph.  Page names in citations: [talker] inferencelayer 0.2.8 src/qwen3tts_gpu.rs,
+// [mimi] 0.2.1 src/mimi_gpu.rs, [pocket] 0.2.4 src/pocket_tts_gpu.rs.
+
+#include "sdec.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace sdec;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess)                                                                  \
+      return fail(SDEC_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));              \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct sdec_handle {
+  sdec_config cfg{};
+  std::vector<sdec_layer_weights> layers;
+  sdec_final_weights fin{};
+  uint32_t ring = 0;
+  uint32_t n_chunks = 0;
+  uint32_t chunk = 0;
+  int device = 0;
+
+  // library-owned device memory
+  float* k_rings = nullptr;   // [m][L][R][Hkv][hd]
+  float* v_rings = nullptr;
+  uint32_t* pos_rings = nullptr;  // [m][R]
+  float* xres = nullptr;      // [m][d]
+  float* qkv = nullptr;       // [m][(Hq+2Hkv)hd]
+  float* q_out = nullptr;     // [m][Hq hd]
+  float* attn_out = nullptr;  // [m][Hq hd], or [L][m][Hq hd] with taps
+  float* act = nullptr;       // [m][d_ff]
+  float* part = nullptr;      // [m][Hq][n_chunks][hd+2]
+  uint32_t* counters = nullptr;  // [m][Hkv]
+  float* cs = nullptr;        // [hd]
+  DevState* st = nullptr;
+  float* tap_attn_proj = nullptr;  // [L][m][d]
+  float* tap_ffn_proj = nullptr;   // [L][m][d]
+
+  uint64_t ring_stream_stride = 0;  // floats between streams in k_rings / v_rings
+  uint64_t ring_layer_stride = 0;   // floats between layers of one stream
+
+  std::vector<GemvLaunch> plan_qkv, plan_o, plan_up, plan_down;
+
+  hipStream_t cap_stream = nullptr;
+  hipGraphExec_t exec = nullptr;
+  bool graph_ready = false;
+
+  bool has_next = false;
+  uint32_t next_pos = 0;
+};
+
+namespace {
+
+struct Alloc {
+  std::vector<void*> ptrs;
+  int code = SDEC_OK;
+  template <class T>
+  T* get(size_t count) {
+    if (code != SDEC_OK) return nullptr;
+    void* p = nullptr;
+    size_t bytes = count * sizeof(T);
+    if (bytes == 0) bytes = 16;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+      code = fail(SDEC_E_NOMEM, "hipMalloc of %zu bytes failed: %s", bytes, hipGetErrorString(e));
+      return nullptr;
+    }
+    ptrs.push_back(p);
+    return static_cast<T*>(p);
+  }
+};
+
+void free_handle_memory(sdec_handle* h) {
+  void* ps[] = {h->k_rings, h->v_rings, h->pos_rings, h->xres, h->qkv, h->q_out, h->attn_out,
+                h->act, h->part, h->counters, h->cs, h->st, h->tap_attn_proj, h->tap_ffn_proj};
+  for (void* p : ps)
+    if (p) (void)hipFree(p);
+}
+
+int validate_config(const sdec_config* c, uint32_t ring) {
+  if (c->n_layers < 1) return fail(SDEC_E_ARG, "n_layers must be >= 1");
+  if (c->d_model == 0 || c->d_model % 4) return fail(SDEC_E_ARG, "d_model must be a positive multiple of 4");
+  if (c->d_ff == 0 || c->d_ff % 4) return fail(SDEC_E_ARG, "d_ff must be a positive multiple of 4");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(SDEC_E_ARG, "head_dim %u unsupported (64 or 128)", c->head_dim);
+  if (c->n_kv_heads == 0 || c->n_q_heads == 0 || c->n_q_heads % c->n_kv_heads)
+    return fail(SDEC_E_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+  const uint32_t group = c->n_q_heads / c->n_kv_heads;
+  if (group != 1 && group != 2 && group != 4)
+    return fail(SDEC_E_ARG, "GQA group %u unsupported (1, 2 or 4)", group);
+  if (c->m < 1 || c->m > kMaxM) return fail(SDEC_E_ARG, "m must be in [1, %d]", kMaxM);
+  if (c->norm > SDEC_NORM_LAYER) return fail(SDEC_E_ARG, "bad norm kind");
+  if (c->rope > SDEC_ROPE_INTERLEAVED) return fail(SDEC_E_ARG, "bad rope kind");
+  if (c->ffn > SDEC_FFN_GELU_ERF) return fail(SDEC_E_ARG, "bad ffn kind");
+  if (!(c->rope_theta > 0.0)) return fail(SDEC_E_ARG, "rope_theta must be positive");
+  if (ring < 1) return fail(SDEC_E_ARG, "ring_slots must be >= 1");
+  if (c->window < 1 || c->window > ring)
+    return fail(SDEC_E_ARG, "window %u must be in [1, ring_slots=%u]", c->window, ring);
+  if (c->unbounded && c->window != ring)
+    return fail(SDEC_E_ARG, "an unbounded stack needs window == ring_slots");
+  const uint32_t mp = c->m <= 1 ? 1 : c->m <= 2 ? 2 : c->m <= 4 ? 4 : 8;
+  if (static_cast<uint64_t>(mp) * c->d_model * sizeof(float) > 65536)
+    return fail(SDEC_E_ARG, "m=%u rows of d_model=%u exceed the 64 KiB staging tile", c->m,
+                c->d_model);
+  return SDEC_OK;
+}
+
+int check_vec(const float* p, const char* name, uint32_t layer) {
+  if (p == nullptr) return fail(SDEC_E_ARG, "layer %u: %s is NULL", layer, name);
+  if (!aligned16(p)) return fail(SDEC_E_ARG, "layer %u: %s is not 16-byte aligned", layer, name);
+  return SDEC_OK;
+}
+
+int validate_weights(const sdec_config* c, const sdec_layer_weights* L,
+                     const sdec_final_weights* fw) {
+  for (uint32_t l = 0; l < c->n_layers; ++l) {
+    const sdec_layer_weights& w = L[l];
+    int r;
+#define REQ(field) \
+  if ((r = check_vec(w.field, #field, l)) != SDEC_OK) return r;
+    REQ(attn_norm_w) REQ(wq) REQ(wk) REQ(wv) REQ(wo) REQ(ffn_norm_w) REQ(w_up) REQ(w_down)
+    if (c->norm == SDEC_NORM_LAYER) { REQ(attn_norm_b) REQ(ffn_norm_b) }
+    if (c->qk_norm) { REQ(q_norm) REQ(k_norm) }
+    if (c->layer_scale) { REQ(ls1) REQ(ls2) }
+    if (c->ffn == SDEC_FFN_SWIGLU) { REQ(w_gate) }
+#undef REQ
+  }
+  if (c->final_norm) {
+    if (!fw || !fw->norm_w || !aligned16(fw->norm_w))
+      return fail(SDEC_E_ARG, "final_norm needs a 16-byte aligned norm_w");
+    if (c->norm == SDEC_NORM_LAYER && (!fw->norm_b || !aligned16(fw->norm_b)))
+      return fail(SDEC_E_ARG, "final LayerNorm needs a 16-byte aligned norm_b");
+  }
+  return SDEC_OK;
+}
+
+// Device pointer of stream s, layer l in a ring array.
+inline float* ring_at(const sdec_handle* h, float* base, uint32_t s, uint32_t l) {
+  return base + s * h->ring_stream_stride + l * h->ring_layer_stride;
+}
+
+// Which launch of the per-layer sequence is about to be enqueued (for per-kernel timing).
+struct Hooks {
+  hipEvent_t* ev = nullptr;  // pairs
+  int* kinds = nullptr;
+  int n = 0;
+  int cap = 0;
+};
+
+int hook_pre(Hooks* k, hipStream_t s) {
+  if (!k) return SDEC_OK;
+  if (k->n >= k->cap) return fail(SDEC_E_ARG, "profile event buffer too small");
+  HIP_TRY(hipEventRecord(k->ev[2 * k->n], s));
+  return SDEC_OK;
+}
+int hook_post(Hooks* k, hipStream_t s, int kind) {
+  if (!k) return SDEC_OK;
+  HIP_TRY(hipEventRecord(k->ev[2 * k->n + 1], s));
+  k->kinds[k->n++] = kind;
+  return SDEC_OK;
+}
+
+#define LAUNCH(hooks, stream, kind, call)                                               \
+  do {                                                                                  \
+    int r_ = hook_pre(hooks, stream);                                                   \
+    if (r_ != SDEC_OK) return r_;                                                       \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess) return fail(SDEC_E_HIP, "launch of %s failed: %s", #kind,     \
+                                      hipGetErrorString(e_));                           \
+    r_ = hook_post(hooks, stream, kind);                                                \
+    if (r_ != SDEC_OK) return r_;                                                       \
+  } while (0)
+
+// The per-token launch sequence of every layer ([talker] build_step_plan; [mimi]
+// Builder::transformer_shaped), on `s`.  Position-dependent values come from h->st.
+int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk) {
+  const sdec_config& c = h->cfg;
+  const uint32_t hd = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads;
+  const uint32_t qw = hq * hd, kw = hkv * hd, nqkv = qw + 2 * kw;
+  const bool taps = (c.flags & SDEC_FLAG_TAPS) != 0;
+  const int pro = c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN;
+  for (uint32_t l = 0; l < c.n_layers; ++l) {
+    const sdec_layer_weights& w = h->layers[l];
+    // attention norm + q/k/v projections
+    GemvArgs g{};
+    g.w[0] = w.wq; g.w[1] = w.wk; g.w[2] = w.wv;
+    g.seg_end[0] = qw; g.seg_end[1] = qw + kw; g.seg_end[2] = nqkv;
+    g.n_rows = nqkv; g.k = c.d_model; g.m = c.m;
+    g.x = h->xres; g.x_stride = c.d_model;
+    g.norm_w = w.attn_norm_w; g.norm_b = w.attn_norm_b; g.eps = c.norm_eps;
+    g.y = h->qkv; g.y_stride = nqkv;
+    LAUNCH(hk, s, SDEC_K_QKV, launch_gemv(g, h->plan_qkv[l], s));
+    // qk-norm + rope + ring push
+    QkRopeArgs qa{};
+    qa.qkv = h->qkv; qa.qkv_stride = nqkv; qa.q_out = h->q_out;
+    qa.k_ring = ring_at(h, h->k_rings, 0, l); qa.v_ring = ring_at(h, h->v_rings, 0, l);
+    qa.ring_stream_stride = h->ring_stream_stride;
+    qa.n_q_heads = hq; qa.n_kv_heads = hkv; qa.head_dim = hd; qa.m = c.m;
+    qa.q_norm = c.qk_norm ? w.q_norm : nullptr; qa.k_norm = c.qk_norm ? w.k_norm : nullptr;
+    qa.eps = c.qk_norm_eps; qa.rope_style = c.rope == SDEC_ROPE_HALF ? 0 : 1;
+    qa.cs = h->cs; qa.st = h->st;
+    LAUNCH(hk, s, SDEC_K_QK_ROPE_PUSH, launch_qk_rope_push(qa, s));
+    // ring attention
+    float* att = taps ? h->attn_out + static_cast<size_t>(l) * c.m * qw : h->attn_out;
+    AttnArgs aa{};
+    aa.q = h->q_out; aa.k_ring = qa.k_ring; aa.v_ring = qa.v_ring;
+    aa.ring_stream_stride = h->ring_stream_stride;
+    aa.pos_ring = h->pos_rings; aa.pos_stream_stride = h->ring;
+    aa.out = att; aa.part = h->part; aa.counters = h->counters;
+    aa.m = c.m; aa.n_q_heads = hq; aa.n_kv_heads = hkv; aa.head_dim = hd; aa.ring = h->ring;
+    aa.window = c.window; aa.chunk = h->chunk; aa.n_chunks = h->n_chunks; aa.st = h->st;
+    LAUNCH(hk, s, SDEC_K_ATTENTION, launch_attention(aa, s));
+    // o projection + (LayerScale) residual
+    GemvArgs o{};
+    o.w[0] = o.w[1] = o.w[2] = w.wo;
+    o.seg_end[0] = o.seg_end[1] = o.seg_end[2] = c.d_model;
+    o.n_rows = c.d_model; o.k = qw; o.m = c.m; o.x = att; o.x_stride = qw;
+    o.res = h->xres; o.res_stride = c.d_model; o.ls = c.layer_scale ? w.ls1 : nullptr;
+    o.tap = taps ? h->tap_attn_proj + static_cast<size_t>(l) * c.m * c.d_model : nullptr;
+    o.tap_stride = c.d_model;
+    LAUNCH(hk, s, SDEC_K_O, launch_gemv(o, h->plan_o[l], s));
+    // FFN norm + up projection(s) + activation
+    GemvArgs u{};
+    if (c.ffn == SDEC_FFN_SWIGLU) {
+      u.w[0] = w.w_gate; u.w[1] = w.w_up; u.w[2] = w.w_up;
+    } else {
+      u.w[0] = u.w[1] = u.w[2] = w.w_up;
+    }
+    u.seg_end[0] = u.seg_end[1] = u.seg_end[2] = c.d_ff;
+    u.n_rows = c.d_ff; u.k = c.d_model; u.m = c.m; u.x = h->xres; u.x_stride = c.d_model;
+    u.norm_w = w.ffn_norm_w; u.norm_b = w.ffn_norm_b; u.eps = c.norm_eps;
+    u.y = h->act; u.y_stride = c.d_ff;
+    (void)pro;
+    LAUNCH(hk, s, SDEC_K_FFN_UP, launch_gemv(u, h->plan_up[l], s));
+    // down projection + (LayerScale) residual
+    GemvArgs dn{};
+    dn.w[0] = dn.w[1] = dn.w[2] = w.w_down;
+    dn.seg_end[0] = dn.seg_end[1] = dn.seg_end[2] = c.d_model;
+    dn.n_rows = c.d_model; dn.k = c.d_ff; dn.m = c.m; dn.x = h->act; dn.x_stride = c.d_ff;
+    dn.res = h->xres; dn.res_stride = c.d_model; dn.ls = c.layer_scale ? w.ls2 : nullptr;
+    dn.tap = taps ? h->tap_ffn_proj + static_cast<size_t>(l) * c.m * c.d_model : nullptr;
+    dn.tap_stride = c.d_model;
+    LAUNCH(hk, s, SDEC_K_FFN_DOWN, launch_gemv(dn, h->plan_down[l], s));
+  }
+  return SDEC_OK;
+}
+
+int check_step(sdec_handle* h, const float* x, uint32_t pos, uint32_t first) {
+  if (!h) return fail(SDEC_E_ARG, "null handle");
+  if (!x || !aligned16(x)) return fail(SDEC_E_ARG, "x must be a 16-byte aligned device pointer");
+  if (pos == kInvalidPos) return fail(SDEC_E_ARG, "pos 0xFFFFFFFF is the empty-slot marker");
+  if (!first && h->has_next && pos != h->next_pos)
+    return fail(SDEC_E_POS, "step pos %u != next position %u (positions must be contiguous)",
+                pos, h->next_pos);
+  if (h->cfg.unbounded && pos >= h->ring)
+    return fail(SDEC_E_CAPACITY, "position %u exceeds the %u-slot ring of an unbounded stack",
+                pos, h->ring);
+  return SDEC_OK;
+}
+
+int enqueue_begin(sdec_handle* h, const float* x, uint32_t pos, uint32_t first, hipStream_t s,
+                  Hooks* hk) {
+  const sdec_config& c = h->cfg;
+  BeginArgs b{};
+  b.x_in = x; b.xres = h->xres; b.md = c.m * c.d_model; b.pos_rings = h->pos_rings;
+  b.m = c.m; b.ring = h->ring; b.pos = pos; b.first = first ? 1u : 0u; b.cs = h->cs;
+  b.head_dim = c.head_dim; b.theta = c.rope_theta; b.st = h->st;
+  LAUNCH(hk, s, SDEC_K_BEGIN, launch_begin(b, s));
+  return SDEC_OK;
+}
+
+int enqueue_end(sdec_handle* h, float* x, hipStream_t s, Hooks* hk) {
+  const sdec_config& c = h->cfg;
+  EndArgs e{};
+  e.xres = h->xres; e.x_out = x; e.m = c.m; e.d = c.d_model;
+  e.norm = c.final_norm ? (c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN) : -1;
+  e.w = h->fin.norm_w; e.b = h->fin.norm_b; e.eps = c.norm_eps;
+  LAUNCH(hk, s, SDEC_K_END, launch_end(e, s));
+  return SDEC_OK;
+}
+
+int clear_state(sdec_handle* h, hipStream_t s) {
+  const sdec_config& c = h->cfg;
+  const uint64_t nkv = static_cast<uint64_t>(c.m) * c.n_layers * h->ring * c.n_kv_heads * c.head_dim;
+  HIP_TRY(launch_fill_f32(h->k_rings, 0.f, nkv, s));
+  HIP_TRY(launch_fill_f32(h->v_rings, 0.f, nkv, s));
+  HIP_TRY(launch_fill_u32(h->pos_rings, kInvalidPos, static_cast<uint64_t>(c.m) * h->ring, s));
+  HIP_TRY(launch_fill_u32(h->counters, 0u, static_cast<uint64_t>(c.m) * c.n_kv_heads, s));
+  return SDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sdec_last_error(void) { return g_err.c_str(); }
+
+int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
+                const sdec_final_weights* final_weights, uint32_t ring_slots,
+                sdec_handle** out) {
+  g_err.clear();
+  if (!cfg || !layers || !out) return fail(SDEC_E_ARG, "null argument");
+  int r = validate_config(cfg, ring_slots);
+  if (r != SDEC_OK) return r;
+  r = validate_weights(cfg, layers, final_weights);
+  if (r != SDEC_OK) return r;
+
+  int device = 0;
+  HIP_TRY(hipGetDevice(&device));
+  sdec_handle* h = new sdec_handle();
+  h->device = device;
+  h->cfg = *cfg;
+  h->layers.assign(layers, layers + cfg->n_layers);
+  if (final_weights) h->fin = *final_weights;
+  h->ring = ring_slots;
+  const sdec_config& c = h->cfg;
+  const uint32_t hd = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads;
+  const uint32_t qw = hq * hd, kw = hkv * hd;
+  h->chunk = attention_chunk(hd);
+  h->n_chunks = (ring_slots + h->chunk - 1) / h->chunk;
+  h->ring_layer_stride = static_cast<uint64_t>(ring_slots) * kw;
+  h->ring_stream_stride = h->ring_layer_stride * c.n_layers;
+  const bool taps = (c.flags & SDEC_FLAG_TAPS) != 0;
+
+  Alloc A;
+  h->k_rings = A.get<float>(h->ring_stream_stride * c.m);
+  h->v_rings = A.get<float>(h->ring_stream_stride * c.m);
+  h->pos_rings = A.get<uint32_t>(static_cast<size_t>(c.m) * ring_slots);
+  h->xres = A.get<float>(static_cast<size_t>(c.m) * c.d_model);
+  h->qkv = A.get<float>(static_cast<size_t>(c.m) * (qw + 2 * kw));
+  h->q_out = A.get<float>(static_cast<size_t>(c.m) * qw);
+  h->attn_out = A.get<float>(static_cast<size_t>(c.m) * qw * (taps ? c.n_layers : 1));
+  h->act = A.get<float>(static_cast<size_t>(c.m) * c.d_ff);
+  h->part = A.get<float>(static_cast<size_t>(c.m) * hq * h->n_chunks * (hd + 2));
+  h->counters = A.get<uint32_t>(static_cast<size_t>(c.m) * hkv);
+  h->cs = A.get<float>(hd);
+  h->st = A.get<DevState>(1);
+  if (taps) {
+    h->tap_attn_proj = A.get<float>(static_cast<size_t>(c.n_layers) * c.m * c.d_model);
+    h->tap_ffn_proj = A.get<float>(static_cast<size_t>(c.n_layers) * c.m * c.d_model);
+  }
+  if (A.code != SDEC_OK) {
+    for (void* p : A.ptrs) (void)hipFree(p);
+    delete h;
+    return A.code;
+  }
+
+  for (uint32_t l = 0; l < c.n_layers; ++l) {
+    h->plan_qkv.push_back(plan_gemv(c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN, EPI_STORE,
+                                    qw + 2 * kw, c.d_model, c.m));
+    h->plan_o.push_back(plan_gemv(PRO_NONE, EPI_RESIDUAL, c.d_model, qw, c.m));
+    h->plan_up.push_back(plan_gemv(c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN,
+                                   c.ffn == SDEC_FFN_SWIGLU ? EPI_SWIGLU : EPI_GELU, c.d_ff,
+                                   c.d_model, c.m));
+    h->plan_down.push_back(plan_gemv(PRO_NONE, EPI_RESIDUAL, c.d_model, c.d_ff, c.m));
+  }
+
+  auto bail = [&](int code) {
+    if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
+    free_handle_memory(h);
+    delete h;
+    return code;
+  };
+  hipError_t e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "hipStreamCreate: %s", hipGetErrorString(e)));
+  r = clear_state(h, h->cap_stream);
+  if (r != SDEC_OK) return bail(r);
+  e = hipStreamSynchronize(h->cap_stream);
+  if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "init: %s", hipGetErrorString(e)));
+
+  if (!(c.flags & SDEC_FLAG_EAGER)) {
+    e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "begin capture: %s", hipGetErrorString(e)));
+    r = enqueue_layers(h, h->cap_stream, nullptr);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(h->cap_stream, &graph);
+    if (r != SDEC_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return bail(r);
+    }
+    if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "end capture: %s", hipGetErrorString(e)));
+    e = hipGraphInstantiate(&h->exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "graph instantiate: %s", hipGetErrorString(e)));
+    h->graph_ready = true;
+  }
+  *out = h;
+  return SDEC_OK;
+}
+
+int sdec_step(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stream) {
+  int r = check_step(h, x, pos, first);
+  if (r != SDEC_OK) return r;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r = enqueue_begin(h, x, pos, first, s, nullptr);
+  if (r != SDEC_OK) return r;
+  if (h->graph_ready) {
+    HIP_TRY(hipGraphLaunch(h->exec, s));
+  } else {
+    r = enqueue_layers(h, s, nullptr);
+    if (r != SDEC_OK) return r;
+  }
+  r = enqueue_end(h, x, s, nullptr);
+  if (r != SDEC_OK) return r;
+  h->has_next = true;
+  h->next_pos = pos + 1;
+  return SDEC_OK;
+}
+
+int sdec_step_profile(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stream,
+                      double* ms, uint32_t* calls) {
+  int r = check_step(h, x, pos, first);
+  if (r != SDEC_OK) return r;
+  if (!ms || !calls) return fail(SDEC_E_ARG, "null timing arrays");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int cap = 2 + 6 * static_cast<int>(h->cfg.n_layers);
+  std::vector<hipEvent_t> ev(2 * cap, nullptr);
+  std::vector<int> kinds(cap, 0);
+  for (auto& e : ev) HIP_TRY(hipEventCreate(&e));
+  Hooks hk;
+  hk.ev = ev.data(); hk.kinds = kinds.data(); hk.cap = cap;
+  r = enqueue_begin(h, x, pos, first, s, &hk);
+  if (r == SDEC_OK) r = enqueue_layers(h, s, &hk);
+  if (r == SDEC_OK) r = enqueue_end(h, x, s, &hk);
+  hipError_t e = hipStreamSynchronize(s);
+  if (r == SDEC_OK && e != hipSuccess) r = fail(SDEC_E_HIP, "sync: %s", hipGetErrorString(e));
+  if (r == SDEC_OK) {
+    for (int i = 0; i < hk.n; ++i) {
+      float t = 0.f;
+      e = hipEventElapsedTime(&t, ev[2 * i], ev[2 * i + 1]);
+      if (e != hipSuccess) {
+        r = fail(SDEC_E_HIP, "event time: %s", hipGetErrorString(e));
+        break;
+      }
+      ms[kinds[i]] += t;
+      calls[kinds[i]] += 1;
+    }
+    h->has_next = true;
+    h->next_pos = pos + 1;
+  }
+  for (auto& ev1 : ev) (void)hipEventDestroy(ev1);
+  return r;
+}
+
+int sdec_reset(sdec_handle* h, void* stream) {
+  if (!h) return fail(SDEC_E_ARG, "null handle");
+  int r = clear_state(h, static_cast<hipStream_t>(stream));
+  if (r != SDEC_OK) return r;
+  h->has_next = false;
+  h->next_pos = 0;
+  return SDEC_OK;
+}
+
+void sdec_destroy(sdec_handle* h) {
+  if (!h) return;
+  (void)hipDeviceSynchronize();
+  if (h->exec) (void)hipGraphExecDestroy(h->exec);
+  if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
+  free_handle_memory(h);
+  delete h;
+}
+
+int sdec_kv_view(sdec_handle* h, uint32_t stream_idx, uint32_t layer, float** k, float** v,
+                 uint32_t** pos_ring) {
+  if (!h) return fail(SDEC_E_ARG, "null handle");
+  if (stream_idx >= h->cfg.m || layer >= h->cfg.n_layers)
+    return fail(SDEC_E_ARG, "stream %u / layer %u out of range", stream_idx, layer);
+  if (k) *k = ring_at(h, h->k_rings, stream_idx, layer);
+  if (v) *v = ring_at(h, h->v_rings, stream_idx, layer);
+  if (pos_ring) *pos_ring = h->pos_rings + static_cast<size_t>(stream_idx) * h->ring;
+  return SDEC_OK;
+}
+
+int sdec_set_next_position(sdec_handle* h, uint32_t next_pos) {
+  if (!h) return fail(SDEC_E_ARG, "null handle");
+  if (next_pos == kInvalidPos) return fail(SDEC_E_ARG, "bad position");
+  h->has_next = true;
+  h->next_pos = next_pos;
+  return SDEC_OK;
+}
+
+int sdec_tap_view(sdec_handle* h, uint32_t layer, uint32_t which, float** ptr) {
+  if (!h || !ptr) return fail(SDEC_E_ARG, "null argument");
+  if (!(h->cfg.flags & SDEC_FLAG_TAPS)) return fail(SDEC_E_ARG, "handle built without SDEC_FLAG_TAPS");
+  if (layer >= h->cfg.n_layers || which > 2) return fail(SDEC_E_ARG, "tap out of range");
+  const size_t md = static_cast<size_t>(h->cfg.m) * h->cfg.d_model;
+  const size_t mq = static_cast<size_t>(h->cfg.m) * h->cfg.n_q_heads * h->cfg.head_dim;
+  if (which == 0) *ptr = h->attn_out + layer * mq;
+  else if (which == 1) *ptr = h->tap_attn_proj + layer * md;
+  else *ptr = h->tap_ffn_proj + layer * md;
+  return SDEC_OK;
+}
+
+int sdec_gemv(const float* w, const float* x, float* y, uint32_t n, uint32_t k, uint32_t m,
+              void* stream) {
+  if (!w || !x || !y) return fail(SDEC_E_ARG, "null pointer");
+  if (!aligned16(w) || !aligned16(x)) return fail(SDEC_E_ARG, "w and x must be 16-byte aligned");
+  if (n == 0 || k == 0 || k % 4) return fail(SDEC_E_ARG, "need n > 0 and k a positive multiple of 4");
+  if (m < 1 || m > static_cast<uint32_t>(kMaxM)) return fail(SDEC_E_ARG, "m must be in [1, %d]", kMaxM);
+  GemvArgs g{};
+  g.w[0] = g.w[1] = g.w[2] = w;
+  g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = n;
+  g.n_rows = n; g.k = k; g.m = m; g.x = x; g.x_stride = k; g.y = y; g.y_stride = n;
+  const GemvLaunch l = plan_gemv(PRO_NONE, EPI_STORE, n, k, m);
+  HIP_TRY(launch_gemv(g, l, static_cast<hipStream_t>(stream)));
+  return SDEC_OK;
+}
+
+int sdec_ring_attention(const float* q, const float* k_ring, const float* v_ring,
+                        const uint32_t* pos_ring, float* out, uint32_t m, uint32_t n_q_heads,
+                        uint32_t n_kv_heads, uint32_t head_dim, uint32_t ring_slots,
+                        uint32_t window, uint32_t pos, void* stream) {
+  if (!q || !k_ring || !v_ring || !pos_ring || !out) return fail(SDEC_E_ARG, "null pointer");
+  if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring))
+    return fail(SDEC_E_ARG, "q and the rings must be 16-byte aligned");
+  if (head_dim != 64 && head_dim != 128) return fail(SDEC_E_ARG, "head_dim must be 64 or 128");
+  if (!n_kv_heads || !n_q_heads || n_q_heads % n_kv_heads) return fail(SDEC_E_ARG, "bad heads");
+  const uint32_t group = n_q_heads / n_kv_heads;
+  if (group != 1 && group != 2 && group != 4) return fail(SDEC_E_ARG, "GQA group must be 1, 2 or 4");
+  if (m < 1 || m > static_cast<uint32_t>(kMaxM) || ring_slots < 1 || window < 1)
+    return fail(SDEC_E_ARG, "bad m, ring_slots or window");
+  // The chunk partials and counters live in a buffer kept for the life of the process and grown
+  // on demand; the counters are returned to zero by each launch.
+  static float* part = nullptr;
+  static size_t part_cap = 0;
+  static uint32_t* counters = nullptr;
+  static size_t cnt_cap = 0;
+  const uint32_t chunk = attention_chunk(head_dim);
+  const uint32_t n_chunks = (ring_slots + chunk - 1) / chunk;
+  const size_t need = static_cast<size_t>(m) * n_q_heads * n_chunks * (head_dim + 2);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (need > part_cap) {
+    HIP_TRY(hipDeviceSynchronize());
+    if (part) HIP_TRY(hipFree(part));
+    part = nullptr;
+    part_cap = 0;
+    HIP_TRY(hipMalloc(&part, need * sizeof(float)));
+    part_cap = need;
+  }
+  const size_t ncnt = static_cast<size_t>(m) * n_kv_heads;
+  if (ncnt > cnt_cap) {
+    HIP_TRY(hipDeviceSynchronize());
+    if (counters) HIP_TRY(hipFree(counters));
+    counters = nullptr;
+    cnt_cap = 0;
+    const size_t alloc = ncnt > 64 ? ncnt : 64;
+    HIP_TRY(hipMalloc(&counters, alloc * sizeof(uint32_t)));
+    cnt_cap = alloc;
+    HIP_TRY(launch_fill_u32(counters, 0u, cnt_cap, s));
+  }
+  AttnArgs a{};
+  a.q = q; a.k_ring = k_ring; a.v_ring = v_ring;
+  a.ring_stream_stride = static_cast<uint64_t>(ring_slots) * n_kv_heads * head_dim;
+  a.pos_ring = pos_ring; a.pos_stream_stride = ring_slots; a.out = out; a.part = part;
+  a.counters = counters; a.m = m; a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads;
+  a.head_dim = head_dim; a.ring = ring_slots; a.window = window; a.chunk = chunk;
+  a.n_chunks = n_chunks; a.st = nullptr; a.pos = pos;
+  HIP_TRY(launch_attention(a, s));
+  return SDEC_OK;
+}
+
+}  // extern "C"

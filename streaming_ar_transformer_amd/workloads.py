@@ -16,7 +16,7 @@ Shapes follow the pages' two layer families:
   no final norm.
 
 Seeds: ``numpy.random.default_rng([cfg_id, role, ...])`` with role 0 = weights
-(``[cfg_id, 0, layer, matrix]``), role 1 = per-step inputs (``[cfg_id, 1, stream]``), role 2 =
+(``[cfg_id, 0, layer, matrix]``; the m=8 talker reuses the m=1 talker's weights), role 1 = per-step inputs (``[cfg_id, 1, stream]``), role 2 =
 K/V prefill (``[cfg_id, 2, stream, layer, 0 for K / 1 for V]``).  Every draw is float32
 ``standard_normal`` scaled by the stated std, so each array can be drawn on its own thread.
 """
@@ -64,6 +64,7 @@ class StepConfig:
     start_pos: int = 0  # first decoded position (>0 when the rings are prefilled)
     weight_std: float | None = None  # fixed std, or None for 1/sqrt(k)
     bf16_round: bool = False
+    weight_seed: int | None = None  # cfg_id whose weights this stack shares (None: its own)
 
     @property
     def q_width(self) -> int:
@@ -86,13 +87,13 @@ def _codec(name, cfg_id, layers, ring, window, steps):
         window=window, steps=steps, weight_std=0.02)
 
 
-def _talker(name, cfg_id, m, ring, steps, start_pos):
+def _talker(name, cfg_id, m, ring, steps, start_pos, weight_seed=None):
     return StepConfig(
         name=name, cfg_id=cfg_id, family="T", n_layers=28, d_model=2048, n_q_heads=16,
         n_kv_heads=8, head_dim=128, d_ff=6144, m=m, norm=NORM_RMS, norm_eps=1e-6, qk_norm=True,
         qk_norm_eps=1e-6, rope=ROPE_HALF, rope_theta=1e6, ffn=FFN_SWIGLU, layer_scale=False,
         layer_scale_init=1.0, final_norm=True, ring=ring, window=ring, steps=steps,
-        start_pos=start_pos, weight_std=None, bf16_round=True)
+        start_pos=start_pos, weight_std=None, bf16_round=True, weight_seed=weight_seed)
 
 
 # The five workloads.  Ring/window readings: a ring that holds exactly the window is exact at one
@@ -103,7 +104,8 @@ CONFIGS = {
     2: _codec("codec2_d512_r251w250", 2, 2, 251, 250, 1000),
     3: _codec("codec8_d512_r250", 3, 8, 250, 250, 2000),
     4: _talker("talker28_h2048_m1", 4, 1, 2048, 2048, 0),
-    5: _talker("talker28_h2048_m8_prefill4096", 5, 8, 4352, 256, 4096),
+    # The m=8 workload runs the same talker as config 4, so it shares config 4's weights.
+    5: _talker("talker28_h2048_m8_prefill4096", 5, 8, 4352, 256, 4096, weight_seed=4),
 }
 
 
@@ -160,15 +162,16 @@ def make_weights(cfg: StepConfig, threads: int = 8):
     ``[q; k; v]``).  ``final`` holds ``norm_w`` (and ``norm_b`` for LayerNorm) when the stack has
     a final norm, else it is empty."""
     specs = layer_weight_specs(cfg)
+    wid = cfg.cfg_id if cfg.weight_seed is None else cfg.weight_seed
     jobs = []
     for l in range(cfg.n_layers):
         for i, (name, shape, std, mean) in enumerate(specs):
-            jobs.append((l, name, [cfg.cfg_id, 0, l, i], shape, std, mean))
+            jobs.append((l, name, [wid, 0, l, i], shape, std, mean))
     if cfg.final_norm:
-        jobs.append((cfg.n_layers, "norm_w", [cfg.cfg_id, 0, cfg.n_layers, 0], (cfg.d_model,),
+        jobs.append((cfg.n_layers, "norm_w", [wid, 0, cfg.n_layers, 0], (cfg.d_model,),
                      0.02, 1.0))
         if cfg.norm == NORM_LAYER:
-            jobs.append((cfg.n_layers, "norm_b", [cfg.cfg_id, 0, cfg.n_layers, 1],
+            jobs.append((cfg.n_layers, "norm_b", [wid, 0, cfg.n_layers, 1],
                          (cfg.d_model,), 0.02, 0.0))
 
     def run(job):
