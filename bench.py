@@ -1,0 +1,234 @@
+"""Decode-step benchmark: steps/s and achieved HBM bandwidth of the streaming decode step.
+
+Default workload: the 28-layer talker-family stack at m=1 (hidden 2048, 16 q / 8 kv heads x 128,
+SwiGLU 6144, 2048-slot cache), float32 with bf16-rounded synthetic weights, run over positions
+0..K-1 of a fresh stream (K = 2048 covers the whole cache).  Inputs, weights and state are resident
+in HBM before the timed region; each step's input row is a slice of a pre-drawn device tensor.
+
+One JSON line on stdout:
+  value        steps/s over the K timed steps (one step = the whole layer stack for one position)
+  roofline     the dominant kernel (the FFN gate/up GEMV with its fused norm and SwiGLU): its
+               algorithmic bytes per launch / its mean launch time, measured with HIP event pairs
+               around each launch of profiled eager steps
+  cpu_baseline the CPU oracle on a bounded sample of the same run (first positions), host cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--config", type=int, default=4, help="workload id (4: the m=1 talker)")
+    ap.add_argument("--eager", action="store_true", help="launch kernels one by one, no graph")
+    ap.add_argument("--profile-steps", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-timed", action="store_true",
+                    help="warmup + timed steps only (for running under a profiler)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes three times (the "
+                         "known-size kernel that calibrates HBM byte counters)")
+    return ap.parse_args()
+
+
+def layer_weight_bytes(cfg):
+    d, f, qw, kw = cfg.d_model, cfg.d_ff, cfg.q_width, cfg.kv_width
+    mats = (qw + 2 * kw) * d + d * qw + (2 if cfg.ffn == 0 else 1) * f * d + d * f
+    vecs = 2 * d * (2 if cfg.norm == 1 else 1) + (2 * cfg.head_dim if cfg.qk_norm else 0) \
+        + (2 * d if cfg.layer_scale else 0)
+    return 4 * (mats + vecs)
+
+
+def step_bytes(cfg, pos, ring, window):
+    """Algorithmic HBM bytes of one step at `pos` (each weight, live K/V row and position-ring
+    word read once, the new K/V rows written once, the m input and output rows)."""
+    w = cfg.n_layers * layer_weight_bytes(cfg)
+    if cfg.final_norm:
+        w += 4 * cfg.d_model * (2 if cfg.norm == 1 else 1)
+    live = min(pos + 1, window, ring)
+    kv_row = 2 * 4 * cfg.kv_width
+    per_stream = cfg.n_layers * (kv_row * live + kv_row + 4 * ring) + 2 * 4 * cfg.d_model
+    return w + cfg.m * per_stream
+
+
+def ffn_up_bytes(cfg):
+    d, f = cfg.d_model, cfg.d_ff
+    mats = (2 if cfg.ffn == 0 else 1) * f * d
+    return 4 * (mats + d * (2 if cfg.norm == 1 else 1) + cfg.m * d + cfg.m * f)
+
+
+def kernel_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel source they were
+    taken on is the current one; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    src = open(os.path.join(ROOT, "streaming_ar_transformer_amd", "csrc", "kernels.hip"), "rb").read()
+    digest = hashlib.sha256(src).hexdigest()[:16]
+    rec = json.load(open(path)).get(f"{kernel}@{workload}")
+    if not rec or rec.get("kernels_hip_sha256_16") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, layers, final, xs, budget_s):
+    import numpy as np  # noqa: F401
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    t0 = time.perf_counter()
+    n = 0
+    while n < xs.shape[0]:
+        orc.step(xs[n], n, first=(n == 0))
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"positions 0..{n - 1} of a fresh stream of this workload "
+                      f"({n} steps, {dt:.1f} s, NumPy float32, BLAS threads={threads})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(independent streams shard across GPUs with no exchange: run one process per GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {n * 4} bytes x3", file=sys.stderr)
+        return
+
+    from streaming_ar_transformer_amd import sdec, workloads as wl
+    from streaming_ar_transformer_amd.device import to_device, upload_weights
+
+    torch.cuda.set_device(0)
+    cfg = wl.CONFIGS[args.config]
+    ring, window = cfg.ring, cfg.window
+    unbounded = cfg.family == "T"
+    t0 = time.perf_counter()
+    layers, final = wl.make_weights(cfg)
+    dl, df = upload_weights(layers, final)
+    n_in = max(args.steps, args.warmup, 1)
+    xs_host = wl.make_inputs(cfg, n_in)
+    xs = to_device(xs_host)  # [n, m, d] resident in HBM
+    dec = sdec.Decoder(cfg, dl, df, eager=args.eager)
+    torch.cuda.synchronize()
+    print(f"setup {time.perf_counter() - t0:.1f}s: {cfg.name}", file=sys.stderr, flush=True)
+
+    def positions(n):
+        # A fresh stream from position 0; an unbounded stack restarts (first=1) when full.
+        out = []
+        p = 0
+        for _ in range(n):
+            if unbounded and p >= ring:
+                p = 0
+            out.append(p)
+            p += 1
+        return out
+
+    # warmup
+    wpos = positions(args.warmup)
+    for i, p in enumerate(wpos):
+        dec.step(xs[i], p, first=(p == 0))
+    torch.cuda.synchronize()
+    # reload the inputs the warmup overwrote, start a fresh stream
+    xs.copy_(torch.from_numpy(xs_host))
+    dec.reset()
+    torch.cuda.synchronize()
+
+    tpos = positions(args.steps)
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i, p in enumerate(tpos):
+        dec.step(xs[i], p, first=(p == 0), stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / args.steps
+    steps_per_s = 1000.0 / ms_per_step
+    bytes_avg = float(np.mean([step_bytes(cfg, p, ring, window) for p in tpos]))
+    hbm_gbs = bytes_avg / (ms_per_step * 1e-3) / 1e9
+    print(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {hbm_gbs:.0f} GB/s "
+          f"({100 * hbm_gbs / PEAK_HBM_GBS:.1f}% of peak)", file=sys.stderr, flush=True)
+    if args.only_timed:
+        dec.close()
+        return
+
+    # per-kernel launch times from profiled eager steps (HIP event pair around every launch)
+    xs.copy_(torch.from_numpy(xs_host))
+    dec.reset()
+    prof = None
+    for i, p in enumerate(positions(args.profile_steps)):
+        prof = dec.step_profile(xs[i], p, first=(p == 0), stream=stream, into=prof)
+    kernels = {k: {"mean_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]}
+               for k, v in prof.items() if v[1]}
+    up_us = 1e3 * prof["ffn_up"][0] / prof["ffn_up"][1]
+    up_bytes = ffn_up_bytes(cfg)
+    achieved = up_bytes / (up_us * 1e-6) / 1e9
+    for k, b in (("qkv", 4 * ((cfg.q_width + 2 * cfg.kv_width) * cfg.d_model)),
+                 ("o_proj", 4 * cfg.d_model * cfg.q_width), ("ffn_up", up_bytes),
+                 ("ffn_down", 4 * cfg.d_model * cfg.d_ff)):
+        if k in kernels:
+            kernels[k]["weight_gbs"] = round(b / (kernels[k]["mean_us"] * 1e-6) / 1e9, 1)
+    traffic = kernel_traffic("ffn_up", cfg.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "kernel": "k_gemv ffn gate/up + RMSNorm + SwiGLU",
+                "bytes_per_launch": up_bytes, "mean_launch_us": round(up_us, 2)}
+    dec.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, layers, final, xs_host, args.cpu_seconds)
+
+    line = {
+        "metric": "decode steps/s + achieved HBM GB/s (% of peak), 28L talker step at m=1",
+        "value": round(steps_per_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": cfg.n_layers, "hidden": cfg.d_model,
+                   "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "ffn": cfg.d_ff, "m": cfg.m, "ring": ring,
+                   "window": window, "positions": f"{tpos[0]}..{tpos[-1]}",
+                   "mode": "eager" if args.eager else "hipgraph"},
+        "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
+        "bytes_per_step": int(bytes_avg),
+        "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
