@@ -153,8 +153,14 @@ int sdec_tap_view(sdec_handle* h, uint32_t layer, uint32_t which, float** ptr);
  * update) with a hipEvent pair around every launch, waits for it, and adds each launch's
  * milliseconds into ms[kind] and 1 into calls[kind] (kind = SDEC_K_*; arrays of SDEC_K_COUNT). */
 enum {
-  SDEC_K_BEGIN = 0, SDEC_K_QKV = 1, SDEC_K_QK_ROPE_PUSH = 2, SDEC_K_ATTENTION = 3, SDEC_K_O = 4,
-  SDEC_K_FFN_UP = 5, SDEC_K_FFN_DOWN = 6, SDEC_K_END = 7, SDEC_K_COUNT = 8
+  SDEC_K_BEGIN = 0,     /* input copy, position-ring stamp, this position's rope cos/sin */
+  SDEC_K_QKV = 1,       /* pre-attention norm + q/k/v projections */
+  SDEC_K_ATTENTION = 2, /* qk-norm + rope + ring push + ring attention */
+  SDEC_K_O = 3,         /* o projection + (LayerScale) residual */
+  SDEC_K_FFN_UP = 4,    /* pre-FFN norm + gate/up (SwiGLU) or W1 (GELU) projection */
+  SDEC_K_FFN_DOWN = 5,  /* down projection + (LayerScale) residual */
+  SDEC_K_END = 6,       /* final norm, or copy of the residual stream, into x */
+  SDEC_K_COUNT = 7
 };
 int sdec_step_profile(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stream,
                       double* ms, uint32_t* calls);

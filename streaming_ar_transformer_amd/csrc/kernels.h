@@ -46,43 +46,37 @@ struct GemvLaunch {
   int prologue;
   int epilogue;
   int rows_per_wave;  // R: rows one wave reduces together
+  int kb;             // >0: k == 256*kb and the input rows live in registers; 0: generic k
   int waves_per_wg;
-  uint32_t grid;      // workgroups
+  uint32_t grid;      // workgroups; each wave owns a contiguous, balanced range of row tiles
 };
 
 hipError_t launch_gemv(const GemvArgs& a, const GemvLaunch& l, hipStream_t s);
 // A launch shape for this GEMV on this device (grid sized to the row tiles).
 GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, uint32_t m);
 
-struct QkRopeArgs {
-  const float* qkv;      // [m][qkv_stride]: q (Hq*hd), k (Hkv*hd), v (Hkv*hd)
+// Ring attention of one layer for every stream.  In the step it also finishes the new position:
+// qk-RMSNorm and rope of this step's q and k (from the raw q/k/v projection), and the push of the
+// roped k and raw v into ring slot st->slot by the workgroup whose slot chunk holds that slot.
+struct AttnArgs {
+  const float* qkv;      // [m][qkv_stride]: raw q (Hq*hd), then k (Hkv*hd), then v (Hkv*hd)
   uint32_t qkv_stride;
-  float* q_out;          // [m][Hq*hd] normed + roped queries
-  float* k_ring;         // this layer's K ring of stream 0: [R][Hkv][hd]
-  float* v_ring;
-  uint64_t ring_stream_stride;  // floats between consecutive streams' rings
-  uint32_t n_q_heads, n_kv_heads, head_dim, m;
-  const float* q_norm;   // null: no qk-norm
+  const float* q_norm;   // [hd] or null (no qk-norm)
   const float* k_norm;
   float eps;
   int rope_style;        // 0 rotate_half, 1 interleaved
-  const float* cs;       // [hd/2] cos then [hd/2] sin for this step's position
-  const DevState* st;
-};
-hipError_t launch_qk_rope_push(const QkRopeArgs& a, hipStream_t s);
-
-struct AttnArgs {
-  const float* q;        // [m][Hq*hd]
-  const float* k_ring;   // stream 0 of this layer: [R][Hkv][hd]
-  const float* v_ring;
-  uint64_t ring_stream_stride;
-  const uint32_t* pos_ring;  // [m][R]
+  const float* cs;       // [hd/2] cos then [hd/2] sin of this position; null: q used as given
+  int push;              // nonzero: push this step's k/v into the rings
+  float* k_ring;         // stream 0 of this layer: [R][Hkv][hd]
+  float* v_ring;
+  uint64_t ring_stream_stride;  // floats between consecutive streams' rings
+  const uint32_t* pos_ring;     // [m][R]
   uint32_t pos_stream_stride;
   float* out;            // [m][Hq*hd]
   float* part;           // [m][Hq][n_chunks][hd + 2] chunk partials
   uint32_t* counters;    // [m][Hkv], zero between launches (the last chunk resets it)
   uint32_t m, n_q_heads, n_kv_heads, head_dim, ring, window, chunk, n_chunks;
-  const DevState* st;    // position source; null: use `pos`
+  const DevState* st;    // position source; null: use `pos` (and no push)
   uint32_t pos;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

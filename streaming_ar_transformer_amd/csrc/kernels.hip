@@ -10,6 +10,7 @@
 // elementwise work (norm prologue, SwiGLU / GELU / LayerScale-residual epilogues) into itself.
 
 #include <math.h>
+#include <stdlib.h>
 
 #include "kernels.h"
 
@@ -26,6 +27,25 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float4 f4zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+
+// Weights are streamed once per step: load them non-temporally so they do not displace the
+// small, reused activations from the caches.
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ldw(const float4* p) {
+  const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// Device-coherent (agent-scope) stores and loads: they bypass the per-XCD cache state, so data
+// handed between workgroups needs no cache-wide writeback or invalidate -- only completion of the
+// stores before the hand-off counter is bumped.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ float dot4(float4 w, float4 x, float acc) {
   acc = fmaf(w.x, x.x, acc);
@@ -126,66 +146,220 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, float4* xs, uint32_t 
 
 // ------------------------------------------------------------------------------------------------
 // Weight-streaming GEMV: y[m][n] = sum_k x[m][k] W[n][k], W row-major [n][k] read exactly once
-// ([talker] MATVEC_SRC; [mimi] MATVEC, MV_LS).  One wave owns R rows (a "tile") for all M input
-// rows; lane l reads float4 column l, l+64, ... of each row, so a wave's loads cover 1 KiB of a
-// row per instruction.  U float4 per row are issued before any use to keep bytes in flight.
+// ([talker] MATVEC_SRC; [mimi] MATVEC, MV_LS).  One wave owns R rows at a time (a "tile") for all
+// M input rows; lane l reads float4 columns l, l+64, ... of each row, so one load instruction of a
+// wave covers 1 KiB of a row.  Each wave owns a contiguous, balanced range of tiles, and the first
+// tile's weights are requested before anything that depends on x, so the HBM latency overlaps
+// the input prologue.
 // ------------------------------------------------------------------------------------------------
+template <int R, int EPI>
+__device__ __forceinline__ void tile_rows(const GemvArgs& a, uint32_t t, const float4* (&wr)[R]) {
+  constexpr int RH = EPI == EPI_SWIGLU ? R / 2 : R;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    uint32_t row;
+    const float* base;
+    if (EPI == EPI_SWIGLU) {
+      row = min(t * RH + (r % RH), a.n_rows - 1);
+      base = r < RH ? a.w[0] : a.w[1];
+    } else {
+      row = min(t * RH + r, a.n_rows - 1);
+      if (row < a.seg_end[0]) {
+        base = a.w[0];
+      } else if (row < a.seg_end[1]) {
+        base = a.w[1];
+        row -= a.seg_end[0];
+      } else {
+        base = a.w[2];
+        row -= a.seg_end[1];
+      }
+    }
+    wr[r] = reinterpret_cast<const float4*>(base + static_cast<size_t>(row) * a.k);
+  }
+}
+
+// Reduce the tile's R*M lane partials and apply the epilogue: store, GELU, SwiGLU (gate row r and
+// up row r + R/2 of the same FFN index sit 32 lanes apart after the reduce-scatter), or the
+// (LayerScale) residual add ([mimi] MV_LS: y += ls * (W x)).
+template <int M, int R, int EPI>
+__device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, uint32_t t, float* acc, int lane) {
+  constexpr int V = R * M;
+  constexpr int S = kWave / V;
+  constexpr int RH = EPI == EPI_SWIGLU ? R / 2 : R;
+  ReduceScatter<V, 32>::run(acc, lane);
+  const float val = acc[0];
+  const int idx = lane / S;
+  const bool owner = (lane % S) == 0;
+  const int r = idx / M, m = idx % M;
+  if (EPI == EPI_SWIGLU) {
+    const float up = __shfl_xor(val, 32, kWave);
+    const uint32_t i = t * RH + r;
+    if (owner && lane < 32 && i < a.n_rows && m < static_cast<int>(a.m))
+      a.y[m * a.y_stride + i] = silu(val) * up;
+  } else {
+    const uint32_t row = t * RH + r;
+    if (owner && row < a.n_rows && m < static_cast<int>(a.m)) {
+      if (EPI == EPI_STORE) {
+        a.y[m * a.y_stride + row] = val;
+      } else if (EPI == EPI_GELU) {
+        a.y[m * a.y_stride + row] = gelu_erf(val);
+      } else {
+        if (a.tap) a.tap[m * a.tap_stride + row] = val;
+        float* dst = a.res + m * a.res_stride + row;
+        *dst = *dst + (a.ls ? a.ls[row] * val : val);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void wave_tiles(uint32_t n_tiles, uint32_t& t, uint32_t& t_end) {
+  const uint32_t nw = blockDim.x / kWave;
+  const uint32_t gw = blockIdx.x * nw + threadIdx.x / kWave;
+  const uint64_t nwaves = static_cast<uint64_t>(gridDim.x) * nw;
+  t = static_cast<uint32_t>(gw * static_cast<uint64_t>(n_tiles) / nwaves);
+  t_end = static_cast<uint32_t>((gw + 1) * static_cast<uint64_t>(n_tiles) / nwaves);
+}
+
+// Register-resident variant: k == 256*KB, and each lane keeps its KB float4 of every input row in
+// registers, normalised by the wave itself (no LDS, no workgroup barrier).
+template <int M, int R, int PRO, int EPI, int KB>
+__global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
+  constexpr int V = R * M;
+  static_assert(V <= 64, "tile too large for one wave");
+  constexpr int RH = EPI == EPI_SWIGLU ? R / 2 : R;
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t t, t_end;
+  wave_tiles((a.n_rows + RH - 1) / RH, t, t_end);
+  if (t >= t_end) return;
+
+  const float4* wr[R];
+  float4 w[KB][R];
+  tile_rows<R, EPI>(a, t, wr);
+#pragma unroll
+  for (int j = 0; j < KB; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[j][r] = ldw(wr[r] + lane + kWave * j);
+
+  float4 xr[M][KB];
+  const float4* x4 = reinterpret_cast<const float4*>(a.x);
+  const uint32_t xs4 = a.x_stride >> 2;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      xr[m][j] = m < static_cast<int>(a.m) ? x4[m * xs4 + lane + kWave * j] : f4zero();
+  if (PRO != PRO_NONE) {
+    const float4* g4 = reinterpret_cast<const float4*>(a.norm_w);
+    const float4* b4 = reinterpret_cast<const float4*>(a.norm_b);
+    const float kf = static_cast<float>(a.k);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float mean = 0.f, inv;
+      if (PRO == PRO_RMS) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) ss = dot4(xr[m][j], xr[m][j], ss);
+        inv = 1.0f / sqrtf(wave_sum(ss) / kf + a.eps);
+      } else {
+        float sm = 0.f;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) sm += (xr[m][j].x + xr[m][j].y) + (xr[m][j].z + xr[m][j].w);
+        mean = wave_sum(sm) / kf;
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          float4 d = xr[m][j];
+          d.x -= mean; d.y -= mean; d.z -= mean; d.w -= mean;
+          ss = dot4(d, d, ss);
+        }
+        inv = 1.0f / sqrtf(wave_sum(ss) / kf + a.eps);
+      }
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const float4 g = g4[lane + kWave * j];
+        float4 v = xr[m][j];
+        if (PRO == PRO_RMS) {
+          v.x = (v.x * inv) * g.x; v.y = (v.y * inv) * g.y;
+          v.z = (v.z * inv) * g.z; v.w = (v.w * inv) * g.w;
+        } else {
+          const float4 b = b4[lane + kWave * j];
+          v.x = ((v.x - mean) * inv) * g.x + b.x; v.y = ((v.y - mean) * inv) * g.y + b.y;
+          v.z = ((v.z - mean) * inv) * g.z + b.z; v.w = ((v.w - mean) * inv) * g.w + b.w;
+        }
+        xr[m][j] = m < static_cast<int>(a.m) ? v : f4zero();
+      }
+    }
+  }
+
+  while (true) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r * M + m] = dot4(w[j][r], xr[m][j], acc[r * M + m]);
+    const uint32_t cur = t++;
+    if (t < t_end) {
+      tile_rows<R, EPI>(a, t, wr);
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+#pragma unroll
+        for (int r = 0; r < R; ++r) w[j][r] = ldw(wr[r] + lane + kWave * j);
+    }
+    gemv_epilogue<M, R, EPI>(a, cur, acc, lane);
+    if (t >= t_end) break;
+  }
+}
+
+// Generic variant: any k (multiple of 4).  With a norm prologue the input rows are staged in LDS;
+// without one they are read from global memory (they stay in L1/L2).
 template <int M, int R, int PRO, int EPI>
 __global__ __launch_bounds__(kWgThreads) void k_gemv(GemvArgs a) {
   extern __shared__ float4 xs[];
   constexpr int U = M <= 2 ? 8 : (M <= 4 ? 4 : 2);
   constexpr int V = R * M;
   static_assert(V <= 64, "tile too large for one wave");
-  constexpr int S = kWave / V;  // lanes per reduced value
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int nw = blockDim.x / kWave;
+  constexpr int RH = EPI == EPI_SWIGLU ? R / 2 : R;
+  const int lane = threadIdx.x & (kWave - 1);
   const uint32_t K4 = a.k >> 2;
-  if (PRO != PRO_NONE) stage_x<M, PRO>(a, xs, K4);
+  const uint32_t n_iter = (K4 + kWave * U - 1) / (kWave * U);
+  uint32_t t, t_end;
+  wave_tiles((a.n_rows + RH - 1) / RH, t, t_end);
 
-  constexpr int RH = EPI == EPI_SWIGLU ? R / 2 : R;  // output indices per tile
-  const uint32_t n_tiles = (a.n_rows + RH - 1) / RH;
+  const float4* wr[R];
+  float4 wv[U][R];
+  auto load_chunk = [&](uint32_t it) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t c = lane + kWave * (U * it + u);
+#pragma unroll
+      for (int r = 0; r < R; ++r) wv[u][r] = c < K4 ? ldw(wr[r] + c) : f4zero();
+    }
+  };
+  bool prefetched = false;
+  if (t < t_end) {
+    tile_rows<R, EPI>(a, t, wr);
+    load_chunk(0);
+    prefetched = true;
+  }
+  if (PRO != PRO_NONE) stage_x<M, PRO>(a, xs, K4);  // every wave reaches the barriers inside
   const float4* x4 = reinterpret_cast<const float4*>(a.x);
   const uint32_t xstride4 = a.x_stride >> 2;
 
-  for (uint32_t t = blockIdx.x * nw + wave; t < n_tiles; t += gridDim.x * nw) {
-    const float4* wr[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      uint32_t row;
-      const float* base;
-      if (EPI == EPI_SWIGLU) {
-        row = min(t * RH + (r % RH), a.n_rows - 1);
-        base = r < RH ? a.w[0] : a.w[1];
-      } else {
-        row = min(t * RH + r, a.n_rows - 1);
-        if (row < a.seg_end[0]) {
-          base = a.w[0];
-        } else if (row < a.seg_end[1]) {
-          base = a.w[1];
-          row -= a.seg_end[0];
-        } else {
-          base = a.w[2];
-          row -= a.seg_end[1];
-        }
-      }
-      wr[r] = reinterpret_cast<const float4*>(base + static_cast<size_t>(row) * a.k);
-    }
-
+  for (; t < t_end; ++t) {
+    if (!prefetched) tile_rows<R, EPI>(a, t, wr);
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
-
-    for (uint32_t c0 = lane; c0 < K4; c0 += kWave * U) {
-      float4 wv[U][R];
+    for (uint32_t it = 0; it < n_iter; ++it) {
+      if (!prefetched) load_chunk(it);
+      prefetched = false;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t c = c0 + u * kWave;
-#pragma unroll
-        for (int r = 0; r < R; ++r) wv[u][r] = c < K4 ? wr[r][c] : f4zero();
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t c = c0 + u * kWave;
+        const uint32_t c = lane + kWave * (U * it + u);
         if (c < K4) {
 #pragma unroll
           for (int m = 0; m < M; ++m) {
@@ -198,89 +372,48 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv(GemvArgs a) {
         }
       }
     }
-
-    ReduceScatter<V, 32>::run(acc, lane);
-    const float val = acc[0];
-    const int idx = lane / S;
-    const bool owner = (lane % S) == 0;
-    const int r = idx / M, m = idx % M;
-    if (EPI == EPI_SWIGLU) {
-      const float up = __shfl_xor(val, 32, kWave);  // row r + R/2 lives 32 lanes away
-      const uint32_t i = t * RH + r;
-      if (owner && lane < 32 && i < a.n_rows && m < static_cast<int>(a.m))
-        a.y[m * a.y_stride + i] = silu(val) * up;
-    } else {
-      const uint32_t row = t * RH + r;
-      if (owner && row < a.n_rows && m < static_cast<int>(a.m)) {
-        if (EPI == EPI_STORE) {
-          a.y[m * a.y_stride + row] = val;
-        } else if (EPI == EPI_GELU) {
-          a.y[m * a.y_stride + row] = gelu_erf(val);
-        } else {
-          if (a.tap) a.tap[m * a.tap_stride + row] = val;
-          float* dst = a.res + m * a.res_stride + row;
-          *dst = *dst + (a.ls ? a.ls[row] * val : val);
-        }
-      }
-    }
+    gemv_epilogue<M, R, EPI>(a, t, acc, lane);
   }
 }
 
 // ------------------------------------------------------------------------------------------------
-// Per-head qk-RMSNorm + rope + KV ring push ([talker] QK_NORM_SRC, ROPE_SRC, APPEND_SRC;
-// [mimi] rope_push_src).  One wave per (head, stream); lane j owns rope pair j, which is
-// (j, j+hd/2) for rotate_half and (2j, 2j+1) for the interleaved form, so both forms are the same
-// rotation (a, b) -> (a c - b s, a s + b c).  Query heads land in q_out; key heads are written,
-// already roped, into ring slot pos mod R, and the value head is copied beside them.
+// qk-RMSNorm + rope of one head pair ([talker] QK_NORM_SRC then ROPE_SRC; [mimi] rope_push_src).
+// Lane j owns rope pair j: (j, j + hd/2) for rotate_half, (2j, 2j + 1) for the interleaved form;
+// both are the rotation (a, b) -> (a c - b s, a s + b c).  Called by a whole wave.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kWave) void k_qk_rope_push(QkRopeArgs a) {
-  const uint32_t h = blockIdx.x, s = blockIdx.y, j = threadIdx.x;
-  const uint32_t hd = a.head_dim, half = hd >> 1;
-  const bool act = j < half;
-  const bool is_q = h < a.n_q_heads;
-  const float* src = a.qkv + static_cast<size_t>(s) * a.qkv_stride + h * hd;
-  const uint32_t ia = a.rope_style == 0 ? j : 2 * j;
-  const uint32_t ib = a.rope_style == 0 ? j + half : 2 * j + 1;
-  float va = act ? src[ia] : 0.f;
-  float vb = act ? src[ib] : 0.f;
-  const float* g = is_q ? a.q_norm : a.k_norm;
-  if (g != nullptr) {
-    const float ss = wave_sum(va * va + vb * vb);
-    const float inv = 1.0f / sqrtf(ss / static_cast<float>(hd) + a.eps);
+template <int HD>
+__device__ __forceinline__ void norm_rope_pair(float& va, float& vb, int j, const float* gnorm,
+                                               float eps, const float* cs, int style) {
+  constexpr int HALF = HD / 2;
+  const bool act = j < HALF;
+  if (gnorm != nullptr) {
+    const float ss = wave_sum(act ? va * va + vb * vb : 0.f);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(HD) + eps);
     if (act) {
-      va = (va * inv) * g[ia];
-      vb = (vb * inv) * g[ib];
+      const int ia = style == 0 ? j : 2 * j, ib = style == 0 ? j + HALF : 2 * j + 1;
+      va = (va * inv) * gnorm[ia];
+      vb = (vb * inv) * gnorm[ib];
     }
   }
-  if (!act) return;
-  const float c = a.cs[j], sn = a.cs[half + j];
-  const float ra = va * c - vb * sn;
-  const float rb = va * sn + vb * c;
-  if (is_q) {
-    float* d = a.q_out + static_cast<size_t>(s) * a.n_q_heads * hd + h * hd;
-    d[ia] = ra;
-    d[ib] = rb;
-  } else {
-    const uint32_t kvh = h - a.n_q_heads;
-    const size_t off = static_cast<size_t>(s) * a.ring_stream_stride +
-                       (static_cast<size_t>(a.st->slot) * a.n_kv_heads + kvh) * hd;
-    a.k_ring[off + ia] = ra;
-    a.k_ring[off + ib] = rb;
-    const float* vsrc = a.qkv + static_cast<size_t>(s) * a.qkv_stride +
-                        (a.n_q_heads + a.n_kv_heads + kvh) * hd;
-    a.v_ring[off + ia] = vsrc[ia];
-    a.v_ring[off + ib] = vsrc[ib];
+  if (cs != nullptr && act) {
+    const float c = cs[j], sn = cs[HALF + j];
+    const float ra = va * c - vb * sn;
+    const float rb = va * sn + vb * c;
+    va = ra;
+    vb = rb;
   }
 }
 
 // ------------------------------------------------------------------------------------------------
 // Ring attention, split over slot chunks ([mimi] attn_src: legality from the position ring, a
 // masked slot weighs nothing; [talker] GQA_ATTN_SRC: kv head = q head / group, scale 1/sqrt(hd)).
-// Grid (chunk, kv head, stream).  The chunk's legal slots are compacted first, so masked slots
-// cost no K/V traffic.  Slot groups of hd/8 lanes (8 dims per lane) walk the legal slots with an
-// online softmax for all G query heads of the kv head, so each K/V row is read once for the whole
-// GQA group.  Groups merge in LDS; chunks merge in the last workgroup to finish (integer counter),
-// in ascending chunk order, so the result does not depend on which workgroup finishes last.
+// Grid (chunk, kv head, stream).  Each workgroup first finishes this step's queries of its GQA
+// group (qk-norm + rope, in LDS); the workgroup whose chunk holds slot pos mod R also finishes
+// this step's key and pushes it, roped, with the raw value into the rings ([talker] APPEND_SRC;
+// [mimi] rope_push_src).  The chunk's legal slots are compacted, so masked slots cost no K/V
+// traffic.  Slot groups of hd/8 lanes (8 dims per lane) walk the legal slots with an online
+// softmax for all G query heads, so each K/V row is read once for the whole GQA group.  Groups
+// merge in LDS; chunks merge in the last workgroup to finish, in ascending chunk order.
 // ------------------------------------------------------------------------------------------------
 template <int HD, int G>
 __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
@@ -289,8 +422,12 @@ __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
   constexpr int NWV = kWgThreads / kWave;
   constexpr int NG = NWV * GPW;
   constexpr int UNR = 4;
+  constexpr int HALF = HD / 2;
+  constexpr int CB = 16;  // chunks merged per batch by the last workgroup
+  static_assert(CB <= NG, "combine staging reuses the group buffers");
   __shared__ uint32_t list[kWgThreads];
   __shared__ uint32_t wave_cnt[NWV];
+  __shared__ float qs[G][HD];
   __shared__ float sm_m[NG][G], sm_l[NG][G];
   __shared__ float sm_acc[NG][G][HD];
   __shared__ uint32_t is_last;
@@ -302,8 +439,11 @@ __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
   const uint32_t pos = a.st ? a.st->pos : a.pos;
   const uint32_t c0 = chunk * a.chunk;
   const uint32_t c1 = min(c0 + a.chunk, a.ring);
+  const uint32_t hq = a.n_q_heads, hkv = a.n_kv_heads;
+  const uint32_t h0 = kvh * G;
+  const float* qkv = a.qkv + static_cast<size_t>(s) * a.qkv_stride;
 
-  // 1. legal slots of the chunk, in slot order
+  // 1. legal slots of the chunk, in slot order; this step's raw queries
   const uint32_t slot = c0 + tid;
   bool ok = false;
   if (slot < c1) {
@@ -313,6 +453,7 @@ __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
   const unsigned long long mask = __ballot(ok);
   const uint32_t before = __popcll(mask & ((1ull << lane) - 1ull));
   if (lane == 0) wave_cnt[wave] = __popcll(mask);
+  for (int t = tid; t < G * HD; t += kWgThreads) qs[t / HD][t % HD] = qkv[(h0 + t / HD) * HD + t % HD];
   __syncthreads();
   uint32_t off = 0, total = 0;
 #pragma unroll
@@ -321,20 +462,50 @@ __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
     total += wave_cnt[w];
   }
   if (ok) list[off + before] = slot;
-  __syncthreads();
 
-  // 2. online softmax over this group's share of the legal slots
-  const uint32_t hq = a.n_q_heads, hkv = a.n_kv_heads;
-  const uint32_t h0 = kvh * G;
+  // 2. queries: qk-norm + rope, one wave per head
+  if (a.q_norm != nullptr || a.cs != nullptr) {
+    for (int g = wave; g < G; g += NWV) {
+      const int ia = a.rope_style == 0 ? lane : 2 * lane;
+      const int ib = a.rope_style == 0 ? lane + HALF : 2 * lane + 1;
+      float va = lane < HALF ? qs[g][ia] : 0.f, vb = lane < HALF ? qs[g][ib] : 0.f;
+      norm_rope_pair<HD>(va, vb, lane, a.q_norm, a.eps, a.cs, a.rope_style);
+      if (lane < HALF) {
+        qs[g][ia] = va;
+        qs[g][ib] = vb;
+      }
+    }
+  }
+  // 3. the owner of slot pos mod R pushes this step's key (normed, roped) and value
+  if (a.push && a.st != nullptr) {
+    const uint32_t ps = a.st->slot;
+    if (ps >= c0 && ps < c1) {
+      const size_t roff = static_cast<size_t>(s) * a.ring_stream_stride +
+                          (static_cast<size_t>(ps) * hkv + kvh) * HD;
+      if (wave == 0) {
+        const float* kr = qkv + (hq + kvh) * HD;
+        const int ia = a.rope_style == 0 ? lane : 2 * lane;
+        const int ib = a.rope_style == 0 ? lane + HALF : 2 * lane + 1;
+        float va = lane < HALF ? kr[ia] : 0.f, vb = lane < HALF ? kr[ib] : 0.f;
+        norm_rope_pair<HD>(va, vb, lane, a.k_norm, a.eps, a.cs, a.rope_style);
+        if (lane < HALF) {
+          a.k_ring[roff + ia] = va;
+          a.k_ring[roff + ib] = vb;
+        }
+      } else if (wave == 1) {
+        const float* vr = qkv + (hq + hkv + kvh) * HD;
+        for (int d = lane; d < HD; d += kWave) a.v_ring[roff + d] = vr[d];
+      }
+    }
+  }
+  __syncthreads();  // list, queries and the pushed slot are visible to the whole workgroup
+
+  // 4. online softmax over this group's share of the legal slots
   float q[G][8];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float4* qp = reinterpret_cast<const float4*>(
-        a.q + static_cast<size_t>(s) * hq * HD + (h0 + g) * HD + 8 * sub);
-    const float4 q0 = qp[0], q1 = qp[1];
-    q[g][0] = q0.x; q[g][1] = q0.y; q[g][2] = q0.z; q[g][3] = q0.w;
-    q[g][4] = q1.x; q[g][5] = q1.y; q[g][6] = q1.z; q[g][7] = q1.w;
-  }
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[g][e] = qs[g][8 * sub + e];
   const float scale = 1.0f / sqrtf(static_cast<float>(HD));
   float mrun[G], lrun[G], acc[G][8];
 #pragma unroll
@@ -389,7 +560,7 @@ __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
     }
   }
 
-  // 3. merge the slot groups of this workgroup
+  // 5. merge the slot groups of this workgroup into the chunk's (max, sum, output)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (sub == 0) {
@@ -418,40 +589,80 @@ __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
       a.out[static_cast<size_t>(s) * hq * HD + (h0 + g) * HD + d] = L > 0.f ? O / L : 0.f;
     } else {
       float* pp = a.part + ((static_cast<size_t>(s) * hq + h0 + g) * a.n_chunks + chunk) * (HD + 2);
-      pp[d] = O;
+      st_dev(pp + d, O);
       if (d == 0) {
-        pp[HD] = M;
-        pp[HD + 1] = L;
+        st_dev(pp + HD, M);
+        st_dev(pp + HD + 1, L);
       }
     }
   }
   if (single) return;
 
-  // 4. the last chunk of this (stream, kv head) to finish merges all chunks
-  __threadfence();
+  // 6. the last chunk of this (stream, kv head) to finish merges all chunks.  The partials went
+  // out with device-coherent stores; they are complete before this workgroup's count is added.
+  wait_stores();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = atomicAdd(&a.counters[s * hkv + kvh], 1u);
+    const uint32_t prev = __hip_atomic_fetch_add(&a.counters[s * hkv + kvh], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
     is_last = prev == a.n_chunks - 1 ? 1u : 0u;
   }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
-  for (int t = tid; t < G * HD; t += kWgThreads) {
-    const int g = t / HD, d = t % HD;
-    const float* base = a.part + (static_cast<size_t>(s) * hq + h0 + g) * a.n_chunks * (HD + 2);
-    float M = -INFINITY;
-    for (uint32_t c = 0; c < a.n_chunks; ++c) M = fmaxf(M, base[c * (HD + 2) + HD]);
-    float L = 0.f, O = 0.f;
-    for (uint32_t c = 0; c < a.n_chunks; ++c) {
-      const float mc = base[c * (HD + 2) + HD];
-      if (mc != -INFINITY) {
-        const float w = expf(mc - M);
-        L = fmaf(w, base[c * (HD + 2) + HD + 1], L);
-        O = fmaf(w, base[c * (HD + 2) + d], O);
+  float* stage = &sm_acc[0][0][0];  // [CB][G][HD]
+  float Mr[(G * HD + kWgThreads - 1) / kWgThreads], Lr[(G * HD + kWgThreads - 1) / kWgThreads];
+  float Or[(G * HD + kWgThreads - 1) / kWgThreads];
+#pragma unroll
+  for (int i = 0; i < (G * HD + kWgThreads - 1) / kWgThreads; ++i) {
+    Mr[i] = -INFINITY;
+    Lr[i] = 0.f;
+    Or[i] = 0.f;
+  }
+  for (uint32_t b0 = 0; b0 < a.n_chunks; b0 += CB) {
+    const uint32_t nb = min(static_cast<uint32_t>(CB), a.n_chunks - b0);
+    __syncthreads();  // the previous batch is consumed
+    for (uint32_t e = tid; e < nb * G * (HD + 2); e += kWgThreads) {
+      const uint32_t c = e / (G * (HD + 2)), rem = e % (G * (HD + 2));
+      const uint32_t g = rem / (HD + 2), d = rem % (HD + 2);
+      const float v = ld_dev(a.part + ((static_cast<size_t>(s) * hq + h0 + g) * a.n_chunks + b0 + c) *
+                                          (HD + 2) + d);
+      if (d < HD) stage[(c * G + g) * HD + d] = v;
+      else if (d == HD) sm_m[c][g] = v;
+      else sm_l[c][g] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < (G * HD + kWgThreads - 1) / kWgThreads; ++i) {
+      const int t = tid + i * kWgThreads;
+      if (t < G * HD) {
+        const int g = t / HD, d = t % HD;
+        float Mb = Mr[i];
+        for (uint32_t c = 0; c < nb; ++c) Mb = fmaxf(Mb, sm_m[c][g]);
+        if (Mb != -INFINITY) {
+          const float corr = Mr[i] != -INFINITY ? expf(Mr[i] - Mb) : 0.f;
+          float L = Lr[i] * corr, O = Or[i] * corr;
+          for (uint32_t c = 0; c < nb; ++c) {
+            const float mc = sm_m[c][g];
+            if (mc != -INFINITY) {
+              const float w = expf(mc - Mb);
+              L = fmaf(w, sm_l[c][g], L);
+              O = fmaf(w, stage[(c * G + g) * HD + d], O);
+            }
+          }
+          Mr[i] = Mb;
+          Lr[i] = L;
+          Or[i] = O;
+        }
       }
     }
-    a.out[static_cast<size_t>(s) * hq * HD + (h0 + g) * HD + d] = L > 0.f ? O / L : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < (G * HD + kWgThreads - 1) / kWgThreads; ++i) {
+    const int t = tid + i * kWgThreads;
+    if (t < G * HD) {
+      const int g = t / HD, d = t % HD;
+      a.out[static_cast<size_t>(s) * hq * HD + (h0 + g) * HD + d] = Lr[i] > 0.f ? Or[i] / Lr[i] : 0.f;
+    }
   }
   if (tid == 0) a.counters[s * hkv + kvh] = 0u;
 }
@@ -551,31 +762,64 @@ __global__ void k_fill_f32(float* p, float v, uint64_t n) {
     p[i] = v;
 }
 
+// The kernel a launch plan names, and its dynamic LDS.
+struct GemvKernel {
+  const void* fn;
+  size_t lds;
+};
+
 template <int M, int R, int PRO, int EPI>
-hipError_t launch_gemv_t(const GemvArgs& a, const GemvLaunch& l, hipStream_t s) {
-  const size_t lds = PRO == PRO_NONE ? 0 : static_cast<size_t>(M) * a.k * sizeof(float);
-  hipLaunchKernelGGL((k_gemv<M, R, PRO, EPI>), dim3(l.grid), dim3(l.waves_per_wg * kWave), lds,
-                     s, a);
-  return hipGetLastError();
+GemvKernel gemv_generic(uint32_t k) {
+  return {reinterpret_cast<const void*>(&k_gemv<M, R, PRO, EPI>),
+          PRO == PRO_NONE ? 0 : static_cast<size_t>(M) * k * sizeof(float)};
+}
+
+template <int M, int R, int PRO, int EPI>
+GemvKernel gemv_rx(int kb) {
+  switch (kb) {
+    case 2: return {reinterpret_cast<const void*>(&k_gemv_rx<M, R, PRO, EPI, 2>), 0};
+    case 8: return {reinterpret_cast<const void*>(&k_gemv_rx<M, R, PRO, EPI, 8>), 0};
+    case 24:
+      if constexpr (M == 1 && R == 1)
+        return {reinterpret_cast<const void*>(&k_gemv_rx<M, R, PRO, EPI, 24>), 0};
+      break;
+    default: break;
+  }
+  return {nullptr, 0};
 }
 
 template <int M, int PRO, int EPI>
-hipError_t launch_gemv_r(const GemvArgs& a, const GemvLaunch& l, hipStream_t s) {
+GemvKernel gemv_pick_r(const GemvLaunch& l, uint32_t k) {
+  if (l.kb > 0) {
+    if constexpr (M <= 2) {
+      switch (l.rows_per_wave) {
+        case 1:
+          if constexpr (EPI != EPI_SWIGLU) return gemv_rx<M, 1, PRO, EPI>(l.kb);
+          break;
+        case 2: return gemv_rx<M, 2, PRO, EPI>(l.kb);
+        case 4:
+          if constexpr (M == 1) return gemv_rx<M, 4, PRO, EPI>(l.kb);
+          break;
+        default: break;
+      }
+    }
+    return {nullptr, 0};
+  }
   switch (l.rows_per_wave) {
     case 1:
-      if constexpr (EPI != EPI_SWIGLU) return launch_gemv_t<M, 1, PRO, EPI>(a, l, s);
+      if constexpr (EPI != EPI_SWIGLU) return gemv_generic<M, 1, PRO, EPI>(k);
       break;
-    case 2: return launch_gemv_t<M, 2, PRO, EPI>(a, l, s);
-    case 4: return launch_gemv_t<M, 4, PRO, EPI>(a, l, s);
+    case 2: return gemv_generic<M, 2, PRO, EPI>(k);
+    case 4: return gemv_generic<M, 4, PRO, EPI>(k);
     default: break;
   }
-  return hipErrorInvalidValue;
+  return {nullptr, 0};
 }
 
 template <int M>
-hipError_t launch_gemv_m(const GemvArgs& a, const GemvLaunch& l, hipStream_t s) {
+GemvKernel gemv_pick_m(const GemvLaunch& l, uint32_t k) {
 #define SDEC_KIND(P, E) \
-  if (l.prologue == P && l.epilogue == E) return launch_gemv_r<M, P, E>(a, l, s);
+  if (l.prologue == P && l.epilogue == E) return gemv_pick_r<M, P, E>(l, k);
   SDEC_KIND(PRO_NONE, EPI_STORE)
   SDEC_KIND(PRO_NONE, EPI_RESIDUAL)
   SDEC_KIND(PRO_RMS, EPI_STORE)
@@ -585,7 +829,7 @@ hipError_t launch_gemv_m(const GemvArgs& a, const GemvLaunch& l, hipStream_t s) 
   SDEC_KIND(PRO_LN, EPI_SWIGLU)
   SDEC_KIND(PRO_LN, EPI_GELU)
 #undef SDEC_KIND
-  return hipErrorInvalidValue;
+  return {nullptr, 0};
 }
 
 template <int HD>
@@ -605,38 +849,71 @@ hipError_t launch_attention_hd(const AttnArgs& a, hipStream_t s) {
 // Rows m are processed as M = next power of two (unused rows read zeros, write nothing).
 static int round_m(uint32_t m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8; }
 
+static int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v && *v ? atoi(v) : dflt;
+}
+
+static GemvKernel gemv_pick(const GemvLaunch& l, uint32_t k, uint32_t m) {
+  switch (round_m(m)) {
+    case 1: return gemv_pick_m<1>(l, k);
+    case 2: return gemv_pick_m<2>(l, k);
+    case 4: return gemv_pick_m<4>(l, k);
+    default: return gemv_pick_m<8>(l, k);
+  }
+}
+
 GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, uint32_t m) {
-  (void)k;
   GemvLaunch l;
   l.prologue = prologue;
   l.epilogue = epilogue;
   const int M = round_m(m);
-  l.rows_per_wave = M == 1 ? (epilogue == EPI_SWIGLU ? 2 : 1) : (M == 2 ? 2 : 4);
-  if (epilogue == EPI_SWIGLU && l.rows_per_wave < 2) l.rows_per_wave = 2;
+  const uint32_t kb = k % 256 == 0 ? k / 256 : 0;
+  l.kb = 0;
+  if (M <= 2 && (kb == 2 || kb == 8)) l.kb = static_cast<int>(kb);
+  if (M == 1 && kb == 24 && epilogue != EPI_SWIGLU) l.kb = 24;
+  if (l.kb > 0) {
+    // rows in flight per wave: enough 16-byte loads per lane to cover the HBM latency
+    if (epilogue == EPI_SWIGLU) l.rows_per_wave = 2;
+    else if (l.kb == 2) l.rows_per_wave = M == 1 ? 4 : 2;
+    else l.rows_per_wave = 1;
+  } else {
+    l.rows_per_wave = M == 1 ? (epilogue == EPI_SWIGLU ? 2 : 1) : (M == 2 ? 2 : 4);
+  }
   l.waves_per_wg = kWgThreads / kWave;
   const int rh = epilogue == EPI_SWIGLU ? l.rows_per_wave / 2 : l.rows_per_wave;
   const uint32_t tiles = (n_rows + rh - 1) / rh;
-  const uint32_t wgs = (tiles + l.waves_per_wg - 1) / l.waves_per_wg;
+  // Resident waves only: every wave owns a contiguous range of tiles, so a grid larger than what
+  // the device holds at once would leave a second, serial round of workgroups.
+  int dev = 0, cus = 256, occ = 1;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const GemvKernel kern = gemv_pick(l, k, m);
+  if (kern.fn == nullptr ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern.fn, kWgThreads, kern.lds) !=
+          hipSuccess || occ < 1)
+    occ = 1;
+  const int cap = env_int("SDEC_GEMV_WGS_PER_CU", 4);
+  if (occ > cap) occ = cap;
+  const uint32_t max_wgs = static_cast<uint32_t>(cus * occ);
+  uint32_t wgs = (tiles + l.waves_per_wg - 1) / l.waves_per_wg;
+  if (wgs > max_wgs) wgs = max_wgs;
   l.grid = wgs < 1 ? 1 : wgs;
   return l;
 }
 
 hipError_t launch_gemv(const GemvArgs& a, const GemvLaunch& l, hipStream_t s) {
-  switch (round_m(a.m)) {
-    case 1: return launch_gemv_m<1>(a, l, s);
-    case 2: return launch_gemv_m<2>(a, l, s);
-    case 4: return launch_gemv_m<4>(a, l, s);
-    default: return launch_gemv_m<8>(a, l, s);
-  }
+  const GemvKernel kern = gemv_pick(l, a.k, a.m);
+  if (kern.fn == nullptr) return hipErrorInvalidValue;
+  GemvArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchKernel(kern.fn, dim3(l.grid), dim3(l.waves_per_wg * kWave), params, kern.lds, s);
 }
 
-hipError_t launch_qk_rope_push(const QkRopeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_qk_rope_push, dim3(a.n_q_heads + a.n_kv_heads, a.m), dim3(kWave), 0, s,
-                     a);
-  return hipGetLastError();
+uint32_t attention_chunk(uint32_t head_dim) {
+  (void)head_dim;
+  return 128u;
 }
-
-uint32_t attention_chunk(uint32_t head_dim) { return head_dim == 128 ? 64u : 64u; }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.head_dim == 128) return launch_attention_hd<128>(a, s);

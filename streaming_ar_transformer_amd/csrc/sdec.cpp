@@ -56,7 +56,6 @@ struct sdec_handle {
   uint32_t* pos_rings = nullptr;  // [m][R]
   float* xres = nullptr;      // [m][d]
   float* qkv = nullptr;       // [m][(Hq+2Hkv)hd]
-  float* q_out = nullptr;     // [m][Hq hd]
   float* attn_out = nullptr;  // [m][Hq hd], or [L][m][Hq hd] with taps
   float* act = nullptr;       // [m][d_ff]
   float* part = nullptr;      // [m][Hq][n_chunks][hd+2]
@@ -101,7 +100,7 @@ struct Alloc {
 };
 
 void free_handle_memory(sdec_handle* h) {
-  void* ps[] = {h->k_rings, h->v_rings, h->pos_rings, h->xres, h->qkv, h->q_out, h->attn_out,
+  void* ps[] = {h->k_rings, h->v_rings, h->pos_rings, h->xres, h->qkv, h->attn_out,
                 h->act, h->part, h->counters, h->cs, h->st, h->tap_attn_proj, h->tap_ffn_proj};
   for (void* p : ps)
     if (p) (void)hipFree(p);
@@ -220,20 +219,14 @@ int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk) {
     g.norm_w = w.attn_norm_w; g.norm_b = w.attn_norm_b; g.eps = c.norm_eps;
     g.y = h->qkv; g.y_stride = nqkv;
     LAUNCH(hk, s, SDEC_K_QKV, launch_gemv(g, h->plan_qkv[l], s));
-    // qk-norm + rope + ring push
-    QkRopeArgs qa{};
-    qa.qkv = h->qkv; qa.qkv_stride = nqkv; qa.q_out = h->q_out;
-    qa.k_ring = ring_at(h, h->k_rings, 0, l); qa.v_ring = ring_at(h, h->v_rings, 0, l);
-    qa.ring_stream_stride = h->ring_stream_stride;
-    qa.n_q_heads = hq; qa.n_kv_heads = hkv; qa.head_dim = hd; qa.m = c.m;
-    qa.q_norm = c.qk_norm ? w.q_norm : nullptr; qa.k_norm = c.qk_norm ? w.k_norm : nullptr;
-    qa.eps = c.qk_norm_eps; qa.rope_style = c.rope == SDEC_ROPE_HALF ? 0 : 1;
-    qa.cs = h->cs; qa.st = h->st;
-    LAUNCH(hk, s, SDEC_K_QK_ROPE_PUSH, launch_qk_rope_push(qa, s));
-    // ring attention
+    // ring attention; it also finishes this step's q/k (qk-norm, rope) and pushes k/v
     float* att = taps ? h->attn_out + static_cast<size_t>(l) * c.m * qw : h->attn_out;
     AttnArgs aa{};
-    aa.q = h->q_out; aa.k_ring = qa.k_ring; aa.v_ring = qa.v_ring;
+    aa.qkv = h->qkv; aa.qkv_stride = nqkv;
+    aa.q_norm = c.qk_norm ? w.q_norm : nullptr; aa.k_norm = c.qk_norm ? w.k_norm : nullptr;
+    aa.eps = c.qk_norm_eps; aa.rope_style = c.rope == SDEC_ROPE_HALF ? 0 : 1; aa.cs = h->cs;
+    aa.push = 1;
+    aa.k_ring = ring_at(h, h->k_rings, 0, l); aa.v_ring = ring_at(h, h->v_rings, 0, l);
     aa.ring_stream_stride = h->ring_stream_stride;
     aa.pos_ring = h->pos_rings; aa.pos_stream_stride = h->ring;
     aa.out = att; aa.part = h->part; aa.counters = h->counters;
@@ -358,7 +351,6 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
   h->pos_rings = A.get<uint32_t>(static_cast<size_t>(c.m) * ring_slots);
   h->xres = A.get<float>(static_cast<size_t>(c.m) * c.d_model);
   h->qkv = A.get<float>(static_cast<size_t>(c.m) * (qw + 2 * kw));
-  h->q_out = A.get<float>(static_cast<size_t>(c.m) * qw);
   h->attn_out = A.get<float>(static_cast<size_t>(c.m) * qw * (taps ? c.n_layers : 1));
   h->act = A.get<float>(static_cast<size_t>(c.m) * c.d_ff);
   h->part = A.get<float>(static_cast<size_t>(c.m) * hq * h->n_chunks * (hd + 2));
@@ -443,7 +435,7 @@ int sdec_step_profile(sdec_handle* h, float* x, uint32_t pos, uint32_t first, vo
   if (r != SDEC_OK) return r;
   if (!ms || !calls) return fail(SDEC_E_ARG, "null timing arrays");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int cap = 2 + 6 * static_cast<int>(h->cfg.n_layers);
+  const int cap = 2 + 5 * static_cast<int>(h->cfg.n_layers);
   std::vector<hipEvent_t> ev(2 * cap, nullptr);
   std::vector<int> kinds(cap, 0);
   for (auto& e : ev) HIP_TRY(hipEventCreate(&e));
@@ -579,7 +571,9 @@ int sdec_ring_attention(const float* q, const float* k_ring, const float* v_ring
     HIP_TRY(launch_fill_u32(counters, 0u, cnt_cap, s));
   }
   AttnArgs a{};
-  a.q = q; a.k_ring = k_ring; a.v_ring = v_ring;
+  a.qkv = q; a.qkv_stride = n_q_heads * head_dim;
+  a.q_norm = a.k_norm = nullptr; a.cs = nullptr; a.push = 0;
+  a.k_ring = const_cast<float*>(k_ring); a.v_ring = const_cast<float*>(v_ring);
   a.ring_stream_stride = static_cast<uint64_t>(ring_slots) * n_kv_heads * head_dim;
   a.pos_ring = pos_ring; a.pos_stream_stride = ring_slots; a.out = out; a.part = part;
   a.counters = counters; a.m = m; a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads;

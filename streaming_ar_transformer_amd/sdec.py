@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libsdec.so")
 
 OK, E_ARG, E_POS, E_CAPACITY, E_HIP, E_NOMEM = 0, -1, -2, -3, -4, -5
 FLAG_EAGER, FLAG_TAPS = 1, 2
-K_NAMES = ["begin", "qkv", "qk_rope_push", "attention", "o_proj", "ffn_up", "ffn_down", "end"]
+K_NAMES = ["begin", "qkv", "attention", "o_proj", "ffn_up", "ffn_down", "end"]
 
 # Every symbol include/sdec.h declares.
 EXPORTS = ["sdec_create", "sdec_step", "sdec_reset", "sdec_destroy", "sdec_last_error",
