@@ -1,0 +1,455 @@
+// Device helpers shared by the per-kernel step path (kernels.hip) and the persistent step kernel
+// (step.hip).  Page names in citations: [talker] inferencelayer 0.2.8 src/qwen3tts_gpu.rs,
+// [mimi] 0.2.1 src/mimi_gpu.rs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace sdec {
+namespace dev {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float4 f4zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+
+// Weights are streamed once per step: load them non-temporally so they do not displace the
+// small, reused activations from the caches.
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ldw(const float4* p) {
+  const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// Device-coherent (agent-scope) stores and loads: they bypass the per-XCD cache state, so data
+// handed between workgroups needs no cache-wide writeback or invalidate -- only completion of the
+// stores before the hand-off counter is bumped.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+// A store that is coherent across the device when COH (a hand-off to other workgroups of the
+// same launch), or an ordinary store.
+template <bool COH>
+__device__ __forceinline__ void put(float* p, float v) {
+  if (COH) st_dev(p, v);
+  else *p = v;
+}
+
+__device__ __forceinline__ float dot4(float4 w, float4 x, float acc) {
+  acc = fmaf(w.x, x.x, acc);
+  acc = fmaf(w.y, x.y, acc);
+  acc = fmaf(w.z, x.z, acc);
+  return fmaf(w.w, x.w, acc);
+}
+
+// Butterfly reduce-scatter of V per-lane partial sums across the wave.  Each halving step swaps
+// half of the values with the lane `off` away, so after log2(V) steps lane l holds the wave total
+// of value index l / (64 / V); the remaining offsets finish the sum inside each lane group.
+template <int V, int OFF>
+struct ReduceScatter {
+  static __device__ __forceinline__ void run(float* v, int lane) {
+    constexpr int H = V / 2;
+    const bool upper = (lane & OFF) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const float send = upper ? v[i] : v[i + H];
+      const float keep = upper ? v[i + H] : v[i];
+      v[i] = keep + __shfl_xor(send, OFF, kWave);
+    }
+    ReduceScatter<H, OFF / 2>::run(v, lane);
+  }
+};
+template <int OFF>
+struct ReduceScatter<1, OFF> {
+  static __device__ __forceinline__ void run(float* v, int) {
+#pragma unroll
+    for (int off = OFF; off > 0; off >>= 1) v[0] += __shfl_xor(v[0], off, kWave);
+  }
+};
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+__device__ __forceinline__ float gelu_erf(float v) {
+  return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
+}
+
+// ------------------------------------------------------------------------------------------------
+// qk-RMSNorm + rope of one head pair ([talker] QK_NORM_SRC then ROPE_SRC; [mimi] rope_push_src).
+// Lane j owns rope pair j: (j, j + hd/2) for rotate_half, (2j, 2j + 1) for the interleaved form;
+// both are the rotation (a, b) -> (a c - b s, a s + b c).  Called by a whole wave.
+// ------------------------------------------------------------------------------------------------
+template <int HD>
+__device__ __forceinline__ void norm_rope_pair(float& va, float& vb, int j, const float* gnorm,
+                                               float eps, const float* cs, int style) {
+  constexpr int HALF = HD / 2;
+  const bool act = j < HALF;
+  if (gnorm != nullptr) {
+    const float ss = wave_sum(act ? va * va + vb * vb : 0.f);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(HD) + eps);
+    if (act) {
+      const int ia = style == 0 ? j : 2 * j, ib = style == 0 ? j + HALF : 2 * j + 1;
+      va = (va * inv) * gnorm[ia];
+      vb = (vb * inv) * gnorm[ib];
+    }
+  }
+  if (cs != nullptr && act) {
+    const float c = cs[j], sn = cs[HALF + j];
+    const float ra = va * c - vb * sn;
+    const float rb = va * sn + vb * c;
+    va = ra;
+    vb = rb;
+  }
+}
+
+template <int R, int EPI>
+__device__ __forceinline__ void tile_rows(const GemvArgs& a, uint32_t t, const float4* (&wr)[R]) {
+  constexpr int RH = EPI == EPI_SWIGLU ? R / 2 : R;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    uint32_t row;
+    const float* base;
+    if (EPI == EPI_SWIGLU) {
+      row = min(t * RH + (r % RH), a.n_rows - 1);
+      base = r < RH ? a.w[0] : a.w[1];
+    } else {
+      row = min(t * RH + r, a.n_rows - 1);
+      if (row < a.seg_end[0]) {
+        base = a.w[0];
+      } else if (row < a.seg_end[1]) {
+        base = a.w[1];
+        row -= a.seg_end[0];
+      } else {
+        base = a.w[2];
+        row -= a.seg_end[1];
+      }
+    }
+    wr[r] = reinterpret_cast<const float4*>(base + static_cast<size_t>(row) * a.k);
+  }
+}
+
+// Reduce the tile's R*M lane partials and apply the epilogue: store, GELU, SwiGLU (gate row r and
+// up row r + R/2 of the same FFN index sit 32 lanes apart after the reduce-scatter), or the
+// (LayerScale) residual add ([mimi] MV_LS: y += ls * (W x)).
+template <int M, int R, int EPI, bool COH = false>
+__device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, uint32_t t, float* acc, int lane) {
+  constexpr int V = R * M;
+  constexpr int S = kWave / V;
+  constexpr int RH = EPI == EPI_SWIGLU ? R / 2 : R;
+  ReduceScatter<V, 32>::run(acc, lane);
+  const float val = acc[0];
+  const int idx = lane / S;
+  const bool owner = (lane % S) == 0;
+  const int r = idx / M, m = idx % M;
+  if (EPI == EPI_SWIGLU) {
+    const float up = __shfl_xor(val, 32, kWave);
+    const uint32_t i = t * RH + r;
+    if (owner && lane < 32 && i < a.n_rows && m < static_cast<int>(a.m))
+      put<COH>(a.y + m * a.y_stride + i, silu(val) * up);
+  } else {
+    const uint32_t row = t * RH + r;
+    if (owner && row < a.n_rows && m < static_cast<int>(a.m)) {
+      if (EPI == EPI_STORE) {
+        put<COH>(a.y + m * a.y_stride + row, val);
+      } else if (EPI == EPI_GELU) {
+        put<COH>(a.y + m * a.y_stride + row, gelu_erf(val));
+      } else {
+        if (a.tap) a.tap[m * a.tap_stride + row] = val;
+        const float* src = (a.res_in ? a.res_in : a.res) + m * a.res_stride + row;
+        put<COH>(a.res + m * a.res_stride + row, *src + (a.ls ? a.ls[row] * val : val));
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void wave_tiles(uint32_t n_tiles, uint32_t& t, uint32_t& t_end) {
+  const uint32_t nw = blockDim.x / kWave;
+  const uint32_t gw = blockIdx.x * nw + threadIdx.x / kWave;
+  const uint64_t nwaves = static_cast<uint64_t>(gridDim.x) * nw;
+  t = static_cast<uint32_t>(gw * static_cast<uint64_t>(n_tiles) / nwaves);
+  t_end = static_cast<uint32_t>((gw + 1) * static_cast<uint64_t>(n_tiles) / nwaves);
+}
+
+template <int HD, int G, int NT>
+struct AttnSmem {
+  static constexpr int LPS = HD / 8;
+  static constexpr int NG = (NT / kWave) * (kWave / LPS);
+  uint32_t list[NT];
+  uint32_t wave_cnt[NT / kWave];
+  float qs[G][HD];
+  float sm_m[NG][G], sm_l[NG][G];
+  float sm_acc[NG][G][HD];
+  uint32_t is_last;
+};
+
+// One (slot chunk, kv head, stream) work item, run by a whole workgroup of NT threads.  COH: the
+// output is handed to other workgroups of the same launch.
+template <int HD, int G, int NT, bool COH>
+__device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk, uint32_t kvh,
+                                               uint32_t s, AttnSmem<HD, G, NT>& sm) {
+  constexpr int LPS = HD / 8;
+  constexpr int GPW = kWave / LPS;
+  constexpr int NWV = NT / kWave;
+  constexpr int NG = NWV * GPW;
+  constexpr int UNR = 4;
+  constexpr int HALF = HD / 2;
+  constexpr int CB = 16;  // chunks merged per batch by the last workgroup
+  static_assert(CB <= NG, "combine staging reuses the group buffers");
+  uint32_t* list = sm.list;
+  uint32_t* wave_cnt = sm.wave_cnt;
+  auto& qs = sm.qs;
+  auto& sm_m = sm.sm_m;
+  auto& sm_l = sm.sm_l;
+  auto& sm_acc = sm.sm_acc;
+  uint32_t& is_last = sm.is_last;
+  __syncthreads();  // the previous item of this workgroup is done with the LDS
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int grp = wave * GPW + lane / LPS;
+  const int sub = lane % LPS;
+    const uint32_t pos = a.st ? a.st->pos : a.pos;
+  const uint32_t c0 = chunk * a.chunk;
+  const uint32_t c1 = min(c0 + a.chunk, a.ring);
+  const uint32_t hq = a.n_q_heads, hkv = a.n_kv_heads;
+  const uint32_t h0 = kvh * G;
+  const float* qkv = a.qkv + static_cast<size_t>(s) * a.qkv_stride;
+
+  // 1. legal slots of the chunk, in slot order; this step's raw queries
+  const uint32_t slot = c0 + tid;
+  bool ok = false;
+  if (slot < c1) {
+    const uint32_t p = a.pos_ring[static_cast<size_t>(s) * a.pos_stream_stride + slot];
+    ok = p != kInvalidPos && p <= pos && pos - p < a.window;
+  }
+  const unsigned long long mask = __ballot(ok);
+  const uint32_t before = __popcll(mask & ((1ull << lane) - 1ull));
+  if (lane == 0) wave_cnt[wave] = __popcll(mask);
+  for (int t = tid; t < G * HD; t += NT) qs[t / HD][t % HD] = qkv[(h0 + t / HD) * HD + t % HD];
+  __syncthreads();
+  uint32_t off = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    off += w < wave ? wave_cnt[w] : 0u;
+    total += wave_cnt[w];
+  }
+  if (ok) list[off + before] = slot;
+
+  // 2. queries: qk-norm + rope, one wave per head
+  if (a.q_norm != nullptr || a.cs != nullptr) {
+    for (int g = wave; g < G; g += NWV) {
+      const int ia = a.rope_style == 0 ? lane : 2 * lane;
+      const int ib = a.rope_style == 0 ? lane + HALF : 2 * lane + 1;
+      float va = lane < HALF ? qs[g][ia] : 0.f, vb = lane < HALF ? qs[g][ib] : 0.f;
+      norm_rope_pair<HD>(va, vb, lane, a.q_norm, a.eps, a.cs, a.rope_style);
+      if (lane < HALF) {
+        qs[g][ia] = va;
+        qs[g][ib] = vb;
+      }
+    }
+  }
+  // 3. the owner of slot pos mod R pushes this step's key (normed, roped) and value
+  if (a.push && a.st != nullptr) {
+    const uint32_t ps = a.st->slot;
+    if (ps >= c0 && ps < c1) {
+      const size_t roff = static_cast<size_t>(s) * a.ring_stream_stride +
+                          (static_cast<size_t>(ps) * hkv + kvh) * HD;
+      if (wave == 0) {
+        const float* kr = qkv + (hq + kvh) * HD;
+        const int ia = a.rope_style == 0 ? lane : 2 * lane;
+        const int ib = a.rope_style == 0 ? lane + HALF : 2 * lane + 1;
+        float va = lane < HALF ? kr[ia] : 0.f, vb = lane < HALF ? kr[ib] : 0.f;
+        norm_rope_pair<HD>(va, vb, lane, a.k_norm, a.eps, a.cs, a.rope_style);
+        if (lane < HALF) {
+          a.k_ring[roff + ia] = va;
+          a.k_ring[roff + ib] = vb;
+        }
+      } else if (wave == 1) {
+        const float* vr = qkv + (hq + hkv + kvh) * HD;
+        for (int d = lane; d < HD; d += kWave) a.v_ring[roff + d] = vr[d];
+      }
+    }
+  }
+  __syncthreads();  // list, queries and the pushed slot are visible to the whole workgroup
+
+  // 4. online softmax over this group's share of the legal slots
+  float q[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[g][e] = qs[g][8 * sub + e];
+  const float scale = 1.0f / sqrtf(static_cast<float>(HD));
+  float mrun[G], lrun[G], acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    mrun[g] = -INFINITY;
+    lrun[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  }
+  const size_t row = static_cast<size_t>(hkv) * HD;
+  const float* kb = a.k_ring + static_cast<size_t>(s) * a.ring_stream_stride + kvh * HD + 8 * sub;
+  const float* vb = a.v_ring + static_cast<size_t>(s) * a.ring_stream_stride + kvh * HD + 8 * sub;
+  for (uint32_t i0 = grp; i0 < total; i0 += NG * UNR) {
+    float4 kk[UNR][2], vv[UNR][2];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const uint32_t i = i0 + u * NG;
+      if (i < total) {
+        const size_t sl = list[i];
+        const float4* kp = reinterpret_cast<const float4*>(kb + sl * row);
+        const float4* vp = reinterpret_cast<const float4*>(vb + sl * row);
+        kk[u][0] = kp[0]; kk[u][1] = kp[1];
+        vv[u][0] = vp[0]; vv[u][1] = vp[1];
+      } else {
+        kk[u][0] = kk[u][1] = vv[u][0] = vv[u][1] = f4zero();
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (i0 + u * NG < total) {
+        const float kf[8] = {kk[u][0].x, kk[u][0].y, kk[u][0].z, kk[u][0].w,
+                             kk[u][1].x, kk[u][1].y, kk[u][1].z, kk[u][1].w};
+        const float vf[8] = {vv[u][0].x, vv[u][0].y, vv[u][0].z, vv[u][0].w,
+                             vv[u][1].x, vv[u][1].y, vv[u][1].z, vv[u][1].w};
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d = fmaf(q[g][e], kf[e], d);
+#pragma unroll
+          for (int o = LPS / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, kWave);
+          const float sc = d * scale;
+          const float mnew = fmaxf(mrun[g], sc);
+          const float corr = expf(mrun[g] - mnew);
+          const float p = expf(sc - mnew);
+          lrun[g] = lrun[g] * corr + p;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[g][e] = acc[g][e] * corr + p * vf[e];
+          mrun[g] = mnew;
+        }
+      }
+    }
+  }
+
+  // 5. merge the slot groups of this workgroup into the chunk's (max, sum, output)
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (sub == 0) {
+      sm_m[grp][g] = mrun[g];
+      sm_l[grp][g] = lrun[g];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm_acc[grp][g][8 * sub + e] = acc[g][e];
+  }
+  __syncthreads();
+  const bool single = a.n_chunks == 1;
+  for (int t = tid; t < G * HD; t += NT) {
+    const int g = t / HD, d = t % HD;
+    float M = -INFINITY;
+    for (int k = 0; k < NG; ++k) M = fmaxf(M, sm_m[k][g]);
+    float L = 0.f, O = 0.f;
+    for (int k = 0; k < NG; ++k) {
+      const float mk = sm_m[k][g];
+      if (mk != -INFINITY) {
+        const float w = expf(mk - M);
+        L = fmaf(w, sm_l[k][g], L);
+        O = fmaf(w, sm_acc[k][g][d], O);
+      }
+    }
+    if (single) {
+      put<COH>(a.out + static_cast<size_t>(s) * hq * HD + (h0 + g) * HD + d, L > 0.f ? O / L : 0.f);
+    } else {
+      float* pp = a.part + ((static_cast<size_t>(s) * hq + h0 + g) * a.n_chunks + chunk) * (HD + 2);
+      st_dev(pp + d, O);
+      if (d == 0) {
+        st_dev(pp + HD, M);
+        st_dev(pp + HD + 1, L);
+      }
+    }
+  }
+  if (single) return;
+
+  // 6. the last chunk of this (stream, kv head) to finish merges all chunks.  The partials went
+  // out with device-coherent stores; they are complete before this workgroup's count is added.
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&a.counters[s * hkv + kvh], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    is_last = prev == a.n_chunks - 1 ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!is_last) return;
+  float* stage = &sm_acc[0][0][0];  // [CB][G][HD]
+  float Mr[(G * HD + NT - 1) / NT], Lr[(G * HD + NT - 1) / NT];
+  float Or[(G * HD + NT - 1) / NT];
+#pragma unroll
+  for (int i = 0; i < (G * HD + NT - 1) / NT; ++i) {
+    Mr[i] = -INFINITY;
+    Lr[i] = 0.f;
+    Or[i] = 0.f;
+  }
+  for (uint32_t b0 = 0; b0 < a.n_chunks; b0 += CB) {
+    const uint32_t nb = min(static_cast<uint32_t>(CB), a.n_chunks - b0);
+    __syncthreads();  // the previous batch is consumed
+    for (uint32_t e = tid; e < nb * G * (HD + 2); e += NT) {
+      const uint32_t c = e / (G * (HD + 2)), rem = e % (G * (HD + 2));
+      const uint32_t g = rem / (HD + 2), d = rem % (HD + 2);
+      const float v = ld_dev(a.part + ((static_cast<size_t>(s) * hq + h0 + g) * a.n_chunks + b0 + c) *
+                                          (HD + 2) + d);
+      if (d < HD) stage[(c * G + g) * HD + d] = v;
+      else if (d == HD) sm_m[c][g] = v;
+      else sm_l[c][g] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < (G * HD + NT - 1) / NT; ++i) {
+      const int t = tid + i * NT;
+      if (t < G * HD) {
+        const int g = t / HD, d = t % HD;
+        float Mb = Mr[i];
+        for (uint32_t c = 0; c < nb; ++c) Mb = fmaxf(Mb, sm_m[c][g]);
+        if (Mb != -INFINITY) {
+          const float corr = Mr[i] != -INFINITY ? expf(Mr[i] - Mb) : 0.f;
+          float L = Lr[i] * corr, O = Or[i] * corr;
+          for (uint32_t c = 0; c < nb; ++c) {
+            const float mc = sm_m[c][g];
+            if (mc != -INFINITY) {
+              const float w = expf(mc - Mb);
+              L = fmaf(w, sm_l[c][g], L);
+              O = fmaf(w, stage[(c * G + g) * HD + d], O);
+            }
+          }
+          Mr[i] = Mb;
+          Lr[i] = L;
+          Or[i] = O;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < (G * HD + NT - 1) / NT; ++i) {
+    const int t = tid + i * NT;
+    if (t < G * HD) {
+      const int g = t / HD, d = t % HD;
+      put<COH>(a.out + static_cast<size_t>(s) * hq * HD + (h0 + g) * HD + d,
+               Lr[i] > 0.f ? Or[i] / Lr[i] : 0.f);
+    }
+  }
+  if (tid == 0)
+    __hip_atomic_store(&a.counters[s * hkv + kvh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace dev
+}  // namespace sdec

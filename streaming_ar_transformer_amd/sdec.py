@@ -16,13 +16,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsdec.so")
 
 OK, E_ARG, E_POS, E_CAPACITY, E_HIP, E_NOMEM = 0, -1, -2, -3, -4, -5
-FLAG_EAGER, FLAG_TAPS = 1, 2
+FLAG_EAGER, FLAG_TAPS, FLAG_PERSISTENT = 1, 2, 4
+PATH_GRAPH, PATH_EAGER, PATH_PERSISTENT = 0, 1, 2
 K_NAMES = ["begin", "qkv", "attention", "o_proj", "ffn_up", "ffn_down", "end"]
 
 # Every symbol include/sdec.h declares.
 EXPORTS = ["sdec_create", "sdec_step", "sdec_reset", "sdec_destroy", "sdec_last_error",
            "sdec_kv_view", "sdec_set_next_position", "sdec_tap_view", "sdec_step_profile",
-           "sdec_gemv", "sdec_ring_attention"]
+           "sdec_gemv", "sdec_ring_attention", "sdec_status", "sdec_step_trace"]
 
 
 class SdecError(RuntimeError):
@@ -81,6 +82,9 @@ def lib():
             "sdec_step_profile": (i32, [vp, vp, u32, u32, vp, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(u32)]),
             "sdec_gemv": (i32, [vp, vp, vp, u32, u32, u32, vp]),
+            "sdec_status": (i32, [vp, ctypes.POINTER(u32), ctypes.POINTER(u32)]),
+            "sdec_step_trace": (i32, [vp, vp, u32, u32, vp, ctypes.POINTER(ctypes.c_uint64), u32,
+                                      ctypes.POINTER(ctypes.c_double)]),
             "sdec_ring_attention": (i32, [vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, u32, u32,
                                           vp]),
         }
@@ -113,7 +117,8 @@ def _ptr(t):
     return t.data_ptr()
 
 
-def make_config(cfg, window=None, unbounded=None, eager=False, taps=False) -> Config:
+def make_config(cfg, window=None, unbounded=None, eager=False, taps=False,
+                persistent=False) -> Config:
     """Fill the C struct from a ``workloads.StepConfig``-like object."""
     c = Config()
     c.n_layers, c.d_model = cfg.n_layers, cfg.d_model
@@ -125,7 +130,8 @@ def make_config(cfg, window=None, unbounded=None, eager=False, taps=False) -> Co
     c.ffn, c.layer_scale, c.final_norm = cfg.ffn, int(cfg.layer_scale), int(cfg.final_norm)
     c.window = cfg.window if window is None else window
     c.unbounded = int((cfg.family == "T") if unbounded is None else unbounded)
-    c.flags = (FLAG_EAGER if eager else 0) | (FLAG_TAPS if taps else 0)
+    c.flags = (FLAG_EAGER if eager else 0) | (FLAG_TAPS if taps else 0) | \
+        (FLAG_PERSISTENT if persistent else 0)
     return c
 
 
@@ -136,10 +142,11 @@ class Decoder:
     they are borrowed (this object keeps references so they outlive the handle)."""
 
     def __init__(self, cfg, layers, final=None, ring=None, window=None, unbounded=None,
-                 eager=False, taps=False):
+                 eager=False, taps=False, persistent=False):
         self.cfg = cfg
         self.ring = cfg.ring if ring is None else ring
-        self.c = make_config(cfg, window=window, unbounded=unbounded, eager=eager, taps=taps)
+        self.c = make_config(cfg, window=window, unbounded=unbounded, eager=eager, taps=taps,
+                             persistent=persistent)
         self._keep = (layers, final)
         arr = (LayerWeights * cfg.n_layers)()
         for i, lw in enumerate(layers):
@@ -168,6 +175,27 @@ class Decoder:
             out[k][0] += ms[i]
             out[k][1] += calls[i]
         return out
+
+    def status(self):
+        """(path, device_error): the step path in use and the persistent kernel's error word."""
+        path, err = ctypes.c_uint32(), ctypes.c_uint32()
+        _check(lib().sdec_status(self.h, ctypes.byref(path), ctypes.byref(err)))
+        return path.value, err.value
+
+    @property
+    def path(self) -> int:
+        path = ctypes.c_uint32()
+        _check(lib().sdec_status(self.h, ctypes.byref(path), None))
+        return path.value
+
+    def step_trace(self, x, pos: int, first: bool = False, stream=None):
+        """One persistent step with per-barrier device-clock stamps; returns (stamps, clock_hz)."""
+        n = 2 * (1 + 5 * self.cfg.n_layers + 1)
+        ts = (ctypes.c_uint64 * n)()
+        hz = ctypes.c_double()
+        _check(lib().sdec_step_trace(self.h, _ptr(x), int(pos), int(bool(first)),
+                                     _stream(stream), ts, n, ctypes.byref(hz)))
+        return list(ts), hz.value
 
     def reset(self, stream=None):
         _check(lib().sdec_reset(self.h, _stream(stream)))
