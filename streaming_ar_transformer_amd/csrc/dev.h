@@ -181,12 +181,59 @@ __device__ __forceinline__ void wave_tiles(uint32_t n_tiles, uint32_t& t, uint32
   t_end = static_cast<uint32_t>((gw + 1) * static_cast<uint64_t>(n_tiles) / nwaves);
 }
 
+// The slots a query at `pos` may attend, from one stream's position ring ([mimi] attn_src: slot
+// j is legal iff P[j] != INVALID, P[j] <= pos and pos - P[j] < window), written to `out` in
+// ascending slot order -- after `lead` when lead >= 0 (the slot this step pushes, legal by
+// construction).  Legality depends only on the ring and pos, so one list serves every layer of
+// the step.  Called by a whole workgroup of NT threads; `scan` is NT words of LDS.
+template <int NT, bool COH>
+__device__ __forceinline__ void compact_legal(const uint32_t* P, uint32_t R, uint32_t pos,
+                                              uint32_t window, int lead, uint32_t* out,
+                                              uint32_t* n_out, uint32_t* scan) {
+  const int tid = threadIdx.x;
+  const uint32_t per = (R + NT - 1) / NT;
+  const uint32_t b = min(static_cast<uint32_t>(tid) * per, R), e = min(b + per, R);
+  auto is_legal = [&](uint32_t j) {
+    const uint32_t p = P[j];
+    return static_cast<int>(j) != lead && p != kInvalidPos && p <= pos && pos - p < window;
+  };
+  uint32_t cnt = 0;
+  for (uint32_t j = b; j < e; ++j) cnt += is_legal(j) ? 1u : 0u;
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {  // inclusive scan
+    const uint32_t v = tid >= off ? scan[tid - off] : 0u;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const uint32_t base = lead >= 0 ? 1u : 0u;
+  uint32_t o = base + scan[tid] - cnt;
+  for (uint32_t j = b; j < e; ++j) {
+    if (is_legal(j)) {
+      if (COH) __hip_atomic_store(out + o, j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else out[o] = j;
+      ++o;
+    }
+  }
+  if (tid == 0) {
+    const uint32_t n = base + scan[NT - 1];
+    if (COH) {
+      if (lead >= 0)
+        __hip_atomic_store(out, static_cast<uint32_t>(lead), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(n_out, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (lead >= 0) out[0] = static_cast<uint32_t>(lead);
+      *n_out = n;
+    }
+  }
+}
+
 template <int HD, int G, int NT>
 struct AttnSmem {
   static constexpr int LPS = HD / 8;
   static constexpr int NG = (NT / kWave) * (kWave / LPS);
   uint32_t list[NT];
-  uint32_t wave_cnt[NT / kWave];
   float qs[G][HD];
   float sm_m[NG][G], sm_l[NG][G];
   float sm_acc[NG][G][HD];
@@ -207,7 +254,6 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   constexpr int CB = 16;  // chunks merged per batch by the last workgroup
   static_assert(CB <= NG, "combine staging reuses the group buffers");
   uint32_t* list = sm.list;
-  uint32_t* wave_cnt = sm.wave_cnt;
   auto& qs = sm.qs;
   auto& sm_m = sm.sm_m;
   auto& sm_l = sm.sm_l;
@@ -218,32 +264,19 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int grp = wave * GPW + lane / LPS;
   const int sub = lane % LPS;
-    const uint32_t pos = a.st ? a.st->pos : a.pos;
-  const uint32_t c0 = chunk * a.chunk;
-  const uint32_t c1 = min(c0 + a.chunk, a.ring);
   const uint32_t hq = a.n_q_heads, hkv = a.n_kv_heads;
   const uint32_t h0 = kvh * G;
   const float* qkv = a.qkv + static_cast<size_t>(s) * a.qkv_stride;
 
-  // 1. legal slots of the chunk, in slot order; this step's raw queries
-  const uint32_t slot = c0 + tid;
-  bool ok = false;
-  if (slot < c1) {
-    const uint32_t p = a.pos_ring[static_cast<size_t>(s) * a.pos_stream_stride + slot];
-    ok = p != kInvalidPos && p <= pos && pos - p < a.window;
-  }
-  const unsigned long long mask = __ballot(ok);
-  const uint32_t before = __popcll(mask & ((1ull << lane) - 1ull));
-  if (lane == 0) wave_cnt[wave] = __popcll(mask);
+  // 1. this item's share of the step's legal slots; this step's raw queries
+  const uint32_t nl = a.n_legal[s];
+  const uint32_t n_items = (nl + a.chunk - 1) / a.chunk;
+  if (chunk >= n_items) return;  // no legal slot falls in this item
+  const uint32_t c0 = chunk * a.chunk;
+  const uint32_t total = min(a.chunk, nl - c0);
+  if (static_cast<uint32_t>(tid) < total) list[tid] = a.legal[static_cast<size_t>(s) * a.ring + c0 + tid];
   for (int t = tid; t < G * HD; t += NT) qs[t / HD][t % HD] = qkv[(h0 + t / HD) * HD + t % HD];
   __syncthreads();
-  uint32_t off = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < NWV; ++w) {
-    off += w < wave ? wave_cnt[w] : 0u;
-    total += wave_cnt[w];
-  }
-  if (ok) list[off + before] = slot;
 
   // 2. queries: qk-norm + rope, one wave per head
   if (a.q_norm != nullptr || a.cs != nullptr) {
@@ -258,10 +291,11 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
       }
     }
   }
-  // 3. the owner of slot pos mod R pushes this step's key (normed, roped) and value
-  if (a.push && a.st != nullptr) {
+  // 3. item 0, whose list starts with slot pos mod R, pushes this step's key (normed, roped) and
+  //    value
+  if (a.push && a.st != nullptr && chunk == 0) {
     const uint32_t ps = a.st->slot;
-    if (ps >= c0 && ps < c1) {
+    {
       const size_t roff = static_cast<size_t>(s) * a.ring_stream_stride +
                           (static_cast<size_t>(ps) * hkv + kvh) * HD;
       if (wave == 0) {
@@ -353,7 +387,7 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
     for (int e = 0; e < 8; ++e) sm_acc[grp][g][8 * sub + e] = acc[g][e];
   }
   __syncthreads();
-  const bool single = a.n_chunks == 1;
+  const bool single = n_items == 1;
   for (int t = tid; t < G * HD; t += NT) {
     const int g = t / HD, d = t % HD;
     float M = -INFINITY;
@@ -387,7 +421,7 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(&a.counters[s * hkv + kvh], 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-    is_last = prev == a.n_chunks - 1 ? 1u : 0u;
+    is_last = prev == n_items - 1 ? 1u : 0u;
   }
   __syncthreads();
   if (!is_last) return;
@@ -400,8 +434,8 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
     Lr[i] = 0.f;
     Or[i] = 0.f;
   }
-  for (uint32_t b0 = 0; b0 < a.n_chunks; b0 += CB) {
-    const uint32_t nb = min(static_cast<uint32_t>(CB), a.n_chunks - b0);
+  for (uint32_t b0 = 0; b0 < n_items; b0 += CB) {
+    const uint32_t nb = min(static_cast<uint32_t>(CB), n_items - b0);
     __syncthreads();  // the previous batch is consumed
     for (uint32_t e = tid; e < nb * G * (HD + 2); e += NT) {
       const uint32_t c = e / (G * (HD + 2)), rem = e % (G * (HD + 2));

@@ -71,24 +71,29 @@ struct AttnArgs {
   float* k_ring;         // stream 0 of this layer: [R][Hkv][hd]
   float* v_ring;
   uint64_t ring_stream_stride;  // floats between consecutive streams' rings
-  const uint32_t* pos_ring;     // [m][R]
-  uint32_t pos_stream_stride;
+  const uint32_t* legal;        // [m][R] slots this step may attend (the pushed slot first)
+  const uint32_t* n_legal;      // [m]
   float* out;            // [m][Hq*hd]
   float* part;           // [m][Hq][n_chunks][hd + 2] chunk partials
   uint32_t* counters;    // [m][Hkv], zero between launches (the last chunk resets it)
-  uint32_t m, n_q_heads, n_kv_heads, head_dim, ring, window, chunk, n_chunks;
-  const DevState* st;    // position source; null: use `pos` (and no push)
-  uint32_t pos;
+  uint32_t m, n_q_heads, n_kv_heads, head_dim, ring, chunk, n_chunks;
+  const DevState* st;    // slot of this step's push; null: no push
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// The legal-slot lists of m streams for a query at `pos` (ascending slot order), for the one-shot
+// attention entry point.
+hipError_t launch_compact_legal(const uint32_t* pos_rings, uint32_t m, uint32_t ring, uint32_t pos,
+                                uint32_t window, uint32_t* legal, uint32_t* n_legal, hipStream_t s);
 uint32_t attention_chunk(uint32_t head_dim);
 
 struct BeginArgs {
   const float* x_in;     // caller rows [m][d]
   float* xres;           // residual stream [m][d]
-  uint32_t md;           // m*d
+  uint32_t d;
   uint32_t* pos_rings;   // [m][R]
-  uint32_t m, ring;
+  uint32_t* legal;       // [m][R] out: the slots this step attends, the new slot first
+  uint32_t* n_legal;     // [m]
+  uint32_t m, ring, window;
   uint32_t pos, first;
   float* cs;             // [hd/2] cos, [hd/2] sin
   uint32_t head_dim;
@@ -133,6 +138,8 @@ struct StepArgs {
   int ffn;                  // EPI_SWIGLU or EPI_GELU
   int layer_scale, final_norm;
   uint32_t window, ring, chunk, n_chunks;
+  uint32_t* legal;          // [R]
+  uint32_t* n_legal;        // [1]
   const float* fin_w;
   const float* fin_b;
   float* x0;                // [d] the step's input row

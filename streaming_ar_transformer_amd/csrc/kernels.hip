@@ -101,14 +101,8 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
   wave_tiles((a.n_rows + RH - 1) / RH, t, t_end);
   if (t >= t_end) return;
 
-  const float4* wr[R];
-  float4 w[KB][R];
-  tile_rows<R, EPI>(a, t, wr);
-#pragma unroll
-  for (int j = 0; j < KB; ++j)
-#pragma unroll
-    for (int r = 0; r < R; ++r) w[j][r] = ldw(wr[r] + lane + kWave * j);
-
+  // The small input row (and the norm gain and bias) are requested first: loads return in
+  // order, so the norm arithmetic runs while the weight rows are still streaming in.
   float4 xr[M][KB];
   const float4* x4 = reinterpret_cast<const float4*>(a.x);
   const uint32_t xs4 = a.x_stride >> 2;
@@ -117,9 +111,27 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
 #pragma unroll
     for (int j = 0; j < KB; ++j)
       xr[m][j] = m < static_cast<int>(a.m) ? x4[m * xs4 + lane + kWave * j] : f4zero();
+  float4 gr[PRO != PRO_NONE ? KB : 1], br[PRO == PRO_LN ? KB : 1];
   if (PRO != PRO_NONE) {
     const float4* g4 = reinterpret_cast<const float4*>(a.norm_w);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) gr[j] = g4[lane + kWave * j];
+  }
+  if (PRO == PRO_LN) {
     const float4* b4 = reinterpret_cast<const float4*>(a.norm_b);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) br[j] = b4[lane + kWave * j];
+  }
+
+  const float4* wr[R];
+  float4 w[KB][R];
+  tile_rows<R, EPI>(a, t, wr);
+#pragma unroll
+  for (int j = 0; j < KB; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[j][r] = ldw(wr[r] + lane + kWave * j);
+
+  if (PRO != PRO_NONE) {
     const float kf = static_cast<float>(a.k);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -145,13 +157,13 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
-        const float4 g = g4[lane + kWave * j];
+        const float4 g = gr[j];
         float4 v = xr[m][j];
         if (PRO == PRO_RMS) {
           v.x = (v.x * inv) * g.x; v.y = (v.y * inv) * g.y;
           v.z = (v.z * inv) * g.z; v.w = (v.w * inv) * g.w;
         } else {
-          const float4 b = b4[lane + kWave * j];
+          const float4 b = br[j];
           v.x = ((v.x - mean) * inv) * g.x + b.x; v.y = ((v.y - mean) * inv) * g.y + b.y;
           v.z = ((v.z - mean) * inv) * g.z + b.z; v.w = ((v.w - mean) * inv) * g.w + b.w;
         }
@@ -269,20 +281,25 @@ __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
 // ([talker] TalkerGpu::load builds its tables on the CPU; rounding once to float32).
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kWgThreads) void k_begin(BeginArgs a) {
-  const uint32_t tid = blockIdx.x * blockDim.x + threadIdx.x;
-  const uint32_t nth = gridDim.x * blockDim.x;
+  __shared__ uint32_t scan[kWgThreads];
+  const uint32_t s = blockIdx.x;  // one workgroup per stream
+  const int tid = threadIdx.x;
   const uint32_t slot = a.pos % a.ring;
-  const float4* src = reinterpret_cast<const float4*>(a.x_in);
-  float4* dst = reinterpret_cast<float4*>(a.xres);
-  for (uint32_t i = tid; i < (a.md >> 2); i += nth) dst[i] = src[i];
+  const float4* src = reinterpret_cast<const float4*>(a.x_in + static_cast<size_t>(s) * a.d);
+  float4* dst = reinterpret_cast<float4*>(a.xres + static_cast<size_t>(s) * a.d);
+  for (uint32_t i = tid; i < (a.d >> 2); i += kWgThreads) dst[i] = src[i];
+  uint32_t* P = a.pos_rings + static_cast<size_t>(s) * a.ring;
   if (a.first) {
-    for (uint32_t i = tid; i < a.m * a.ring; i += nth)
-      a.pos_rings[i] = (i % a.ring) == slot ? a.pos : kInvalidPos;
-  } else {
-    for (uint32_t i = tid; i < a.m; i += nth) a.pos_rings[i * a.ring + slot] = a.pos;
+    for (uint32_t i = tid; i < a.ring; i += kWgThreads) P[i] = i == slot ? a.pos : kInvalidPos;
+  } else if (tid == 0) {
+    P[slot] = a.pos;
   }
+  __syncthreads();
+  compact_legal<kWgThreads, false>(P, a.ring, a.pos, a.window, static_cast<int>(slot),
+                                   a.legal + static_cast<size_t>(s) * a.ring, a.n_legal + s, scan);
+  if (s != 0) return;
   const uint32_t half = a.head_dim >> 1;
-  if (tid < half) {
+  if (static_cast<uint32_t>(tid) < half) {
     const double inv_freq = pow(a.theta, -2.0 * static_cast<double>(tid) /
                                              static_cast<double>(a.head_dim));
     const double ang = static_cast<double>(a.pos) * inv_freq;
@@ -293,6 +310,17 @@ __global__ __launch_bounds__(kWgThreads) void k_begin(BeginArgs a) {
     a.st->pos = a.pos;
     a.st->slot = slot;
   }
+}
+
+// The legal-slot lists of m streams (one workgroup per stream) for the one-shot attention call.
+__global__ __launch_bounds__(kWgThreads) void k_compact_legal(const uint32_t* pos_rings,
+                                                              uint32_t ring, uint32_t pos,
+                                                              uint32_t window, uint32_t* legal,
+                                                              uint32_t* n_legal) {
+  __shared__ uint32_t scan[kWgThreads];
+  const uint32_t s = blockIdx.x;
+  compact_legal<kWgThreads, false>(pos_rings + static_cast<size_t>(s) * ring, ring, pos, window,
+                                   -1, legal + static_cast<size_t>(s) * ring, n_legal + s, scan);
 }
 
 // Step end: the output rows -- the final norm of the residual stream ([talker] build_step_plan's
@@ -507,7 +535,9 @@ hipError_t launch_gemv(const GemvArgs& a, const GemvLaunch& l, hipStream_t s) {
 
 uint32_t attention_chunk(uint32_t head_dim) {
   (void)head_dim;
-  return 128u;
+  // legal slots per workgroup; a tuning override may pick 64 or 256 (at most the workgroup size)
+  const int c = env_int("SDEC_ATTN_CHUNK", 128);
+  return c == 64 || c == 256 ? static_cast<uint32_t>(c) : 128u;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
@@ -517,11 +547,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_begin(const BeginArgs& a, hipStream_t s) {
-  uint64_t work = a.md / 4;
-  if (a.first && static_cast<uint64_t>(a.m) * a.ring > work) work = static_cast<uint64_t>(a.m) * a.ring;
-  uint32_t grid = static_cast<uint32_t>((work + kWgThreads - 1) / kWgThreads);
-  grid = grid < 1 ? 1 : (grid > 64 ? 64 : grid);
-  hipLaunchKernelGGL(k_begin, dim3(grid), dim3(kWgThreads), 0, s, a);
+  hipLaunchKernelGGL(k_begin, dim3(a.m), dim3(kWgThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_legal(const uint32_t* pos_rings, uint32_t m, uint32_t ring, uint32_t pos,
+                                uint32_t window, uint32_t* legal, uint32_t* n_legal, hipStream_t s) {
+  hipLaunchKernelGGL(k_compact_legal, dim3(m), dim3(kWgThreads), 0, s, pos_rings, ring, pos, window,
+                     legal, n_legal);
   return hipGetLastError();
 }
 

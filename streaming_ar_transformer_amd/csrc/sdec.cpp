@@ -54,6 +54,8 @@ struct sdec_handle {
   float* k_rings = nullptr;   // [m][L][R][Hkv][hd]
   float* v_rings = nullptr;
   uint32_t* pos_rings = nullptr;  // [m][R]
+  uint32_t* legal = nullptr;      // [m][R] slots this step attends, the pushed slot first
+  uint32_t* n_legal = nullptr;    // [m]
   float* xres = nullptr;      // [m][d]
   float* qkv = nullptr;       // [m][(Hq+2Hkv)hd]
   float* attn_out = nullptr;  // [m][Hq hd], or [L][m][Hq hd] with taps
@@ -111,7 +113,7 @@ struct Alloc {
 };
 
 void free_handle_memory(sdec_handle* h) {
-  void* ps[] = {h->k_rings, h->v_rings, h->pos_rings, h->xres, h->qkv, h->attn_out,
+  void* ps[] = {h->k_rings, h->v_rings, h->pos_rings, h->legal, h->n_legal, h->xres, h->qkv, h->attn_out,
                 h->act, h->part, h->counters, h->cs, h->st, h->tap_attn_proj, h->tap_ffn_proj,
                 h->step_layers, h->step_bufs, h->bar, h->err};
   for (void* p : ps)
@@ -240,10 +242,10 @@ int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk) {
     aa.push = 1;
     aa.k_ring = ring_at(h, h->k_rings, 0, l); aa.v_ring = ring_at(h, h->v_rings, 0, l);
     aa.ring_stream_stride = h->ring_stream_stride;
-    aa.pos_ring = h->pos_rings; aa.pos_stream_stride = h->ring;
+    aa.legal = h->legal; aa.n_legal = h->n_legal;
     aa.out = att; aa.part = h->part; aa.counters = h->counters;
     aa.m = c.m; aa.n_q_heads = hq; aa.n_kv_heads = hkv; aa.head_dim = hd; aa.ring = h->ring;
-    aa.window = c.window; aa.chunk = h->chunk; aa.n_chunks = h->n_chunks; aa.st = h->st;
+    aa.chunk = h->chunk; aa.n_chunks = h->n_chunks; aa.st = h->st;
     LAUNCH(hk, s, SDEC_K_ATTENTION, launch_attention(aa, s));
     // o projection + (LayerScale) residual
     GemvArgs o{};
@@ -297,8 +299,10 @@ int enqueue_begin(sdec_handle* h, const float* x, uint32_t pos, uint32_t first, 
                   Hooks* hk) {
   const sdec_config& c = h->cfg;
   BeginArgs b{};
-  b.x_in = x; b.xres = h->xres; b.md = c.m * c.d_model; b.pos_rings = h->pos_rings;
-  b.m = c.m; b.ring = h->ring; b.pos = pos; b.first = first ? 1u : 0u; b.cs = h->cs;
+  b.x_in = x; b.xres = h->xres; b.d = c.d_model; b.pos_rings = h->pos_rings;
+  b.legal = h->legal; b.n_legal = h->n_legal;
+  b.m = c.m; b.ring = h->ring; b.window = c.window; b.pos = pos; b.first = first ? 1u : 0u;
+  b.cs = h->cs;
   b.head_dim = c.head_dim; b.theta = c.rope_theta; b.st = h->st;
   LAUNCH(hk, s, SDEC_K_BEGIN, launch_begin(b, s));
   return SDEC_OK;
@@ -393,7 +397,8 @@ int setup_persistent(sdec_handle* h) {
   a.layer_scale = c.layer_scale ? 1 : 0; a.final_norm = c.final_norm ? 1 : 0;
   a.window = c.window; a.ring = h->ring; a.chunk = h->chunk; a.n_chunks = h->n_chunks;
   a.fin_w = h->fin.norm_w; a.fin_b = h->fin.norm_b;
-  a.x0 = x0; a.pos_ring = h->pos_rings; a.cs = h->cs; a.st = h->st; a.bar = h->bar; a.err = h->err;
+  a.x0 = x0; a.pos_ring = h->pos_rings; a.legal = h->legal; a.n_legal = h->n_legal;
+  a.cs = h->cs; a.st = h->st; a.bar = h->bar; a.err = h->err;
   return SDEC_OK;
 }
 
@@ -434,6 +439,8 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
   h->k_rings = A.get<float>(h->ring_stream_stride * c.m);
   h->v_rings = A.get<float>(h->ring_stream_stride * c.m);
   h->pos_rings = A.get<uint32_t>(static_cast<size_t>(c.m) * ring_slots);
+  h->legal = A.get<uint32_t>(static_cast<size_t>(c.m) * ring_slots);
+  h->n_legal = A.get<uint32_t>(static_cast<size_t>(c.m));
   h->xres = A.get<float>(static_cast<size_t>(c.m) * c.d_model);
   h->qkv = A.get<float>(static_cast<size_t>(c.m) * (qw + 2 * kw));
   h->attn_out = A.get<float>(static_cast<size_t>(c.m) * qw * (taps ? c.n_layers : 1));
@@ -685,12 +692,14 @@ int sdec_ring_attention(const float* q, const float* k_ring, const float* v_ring
   if (group != 1 && group != 2 && group != 4) return fail(SDEC_E_ARG, "GQA group must be 1, 2 or 4");
   if (m < 1 || m > static_cast<uint32_t>(kMaxM) || ring_slots < 1 || window < 1)
     return fail(SDEC_E_ARG, "bad m, ring_slots or window");
-  // The chunk partials and counters live in a buffer kept for the life of the process and grown
-  // on demand; the counters are returned to zero by each launch.
+  // The chunk partials, counters and legal-slot lists live in buffers kept for the life of the
+  // process and grown on demand; the counters are returned to zero by each launch.
   static float* part = nullptr;
   static size_t part_cap = 0;
   static uint32_t* counters = nullptr;
   static size_t cnt_cap = 0;
+  static uint32_t* legal = nullptr;
+  static size_t legal_cap = 0;
   const uint32_t chunk = attention_chunk(head_dim);
   const uint32_t n_chunks = (ring_slots + chunk - 1) / chunk;
   const size_t need = static_cast<size_t>(m) * n_q_heads * n_chunks * (head_dim + 2);
@@ -714,15 +723,28 @@ int sdec_ring_attention(const float* q, const float* k_ring, const float* v_ring
     cnt_cap = alloc;
     HIP_TRY(launch_fill_u32(counters, 0u, cnt_cap, s));
   }
+  const size_t nleg = static_cast<size_t>(m) * ring_slots + m;
+  if (nleg > legal_cap) {
+    HIP_TRY(hipDeviceSynchronize());
+    if (legal) HIP_TRY(hipFree(legal));
+    legal = nullptr;
+    legal_cap = 0;
+    HIP_TRY(hipMalloc(&legal, nleg * sizeof(uint32_t)));
+    legal_cap = nleg;
+  }
+  uint32_t* n_legal = legal + static_cast<size_t>(m) * ring_slots;
+  HIP_TRY(launch_compact_legal(pos_ring, m, ring_slots, pos, window, legal, n_legal, s));
   AttnArgs a{};
   a.qkv = q; a.qkv_stride = n_q_heads * head_dim;
   a.q_norm = a.k_norm = nullptr; a.cs = nullptr; a.push = 0;
   a.k_ring = const_cast<float*>(k_ring); a.v_ring = const_cast<float*>(v_ring);
   a.ring_stream_stride = static_cast<uint64_t>(ring_slots) * n_kv_heads * head_dim;
-  a.pos_ring = pos_ring; a.pos_stream_stride = ring_slots; a.out = out; a.part = part;
+  a.legal = legal; a.n_legal = n_legal; a.out = out; a.part = part;
   a.counters = counters; a.m = m; a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads;
-  a.head_dim = head_dim; a.ring = ring_slots; a.window = window; a.chunk = chunk;
-  a.n_chunks = n_chunks; a.st = nullptr; a.pos = pos;
+  a.head_dim = head_dim; a.ring = ring_slots; a.chunk = chunk;
+  a.n_chunks = n_chunks; a.st = nullptr;
+  // a head with no legal slot gets zeros: the attention kernel skips items past the legal count
+  HIP_TRY(launch_fill_f32(out, 0.f, static_cast<uint64_t>(m) * n_q_heads * head_dim, s));
   HIP_TRY(launch_attention(a, s));
   return SDEC_OK;
 }

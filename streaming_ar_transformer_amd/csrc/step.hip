@@ -196,12 +196,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   if (blockIdx.x == 0) {
     for (uint32_t i = tid; i < d; i += kStepThreads) st_dev(a.x0 + i, a.x_in[i]);
     if (a.first) {
-      for (uint32_t i = tid; i < a.ring; i += kStepThreads)
-        __hip_atomic_store(a.pos_ring + i, i == slot ? a.pos : kInvalidPos, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      for (uint32_t i = tid; i < a.ring; i += kStepThreads) a.pos_ring[i] = i == slot ? a.pos : kInvalidPos;
     } else if (tid == 0) {
-      __hip_atomic_store(a.pos_ring + slot, a.pos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a.pos_ring[slot] = a.pos;
     }
+    __syncthreads();
+    compact_legal<kStepThreads, true>(a.pos_ring, a.ring, a.pos, a.window, static_cast<int>(slot),
+                                      a.legal, a.n_legal, reinterpret_cast<uint32_t*>(sm.gemv.raw));
     const uint32_t half = HD / 2;
     if (static_cast<uint32_t>(tid) < half) {
       const double inv_freq = pow(a.theta, -2.0 * static_cast<double>(tid) / static_cast<double>(HD));
@@ -274,10 +275,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       aa.q_norm = L.q_norm; aa.k_norm = L.k_norm; aa.eps = a.qk_eps;
       aa.rope_style = a.rope_style; aa.cs = a.cs; aa.push = 1;
       aa.k_ring = L.k_ring; aa.v_ring = L.v_ring; aa.ring_stream_stride = 0;
-      aa.pos_ring = a.pos_ring; aa.pos_stream_stride = a.ring;
+      aa.legal = a.legal; aa.n_legal = a.n_legal;
       aa.out = L.attn_out; aa.part = L.part; aa.counters = L.counters;
       aa.m = 1; aa.n_q_heads = hq; aa.n_kv_heads = hkv; aa.head_dim = HD; aa.ring = a.ring;
-      aa.window = a.window; aa.chunk = a.chunk; aa.n_chunks = a.n_chunks; aa.st = a.st;
+      aa.chunk = a.chunk; aa.n_chunks = a.n_chunks; aa.st = a.st;
       const uint32_t items = a.n_chunks * hkv;
       for (uint32_t it = blockIdx.x; it < items; it += gridDim.x)
         attention_item<HD, G, kStepThreads, true>(aa, it % a.n_chunks, it / a.n_chunks, 0u, sm.attn);
