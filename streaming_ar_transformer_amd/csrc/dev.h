@@ -80,6 +80,23 @@ struct ReduceScatter<1, OFF> {
   }
 };
 
+// Sum over aligned groups of N lanes (N = 8 or 16), left in every lane of the group: DPP lane
+// moves inside a 16-lane row (swap neighbours, swap pairs, mirror halves of 8, mirror the row), so
+// no LDS traffic is involved.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16, "DPP rows hold 16 lanes");
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  if (N == 16) v += dpp_mov<0x140>(v);  // row_mirror
+  return v;
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
@@ -235,24 +252,32 @@ struct AttnSmem {
   static constexpr int NG = (NT / kWave) * (kWave / LPS);
   uint32_t list[NT];
   float qs[G][HD];
+  float ks[HD], vs[HD];  // this step's key (normed, roped) and value, for the item that pushes
   float sm_m[NG][G], sm_l[NG][G];
   float sm_acc[NG][G][HD];
   uint32_t is_last;
 };
 
 // One (slot chunk, kv head, stream) work item, run by a whole workgroup of NT threads.  COH: the
-// output is handed to other workgroups of the same launch.
-template <int HD, int G, int NT, bool COH>
+// output is handed to other workgroups of the same launch.  UNR: slots per lane group whose keys
+// and values are in flight together.  CG: partials each thread requests together in the chunk
+// combine (0: a whole batch at once).
+//
+// The memory round trips are kept few: the slot list and this head group's raw q/k/v are fetched
+// together; then every key and value row of the item is requested at once, and the query and key
+// normalisation and rope run while those loads are in flight.  The slot this step pushes (always
+// the first of item 0) is scored from LDS, so no load waits for the push.
+template <int HD, int G, int NT, bool COH, int UNR = 4, int CG = 0>
 __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk, uint32_t kvh,
                                                uint32_t s, AttnSmem<HD, G, NT>& sm) {
   constexpr int LPS = HD / 8;
   constexpr int GPW = kWave / LPS;
   constexpr int NWV = NT / kWave;
   constexpr int NG = NWV * GPW;
-  constexpr int UNR = 4;
   constexpr int HALF = HD / 2;
   constexpr int CB = 16;  // chunks merged per batch by the last workgroup
   static_assert(CB <= NG, "combine staging reuses the group buffers");
+  static_assert(G <= NWV, "one wave per query head of the group");
   uint32_t* list = sm.list;
   auto& qs = sm.qs;
   auto& sm_m = sm.sm_m;
@@ -268,53 +293,76 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   const uint32_t h0 = kvh * G;
   const float* qkv = a.qkv + static_cast<size_t>(s) * a.qkv_stride;
 
-  // 1. this item's share of the step's legal slots; this step's raw queries
+  // 1. this item's share of the step's legal slots; this step's raw queries (and, for the item
+  //    that pushes, the raw key and value)
   const uint32_t nl = a.n_legal[s];
   const uint32_t n_items = (nl + a.chunk - 1) / a.chunk;
   if (chunk >= n_items) return;  // no legal slot falls in this item
   const uint32_t c0 = chunk * a.chunk;
   const uint32_t total = min(a.chunk, nl - c0);
+  const bool lead = a.push && a.st != nullptr && chunk == 0;  // list[0] is the slot pushed now
   if (static_cast<uint32_t>(tid) < total) list[tid] = a.legal[static_cast<size_t>(s) * a.ring + c0 + tid];
   for (int t = tid; t < G * HD; t += NT) qs[t / HD][t % HD] = qkv[(h0 + t / HD) * HD + t % HD];
+  if (lead) {
+    for (int t = tid; t < HD; t += NT) {
+      sm.ks[t] = qkv[(hq + kvh) * HD + t];
+      sm.vs[t] = qkv[(hq + hkv + kvh) * HD + t];
+    }
+  }
   __syncthreads();
 
-  // 2. queries: qk-norm + rope, one wave per head
-  if (a.q_norm != nullptr || a.cs != nullptr) {
+  // 2. request this group's first pass of key and value rows
+  const size_t row = static_cast<size_t>(hkv) * HD;
+  const float* kb = a.k_ring + static_cast<size_t>(s) * a.ring_stream_stride + kvh * HD + 8 * sub;
+  const float* vb = a.v_ring + static_cast<size_t>(s) * a.ring_stream_stride + kvh * HD + 8 * sub;
+  float4 kk[UNR][2], vv[UNR][2];
+  auto load_pass = [&](uint32_t i0) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const uint32_t i = i0 + u * NG;
+      if (i < total && !(lead && i == 0)) {
+        const size_t sl = list[i];
+        const float4* kp = reinterpret_cast<const float4*>(kb + sl * row);
+        const float4* vp = reinterpret_cast<const float4*>(vb + sl * row);
+        kk[u][0] = kp[0]; kk[u][1] = kp[1];
+        vv[u][0] = vp[0]; vv[u][1] = vp[1];
+      } else {
+        kk[u][0] = kk[u][1] = vv[u][0] = vv[u][1] = f4zero();
+      }
+    }
+  };
+  load_pass(grp);
+
+  // 3. queries: qk-norm + rope, one wave per head; the pushing item's last wave also normalises and
+  //    ropes this step's key and writes key and value into the ring slot pos mod R
+  const bool prep = a.q_norm != nullptr || a.cs != nullptr;
+  const int ia = a.rope_style == 0 ? lane : 2 * lane;
+  const int ib = a.rope_style == 0 ? lane + HALF : 2 * lane + 1;
+  if (prep) {
     for (int g = wave; g < G; g += NWV) {
-      const int ia = a.rope_style == 0 ? lane : 2 * lane;
-      const int ib = a.rope_style == 0 ? lane + HALF : 2 * lane + 1;
-      float va = lane < HALF ? qs[g][ia] : 0.f, vb = lane < HALF ? qs[g][ib] : 0.f;
-      norm_rope_pair<HD>(va, vb, lane, a.q_norm, a.eps, a.cs, a.rope_style);
+      float va = lane < HALF ? qs[g][ia] : 0.f, vb2 = lane < HALF ? qs[g][ib] : 0.f;
+      norm_rope_pair<HD>(va, vb2, lane, a.q_norm, a.eps, a.cs, a.rope_style);
       if (lane < HALF) {
         qs[g][ia] = va;
-        qs[g][ib] = vb;
+        qs[g][ib] = vb2;
       }
     }
   }
-  // 3. item 0, whose list starts with slot pos mod R, pushes this step's key (normed, roped) and
-  //    value
-  if (a.push && a.st != nullptr && chunk == 0) {
+  if (lead && wave == NWV - 1) {
+    float va = lane < HALF ? sm.ks[ia] : 0.f, vb2 = lane < HALF ? sm.ks[ib] : 0.f;
+    norm_rope_pair<HD>(va, vb2, lane, a.k_norm, a.eps, a.cs, a.rope_style);
     const uint32_t ps = a.st->slot;
-    {
-      const size_t roff = static_cast<size_t>(s) * a.ring_stream_stride +
-                          (static_cast<size_t>(ps) * hkv + kvh) * HD;
-      if (wave == 0) {
-        const float* kr = qkv + (hq + kvh) * HD;
-        const int ia = a.rope_style == 0 ? lane : 2 * lane;
-        const int ib = a.rope_style == 0 ? lane + HALF : 2 * lane + 1;
-        float va = lane < HALF ? kr[ia] : 0.f, vb = lane < HALF ? kr[ib] : 0.f;
-        norm_rope_pair<HD>(va, vb, lane, a.k_norm, a.eps, a.cs, a.rope_style);
-        if (lane < HALF) {
-          a.k_ring[roff + ia] = va;
-          a.k_ring[roff + ib] = vb;
-        }
-      } else if (wave == 1) {
-        const float* vr = qkv + (hq + hkv + kvh) * HD;
-        for (int d = lane; d < HD; d += kWave) a.v_ring[roff + d] = vr[d];
-      }
+    const size_t roff = static_cast<size_t>(s) * a.ring_stream_stride +
+                        (static_cast<size_t>(ps) * hkv + kvh) * HD;
+    if (lane < HALF) {
+      sm.ks[ia] = va;
+      sm.ks[ib] = vb2;
+      a.k_ring[roff + ia] = va;
+      a.k_ring[roff + ib] = vb2;
     }
+    for (int d = lane; d < HD; d += kWave) a.v_ring[roff + d] = sm.vs[d];
   }
-  __syncthreads();  // list, queries and the pushed slot are visible to the whole workgroup
+  __syncthreads();  // queries and this step's key are in LDS
 
   // 4. online softmax over this group's share of the legal slots
   float q[G][8];
@@ -331,49 +379,55 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
   }
-  const size_t row = static_cast<size_t>(hkv) * HD;
-  const float* kb = a.k_ring + static_cast<size_t>(s) * a.ring_stream_stride + kvh * HD + 8 * sub;
-  const float* vb = a.v_ring + static_cast<size_t>(s) * a.ring_stream_stride + kvh * HD + 8 * sub;
-  for (uint32_t i0 = grp; i0 < total; i0 += NG * UNR) {
-    float4 kk[UNR][2], vv[UNR][2];
+  for (uint32_t i0 = grp;;) {
+    // all UNR scores of the pass first (independent chains), then one softmax update per head
+    float sc[UNR][G];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const uint32_t i = i0 + u * NG;
-      if (i < total) {
-        const size_t sl = list[i];
-        const float4* kp = reinterpret_cast<const float4*>(kb + sl * row);
-        const float4* vp = reinterpret_cast<const float4*>(vb + sl * row);
-        kk[u][0] = kp[0]; kk[u][1] = kp[1];
-        vv[u][0] = vp[0]; vv[u][1] = vp[1];
-      } else {
-        kk[u][0] = kk[u][1] = vv[u][0] = vv[u][1] = f4zero();
+      float kf[8] = {kk[u][0].x, kk[u][0].y, kk[u][0].z, kk[u][0].w,
+                     kk[u][1].x, kk[u][1].y, kk[u][1].z, kk[u][1].w};
+      if (lead && i == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kf[e] = sm.ks[8 * sub + e];
+        vv[u][0] = make_float4(sm.vs[8 * sub], sm.vs[8 * sub + 1], sm.vs[8 * sub + 2], sm.vs[8 * sub + 3]);
+        vv[u][1] = make_float4(sm.vs[8 * sub + 4], sm.vs[8 * sub + 5], sm.vs[8 * sub + 6], sm.vs[8 * sub + 7]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(q[g][e], kf[e], d);
+        d = group_sum<LPS>(d);
+        sc[u][g] = i < total ? d * scale : -INFINITY;
       }
     }
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      if (i0 + u * NG < total) {
-        const float kf[8] = {kk[u][0].x, kk[u][0].y, kk[u][0].z, kk[u][0].w,
-                             kk[u][1].x, kk[u][1].y, kk[u][1].z, kk[u][1].w};
-        const float vf[8] = {vv[u][0].x, vv[u][0].y, vv[u][0].z, vv[u][0].w,
-                             vv[u][1].x, vv[u][1].y, vv[u][1].z, vv[u][1].w};
+    for (int g = 0; g < G; ++g) {
+      float mb = sc[0][g];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = 0.f;
+      for (int u = 1; u < UNR; ++u) mb = fmaxf(mb, sc[u][g]);
+      const float mnew = fmaxf(mrun[g], mb);
+      if (mnew != -INFINITY) {
+        const float corr = expf(mrun[g] - mnew);
+        lrun[g] *= corr;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) d = fmaf(q[g][e], kf[e], d);
+        for (int e = 0; e < 8; ++e) acc[g][e] *= corr;
 #pragma unroll
-          for (int o = LPS / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, kWave);
-          const float sc = d * scale;
-          const float mnew = fmaxf(mrun[g], sc);
-          const float corr = expf(mrun[g] - mnew);
-          const float p = expf(sc - mnew);
-          lrun[g] = lrun[g] * corr + p;
+        for (int u = 0; u < UNR; ++u) {
+          const float p = expf(sc[u][g] - mnew);
+          const float vf[8] = {vv[u][0].x, vv[u][0].y, vv[u][0].z, vv[u][0].w,
+                               vv[u][1].x, vv[u][1].y, vv[u][1].z, vv[u][1].w};
+          lrun[g] += p;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[g][e] = acc[g][e] * corr + p * vf[e];
-          mrun[g] = mnew;
+          for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
         }
+        mrun[g] = mnew;
       }
     }
+    i0 += NG * UNR;
+    if (i0 >= total) break;
+    load_pass(i0);
   }
 
   // 5. merge the slot groups of this workgroup into the chunk's (max, sum, output)
@@ -434,17 +488,36 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
     Lr[i] = 0.f;
     Or[i] = 0.f;
   }
+  // A batch's partials are requested CG per thread at a time before any is used (one memory round
+  // trip per batch when CG covers it).
+  constexpr int PER = (CB * G * (HD + 2) + NT - 1) / NT;
+  constexpr int GRP = CG > 0 && CG < PER ? CG : PER;
   for (uint32_t b0 = 0; b0 < n_items; b0 += CB) {
     const uint32_t nb = min(static_cast<uint32_t>(CB), n_items - b0);
+    const uint32_t n_e = nb * G * (HD + 2);
     __syncthreads();  // the previous batch is consumed
-    for (uint32_t e = tid; e < nb * G * (HD + 2); e += NT) {
-      const uint32_t c = e / (G * (HD + 2)), rem = e % (G * (HD + 2));
-      const uint32_t g = rem / (HD + 2), d = rem % (HD + 2);
-      const float v = ld_dev(a.part + ((static_cast<size_t>(s) * hq + h0 + g) * a.n_chunks + b0 + c) *
-                                          (HD + 2) + d);
-      if (d < HD) stage[(c * G + g) * HD + d] = v;
-      else if (d == HD) sm_m[c][g] = v;
-      else sm_l[c][g] = v;
+    for (int k0 = 0; k0 < PER; k0 += GRP) {
+      float pv[GRP];
+#pragma unroll
+      for (int k = 0; k < GRP; ++k) {
+        const uint32_t e = tid + (k0 + k) * NT;
+        const uint32_t c = e / (G * (HD + 2)), rem = e % (G * (HD + 2));
+        const uint32_t g = rem / (HD + 2), d = rem % (HD + 2);
+        pv[k] = e < n_e ? ld_dev(a.part + ((static_cast<size_t>(s) * hq + h0 + g) * a.n_chunks + b0 + c) *
+                                              (HD + 2) + d)
+                        : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < GRP; ++k) {
+        const uint32_t e = tid + (k0 + k) * NT;
+        const uint32_t c = e / (G * (HD + 2)), rem = e % (G * (HD + 2));
+        const uint32_t g = rem / (HD + 2), d = rem % (HD + 2);
+        if (e < n_e) {
+          if (d < HD) stage[(c * G + g) * HD + d] = pv[k];
+          else if (d == HD) sm_m[c][g] = pv[k];
+          else sm_l[c][g] = pv[k];
+        }
+      }
     }
     __syncthreads();
 #pragma unroll

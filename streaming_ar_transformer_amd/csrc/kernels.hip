@@ -123,13 +123,18 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
     for (int j = 0; j < KB; ++j) br[j] = b4[lane + kWave * j];
   }
 
-  const float4* wr[R];
-  float4 w[KB][R];
-  tile_rows<R, EPI>(a, t, wr);
+  // Two tiles of weight rows in flight: tile t+2 is requested as soon as tile t is reduced.
+  float4 w0[KB][R], w1[KB][R];
+  auto load_tile = [&](uint32_t tt, float4 (&w)[KB][R]) {
+    const float4* wr[R];
+    tile_rows<R, EPI>(a, tt, wr);
 #pragma unroll
-  for (int j = 0; j < KB; ++j)
+    for (int j = 0; j < KB; ++j)
 #pragma unroll
-    for (int r = 0; r < R; ++r) w[j][r] = ldw(wr[r] + lane + kWave * j);
+      for (int r = 0; r < R; ++r) w[j][r] = ldw(wr[r] + lane + kWave * j);
+  };
+  load_tile(t, w0);
+  if (t + 1 < t_end) load_tile(t + 1, w1);
 
   if (PRO != PRO_NONE) {
     const float kf = static_cast<float>(a.k);
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
     }
   }
 
-  while (true) {
+  auto reduce_tile = [&](uint32_t tt, const float4 (&w)[KB][R]) {
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
@@ -182,16 +187,16 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
       for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r * M + m] = dot4(w[j][r], xr[m][j], acc[r * M + m]);
-    const uint32_t cur = t++;
-    if (t < t_end) {
-      tile_rows<R, EPI>(a, t, wr);
-#pragma unroll
-      for (int j = 0; j < KB; ++j)
-#pragma unroll
-        for (int r = 0; r < R; ++r) w[j][r] = ldw(wr[r] + lane + kWave * j);
-    }
-    gemv_epilogue<M, R, EPI>(a, cur, acc, lane);
-    if (t >= t_end) break;
+    gemv_epilogue<M, R, EPI>(a, tt, acc, lane);
+  };
+  // ping-pong between the two register buffers (unrolled: registers cannot be indexed)
+  while (true) {
+    reduce_tile(t, w0);
+    if (t + 2 < t_end) load_tile(t + 2, w0);
+    if (++t >= t_end) break;
+    reduce_tile(t, w1);
+    if (t + 2 < t_end) load_tile(t + 2, w1);
+    if (++t >= t_end) break;
   }
 }
 
@@ -271,7 +276,9 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv(GemvArgs a) {
 template <int HD, int G>
 __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
   __shared__ AttnSmem<HD, G, kWgThreads> sm;
-  attention_item<HD, G, kWgThreads, false>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+  // one pass over a default-size chunk: all of a group's key and value rows in flight at once
+  constexpr int UNR = HD >= 128 ? 8 : 4;
+  attention_item<HD, G, kWgThreads, false, UNR>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -495,11 +502,22 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
   l.kb = 0;
   if (M <= 2 && (kb == 2 || kb == 8)) l.kb = static_cast<int>(kb);
   if (M == 1 && kb == 24 && epilogue != EPI_SWIGLU) l.kb = 24;
+  int dev = 0, cus = 256, occ = 1;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (l.kb > 0) {
     // rows in flight per wave: enough 16-byte loads per lane to cover the HBM latency
-    if (epilogue == EPI_SWIGLU) l.rows_per_wave = 2;
-    else if (l.kb == 2) l.rows_per_wave = M == 1 ? 4 : 2;
-    else l.rows_per_wave = 1;
+    if (epilogue == EPI_SWIGLU) {
+      l.rows_per_wave = 2;
+    } else if (l.kb == 2) {
+      l.rows_per_wave = M == 1 ? 4 : 2;
+    } else if (l.kb == 8 && M == 1) {
+      // the widest tile that still gives every SIMD of the device a tile of its own
+      const uint32_t waves = 4u * static_cast<uint32_t>(cus);
+      l.rows_per_wave = n_rows / 4 >= waves ? 4 : n_rows / 2 >= waves ? 2 : 1;
+    } else {
+      l.rows_per_wave = 1;
+    }
   } else {
     l.rows_per_wave = M == 1 ? (epilogue == EPI_SWIGLU ? 2 : 1) : (M == 2 ? 2 : 4);
   }
@@ -508,9 +526,6 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
   const uint32_t tiles = (n_rows + rh - 1) / rh;
   // Resident waves only: every wave owns a contiguous range of tiles, so a grid larger than what
   // the device holds at once would leave a second, serial round of workgroups.
-  int dev = 0, cus = 256, occ = 1;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const GemvKernel kern = gemv_pick(l, k, m);
   if (kern.fn == nullptr ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern.fn, kWgThreads, kern.lds) !=

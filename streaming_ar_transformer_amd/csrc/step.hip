@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       aa.chunk = a.chunk; aa.n_chunks = a.n_chunks; aa.st = a.st;
       const uint32_t items = a.n_chunks * hkv;
       for (uint32_t it = blockIdx.x; it < items; it += gridDim.x)
-        attention_item<HD, G, kStepThreads, true>(aa, it % a.n_chunks, it / a.n_chunks, 0u, sm.attn);
+        attention_item<HD, G, kStepThreads, true, 2, 4>(aa, it % a.n_chunks, it / a.n_chunks, 0u, sm.attn);
     }
     grid_sync(a, bar++);
     // ---- o projection + (LayerScale) residual ([talker] o GEMV + ADD; [mimi] MV_LS)
