@@ -458,15 +458,26 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
     if (single) {
       put<COH>(a.out + static_cast<size_t>(s) * hq * HD + (h0 + g) * HD + d, L > 0.f ? O / L : 0.f);
     } else {
-      float* pp = a.part + ((static_cast<size_t>(s) * hq + h0 + g) * a.n_chunks + chunk) * (HD + 2);
-      st_dev(pp + d, O);
-      if (d == 0) {
-        st_dev(pp + HD, M);
-        st_dev(pp + HD + 1, L);
+      // chunk partials: unnormalised output rows, then (max, sum) pairs after all of them
+      const size_t pi = (static_cast<size_t>(s) * hq + h0 + g) * a.n_chunks + chunk;
+      float* po = a.part + pi * HD + d;
+      float* pml = a.part + static_cast<size_t>(a.m) * hq * a.n_chunks * HD + pi * 2;
+      if (a.partials_only) {
+        *po = O;
+        if (d == 0) {
+          pml[0] = M;
+          pml[1] = L;
+        }
+      } else {
+        st_dev(po, O);
+        if (d == 0) {
+          st_dev(pml, M);
+          st_dev(pml + 1, L);
+        }
       }
     }
   }
-  if (single) return;
+  if (single || a.partials_only) return;
 
   // 6. the last chunk of this (stream, kv head) to finish merges all chunks.  The partials went
   // out with device-coherent stores; they are complete before this workgroup's count is added.
@@ -503,9 +514,11 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
         const uint32_t e = tid + (k0 + k) * NT;
         const uint32_t c = e / (G * (HD + 2)), rem = e % (G * (HD + 2));
         const uint32_t g = rem / (HD + 2), d = rem % (HD + 2);
-        pv[k] = e < n_e ? ld_dev(a.part + ((static_cast<size_t>(s) * hq + h0 + g) * a.n_chunks + b0 + c) *
-                                              (HD + 2) + d)
-                        : 0.f;
+        const size_t pi = (static_cast<size_t>(s) * hq + h0 + g) * a.n_chunks + b0 + c;
+        const float* src = d < HD ? a.part + pi * HD + d
+                                  : a.part + static_cast<size_t>(a.m) * hq * a.n_chunks * HD + pi * 2 +
+                                        (d - HD);
+        pv[k] = e < n_e ? ld_dev(src) : 0.f;
       }
 #pragma unroll
       for (int k = 0; k < GRP; ++k) {

@@ -17,7 +17,11 @@ struct DevState {
   uint32_t slot;
 };
 
-enum GemvPrologue : int { PRO_NONE = 0, PRO_RMS = 1, PRO_LN = 2 };
+// PRO_ATTN: the input row is this step's attention output, combined in the prologue from the
+// per-chunk softmax partials the ring-attention launch left (one stream only).
+enum GemvPrologue : int { PRO_NONE = 0, PRO_RMS = 1, PRO_LN = 2, PRO_ATTN = 3 };
+constexpr uint32_t kAttnMaxChunks = 64;      // chunks a PRO_ATTN prologue combines
+constexpr uint32_t kAttnMaxPartials = 1024;  // heads x chunks a PRO_ATTN prologue combines
 enum GemvEpilogue : int { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2, EPI_GELU = 3 };
 
 // y = x . W^T over up to three row segments (q, k, v share one launch).  With EPI_SWIGLU the
@@ -41,6 +45,13 @@ struct GemvArgs {
   const float* ls;       // LayerScale or null
   float* tap;            // optional copy of the raw branch, [m][tap_stride]
   uint32_t tap_stride;
+  // PRO_ATTN: chunk partials -- unnormalised outputs [k / head_dim heads][n_chunks][head_dim], then
+  // (chunk max, chunk sum) pairs [heads][n_chunks][2] -- and the legal-slot count that sets how
+  // many chunks hold data; with a single chunk the attention output is read from x as usual
+  const float* part;
+  const uint32_t* n_legal;
+  uint32_t chunk, n_chunks, head_dim;
+  float* x_tap;          // PRO_ATTN: optional copy of the combined input row
 };
 
 struct GemvLaunch {
@@ -55,6 +66,8 @@ struct GemvLaunch {
 hipError_t launch_gemv(const GemvArgs& a, const GemvLaunch& l, hipStream_t s);
 // A launch shape for this GEMV on this device (grid sized to the row tiles).
 GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, uint32_t m);
+// Whether a kernel exists for this launch shape.
+bool gemv_supported(const GemvLaunch& l, uint32_t k, uint32_t m);
 
 // Ring attention of one layer for every stream.  In the step it also finishes the new position:
 // qk-RMSNorm and rope of this step's q and k (from the raw q/k/v projection), and the push of the
@@ -78,6 +91,8 @@ struct AttnArgs {
   uint32_t* counters;    // [m][Hkv], zero between launches (the last chunk resets it)
   uint32_t m, n_q_heads, n_kv_heads, head_dim, ring, chunk, n_chunks;
   const DevState* st;    // slot of this step's push; null: no push
+  int partials_only;     // nonzero: with more than one item, every item leaves its chunk
+                         // partial (plain stores) and the consumer of `out` combines them
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // The legal-slot lists of m streams for a query at `pos` (ascending slot order), for the one-shot

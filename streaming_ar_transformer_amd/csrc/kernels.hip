@@ -91,6 +91,103 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, float4* xs, uint32_t 
 // ------------------------------------------------------------------------------------------------
 // Register-resident variant: k == 256*KB, and each lane keeps its KB float4 of every input row in
 // registers, normalised by the wave itself (no LDS, no workgroup barrier).
+// PRO_ATTN input row: this step's attention output.  With one chunk of legal slots the attention
+// launch wrote it to x; otherwise it is combined here from the chunk partials (the attention's
+// softmax, finished here): for each head, with M the largest chunk maximum,
+// out = sum_c e^(M_c - M) O_c / sum_c e^(M_c - M) L_c ([talker] GQA_ATTN_SRC; [mimi] attn_src).
+// Run by the whole workgroup.  The legal-slot count comes through the scalar cache, so the row (or
+// every partial of up to IB chunks) is requested before `issue_weights` streams the weights and
+// the combine overlaps them.
+template <int KB, typename F>
+__device__ __forceinline__ void attn_input(const GemvArgs& a, float4 (&xr)[KB], F issue_weights) {
+  constexpr int K4 = KB * kWave;
+  constexpr int PER = (K4 + kWgThreads - 1) / kWgThreads;  // row float4 per thread
+  constexpr int IB = 16;                                   // chunks per batch
+  __shared__ float4 xsh[K4];
+  __shared__ float msh[kAttnMaxPartials], lsh[kAttnMaxPartials];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const uint32_t HD = a.head_dim, hq = a.k / HD, nc = a.n_chunks;
+  typedef const __attribute__((address_space(4))) uint32_t ConstU32;
+  const uint32_t nl = *((ConstU32*)a.n_legal);
+  const uint32_t n_items = min((nl + a.chunk - 1) / a.chunk, nc);
+  if (n_items <= 1) {
+    const float4* x4 = reinterpret_cast<const float4*>(a.x);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) xr[j] = x4[lane + kWave * j];
+    issue_weights();
+    if (a.x_tap != nullptr && blockIdx.x == 0)
+      for (uint32_t c4 = tid; c4 < K4; c4 += kWgThreads)
+        reinterpret_cast<float4*>(a.x_tap)[c4] = x4[c4];
+    return;
+  }
+  const float* ml = a.part + static_cast<size_t>(hq) * nc * HD;
+  float4 o[PER][IB];
+  auto load_batch = [&](uint32_t i0) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const uint32_t c4 = tid + p * kWgThreads, h = 4 * c4 / HD, d = 4 * c4 % HD;
+#pragma unroll
+      for (int i = 0; i < IB; ++i)
+        o[p][i] = c4 < K4 && i0 + i < n_items
+                      ? *reinterpret_cast<const float4*>(a.part + (static_cast<size_t>(h) * nc + i0 + i) * HD + d)
+                      : f4zero();
+    }
+  };
+  load_batch(0);
+  for (uint32_t e = tid; e < hq * n_items; e += kWgThreads) {
+    const uint32_t h = e / n_items, i = e % n_items;
+    msh[e] = ml[(static_cast<size_t>(h) * nc + i) * 2];
+    lsh[e] = ml[(static_cast<size_t>(h) * nc + i) * 2 + 1];
+  }
+  issue_weights();
+  __syncthreads();
+  for (uint32_t h = tid; h < hq; h += kWgThreads) {  // chunk weights e^(M_c - M) / L
+    float mx = -INFINITY;
+    for (uint32_t i = 0; i < n_items; ++i) mx = fmaxf(mx, msh[h * n_items + i]);
+    float l = 0.f;
+    for (uint32_t i = 0; i < n_items; ++i) {
+      const float mi = msh[h * n_items + i];
+      if (mi != -INFINITY) l = fmaf(expf(mi - mx), lsh[h * n_items + i], l);
+    }
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    for (uint32_t i = 0; i < n_items; ++i) {
+      const float mi = msh[h * n_items + i];
+      msh[h * n_items + i] = mi != -INFINITY ? expf(mi - mx) * inv : 0.f;
+    }
+  }
+  __syncthreads();
+  float4 acc[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) acc[p] = f4zero();
+  for (uint32_t i0 = 0;;) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const uint32_t c4 = tid + p * kWgThreads, h = 4 * c4 / HD;
+#pragma unroll
+      for (int i = 0; i < IB; ++i) {
+        if (c4 < K4 && i0 + i < n_items) {
+          const float w = msh[h * n_items + i0 + i];
+          acc[p].x = fmaf(w, o[p][i].x, acc[p].x); acc[p].y = fmaf(w, o[p][i].y, acc[p].y);
+          acc[p].z = fmaf(w, o[p][i].z, acc[p].z); acc[p].w = fmaf(w, o[p][i].w, acc[p].w);
+        }
+      }
+    }
+    i0 += IB;
+    if (i0 >= n_items) break;
+    load_batch(i0);
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const uint32_t c4 = tid + p * kWgThreads;
+    if (c4 < K4) xsh[c4] = acc[p];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KB; ++j) xr[j] = xsh[lane + kWave * j];
+  if (a.x_tap != nullptr && blockIdx.x == 0)
+    for (uint32_t c4 = tid; c4 < K4; c4 += kWgThreads) reinterpret_cast<float4*>(a.x_tap)[c4] = xsh[c4];
+}
+
 template <int M, int R, int PRO, int EPI, int KB>
 __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
   constexpr int V = R * M;
@@ -99,20 +196,44 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t t, t_end;
   wave_tiles((a.n_rows + RH - 1) / RH, t, t_end);
-  if (t >= t_end) return;
 
-  // The small input row (and the norm gain and bias) are requested first: loads return in
-  // order, so the norm arithmetic runs while the weight rows are still streaming in.
-  float4 xr[M][KB];
-  const float4* x4 = reinterpret_cast<const float4*>(a.x);
-  const uint32_t xs4 = a.x_stride >> 2;
-#pragma unroll
-  for (int m = 0; m < M; ++m)
+  // Two tiles of weight rows in flight: tile t+2 is requested as soon as tile t is reduced (the
+  // attention-combine variant keeps one: its registers hold the chunk partials instead).
+  constexpr bool kTwo = PRO != PRO_ATTN;
+  float4 w0[KB][R], w1[kTwo ? KB : 1][R];
+  auto load_tile = [&](uint32_t tt, float4 (&w)[KB][R]) {
+    const float4* wr[R];
+    tile_rows<R, EPI>(a, tt, wr);
 #pragma unroll
     for (int j = 0; j < KB; ++j)
-      xr[m][j] = m < static_cast<int>(a.m) ? x4[m * xs4 + lane + kWave * j] : f4zero();
-  float4 gr[PRO != PRO_NONE ? KB : 1], br[PRO == PRO_LN ? KB : 1];
-  if (PRO != PRO_NONE) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[j][r] = ldw(wr[r] + lane + kWave * j);
+  };
+  auto load_first = [&]() {
+    if (t < t_end) load_tile(t, w0);
+    if constexpr (kTwo)
+      if (t + 1 < t_end) load_tile(t + 1, w1);
+  };
+
+  float4 xr[M][KB];
+  if constexpr (PRO == PRO_ATTN) {
+    static_assert(M == 1, "the attention combine serves one stream");
+    attn_input<KB>(a, xr[0], load_first);  // the whole workgroup takes part
+    if (t >= t_end) return;
+  } else {
+    if (t >= t_end) return;
+    // The small input row (and the norm gain and bias) are requested first: loads return in
+    // order, so the norm arithmetic runs while the weight rows are still streaming in.
+    const float4* x4 = reinterpret_cast<const float4*>(a.x);
+    const uint32_t xs4 = a.x_stride >> 2;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        xr[m][j] = m < static_cast<int>(a.m) ? x4[m * xs4 + lane + kWave * j] : f4zero();
+  }
+  float4 gr[PRO == PRO_RMS || PRO == PRO_LN ? KB : 1], br[PRO == PRO_LN ? KB : 1];
+  if (PRO == PRO_RMS || PRO == PRO_LN) {
     const float4* g4 = reinterpret_cast<const float4*>(a.norm_w);
 #pragma unroll
     for (int j = 0; j < KB; ++j) gr[j] = g4[lane + kWave * j];
@@ -122,21 +243,9 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
 #pragma unroll
     for (int j = 0; j < KB; ++j) br[j] = b4[lane + kWave * j];
   }
+  if constexpr (PRO != PRO_ATTN) load_first();
 
-  // Two tiles of weight rows in flight: tile t+2 is requested as soon as tile t is reduced.
-  float4 w0[KB][R], w1[KB][R];
-  auto load_tile = [&](uint32_t tt, float4 (&w)[KB][R]) {
-    const float4* wr[R];
-    tile_rows<R, EPI>(a, tt, wr);
-#pragma unroll
-    for (int j = 0; j < KB; ++j)
-#pragma unroll
-      for (int r = 0; r < R; ++r) w[j][r] = ldw(wr[r] + lane + kWave * j);
-  };
-  load_tile(t, w0);
-  if (t + 1 < t_end) load_tile(t + 1, w1);
-
-  if (PRO != PRO_NONE) {
+  if (PRO == PRO_RMS || PRO == PRO_LN) {
     const float kf = static_cast<float>(a.k);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -189,14 +298,22 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
         for (int r = 0; r < R; ++r) acc[r * M + m] = dot4(w[j][r], xr[m][j], acc[r * M + m]);
     gemv_epilogue<M, R, EPI>(a, tt, acc, lane);
   };
-  // ping-pong between the two register buffers (unrolled: registers cannot be indexed)
-  while (true) {
-    reduce_tile(t, w0);
-    if (t + 2 < t_end) load_tile(t + 2, w0);
-    if (++t >= t_end) break;
-    reduce_tile(t, w1);
-    if (t + 2 < t_end) load_tile(t + 2, w1);
-    if (++t >= t_end) break;
+  if constexpr (kTwo) {
+    // ping-pong between the two register buffers (unrolled: registers cannot be indexed)
+    while (true) {
+      reduce_tile(t, w0);
+      if (t + 2 < t_end) load_tile(t + 2, w0);
+      if (++t >= t_end) break;
+      reduce_tile(t, w1);
+      if (t + 2 < t_end) load_tile(t + 2, w1);
+      if (++t >= t_end) break;
+    }
+  } else {
+    while (true) {
+      reduce_tile(t, w0);
+      if (++t >= t_end) break;
+      load_tile(t, w0);
+    }
   }
 }
 
@@ -446,8 +563,28 @@ GemvKernel gemv_pick_r(const GemvLaunch& l, uint32_t k) {
   return {nullptr, 0};
 }
 
+// The attention-combine prologue: one stream, register-resident input rows of 512 or 2048.
+template <int R>
+GemvKernel gemv_rx_attn(int kb) {
+  if (kb == 2) return {reinterpret_cast<const void*>(&k_gemv_rx<1, R, PRO_ATTN, EPI_RESIDUAL, 2>), 0};
+  if (kb == 8) return {reinterpret_cast<const void*>(&k_gemv_rx<1, R, PRO_ATTN, EPI_RESIDUAL, 8>), 0};
+  return {nullptr, 0};
+}
+
 template <int M>
 GemvKernel gemv_pick_m(const GemvLaunch& l, uint32_t k) {
+  if (l.prologue == PRO_ATTN) {
+    if constexpr (M == 1) {
+      if (l.epilogue != EPI_RESIDUAL) return {nullptr, 0};
+      switch (l.rows_per_wave) {
+        case 1: return gemv_rx_attn<1>(l.kb);
+        case 2: return gemv_rx_attn<2>(l.kb);
+        case 4: return gemv_rx_attn<4>(l.kb);
+        default: return {nullptr, 0};
+      }
+    }
+    return {nullptr, 0};
+  }
 #define SDEC_KIND(P, E) \
   if (l.prologue == P && l.epilogue == E) return gemv_pick_r<M, P, E>(l, k);
   SDEC_KIND(PRO_NONE, EPI_STORE)
@@ -538,6 +675,10 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
   if (wgs > max_wgs) wgs = max_wgs;
   l.grid = wgs < 1 ? 1 : wgs;
   return l;
+}
+
+bool gemv_supported(const GemvLaunch& l, uint32_t k, uint32_t m) {
+  return gemv_pick(l, k, m).fn != nullptr;
 }
 
 hipError_t launch_gemv(const GemvArgs& a, const GemvLaunch& l, hipStream_t s) {

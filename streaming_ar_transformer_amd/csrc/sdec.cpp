@@ -60,7 +60,7 @@ struct sdec_handle {
   float* qkv = nullptr;       // [m][(Hq+2Hkv)hd]
   float* attn_out = nullptr;  // [m][Hq hd], or [L][m][Hq hd] with taps
   float* act = nullptr;       // [m][d_ff]
-  float* part = nullptr;      // [m][Hq][n_chunks][hd+2]
+  float* part = nullptr;      // [m][Hq][n_chunks][hd] outputs, then [m][Hq][n_chunks][2] (max, sum)
   uint32_t* counters = nullptr;  // [m][Hkv]
   float* cs = nullptr;        // [hd]
   DevState* st = nullptr;
@@ -71,6 +71,8 @@ struct sdec_handle {
   uint64_t ring_layer_stride = 0;   // floats between layers of one stream
 
   std::vector<GemvLaunch> plan_qkv, plan_o, plan_up, plan_down;
+  // one stream: the attention launch leaves its chunk partials and the o projection combines them
+  bool attn_fused = false;
 
   hipStream_t cap_stream = nullptr;
   hipGraphExec_t exec = nullptr;
@@ -246,12 +248,19 @@ int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk) {
     aa.out = att; aa.part = h->part; aa.counters = h->counters;
     aa.m = c.m; aa.n_q_heads = hq; aa.n_kv_heads = hkv; aa.head_dim = hd; aa.ring = h->ring;
     aa.chunk = h->chunk; aa.n_chunks = h->n_chunks; aa.st = h->st;
+    aa.partials_only = h->attn_fused ? 1 : 0;
     LAUNCH(hk, s, SDEC_K_ATTENTION, launch_attention(aa, s));
-    // o projection + (LayerScale) residual
+    // o projection + (LayerScale) residual; with the fused combine its prologue finishes the
+    // attention output from the chunk partials (and copies it to the tap)
     GemvArgs o{};
     o.w[0] = o.w[1] = o.w[2] = w.wo;
     o.seg_end[0] = o.seg_end[1] = o.seg_end[2] = c.d_model;
     o.n_rows = c.d_model; o.k = qw; o.m = c.m; o.x = att; o.x_stride = qw;
+    if (h->attn_fused) {  // x (= att) still carries a single chunk's output
+      o.part = h->part; o.n_legal = h->n_legal;
+      o.chunk = h->chunk; o.n_chunks = h->n_chunks; o.head_dim = hd;
+      o.x_tap = taps ? att : nullptr;
+    }
     o.res = h->xres; o.res_stride = c.d_model; o.ls = c.layer_scale ? w.ls1 : nullptr;
     o.tap = taps ? h->tap_attn_proj + static_cast<size_t>(l) * c.m * c.d_model : nullptr;
     o.tap_stride = c.d_model;
@@ -459,10 +468,15 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
     return A.code;
   }
 
+  if (c.m == 1 && static_cast<size_t>(hq) * h->n_chunks <= kAttnMaxPartials) {
+    const GemvLaunch fused = plan_gemv(PRO_ATTN, EPI_RESIDUAL, c.d_model, qw, c.m);
+    h->attn_fused = gemv_supported(fused, qw, c.m);
+  }
   for (uint32_t l = 0; l < c.n_layers; ++l) {
     h->plan_qkv.push_back(plan_gemv(c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN, EPI_STORE,
                                     qw + 2 * kw, c.d_model, c.m));
-    h->plan_o.push_back(plan_gemv(PRO_NONE, EPI_RESIDUAL, c.d_model, qw, c.m));
+    h->plan_o.push_back(plan_gemv(h->attn_fused ? PRO_ATTN : PRO_NONE, EPI_RESIDUAL, c.d_model, qw,
+                                  c.m));
     h->plan_up.push_back(plan_gemv(c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN,
                                    c.ffn == SDEC_FFN_SWIGLU ? EPI_SWIGLU : EPI_GELU, c.d_ff,
                                    c.d_model, c.m));
