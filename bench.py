@@ -8,8 +8,8 @@ in HBM before the timed region; each step's input row is a slice of a pre-drawn 
 One JSON line on stdout:
   value        steps/s over the K timed steps (one step = the whole layer stack for one position)
   roofline     the dominant kernel (the FFN gate/up GEMV with its fused norm and SwiGLU): its
-               algorithmic bytes per launch / its mean launch time, measured with HIP event pairs
-               around each launch of profiled eager steps
+               algorithmic bytes per launch / its mean launch time, from HIP event pairs that each
+               launch of the profiled eager steps stamps around the kernel's own execution
   cpu_baseline the CPU oracle on a bounded sample of the same run (first positions), host cores
 """
 from __future__ import annotations
@@ -76,15 +76,16 @@ def ffn_up_bytes(cfg):
 
 
 def kernel_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel source they were
-    taken on is the current one; else None."""
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel sources they were
+    taken on (kernels.hip, dev.h, kernels.h) are the current ones; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    src = open(os.path.join(ROOT, "streaming_ar_transformer_amd", "csrc", "kernels.hip"), "rb").read()
+    src = b"".join(open(os.path.join(ROOT, "streaming_ar_transformer_amd", "csrc", n), "rb").read()
+                   for n in ("kernels.hip", "dev.h", "kernels.h"))
     digest = hashlib.sha256(src).hexdigest()[:16]
     rec = json.load(open(path)).get(f"{kernel}@{workload}")
-    if not rec or rec.get("kernels_hip_sha256_16") != digest:
+    if not rec or rec.get("source_sha256_16") != digest:
         return None
     return rec.get("bytes_per_launch")
 
@@ -196,7 +197,8 @@ def main():
         dec.close()
         return
 
-    # per-kernel launch times from profiled eager steps (HIP event pair around every launch)
+    # per-kernel launch times from profiled eager steps (each launch stamps a HIP event pair around
+    # its own execution)
     xs.copy_(torch.from_numpy(xs_host))
     dec.reset()
     prof = None

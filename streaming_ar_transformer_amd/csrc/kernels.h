@@ -68,6 +68,9 @@ hipError_t launch_gemv(const GemvArgs& a, const GemvLaunch& l, hipStream_t s);
 GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, uint32_t m);
 // Whether a kernel exists for this launch shape.
 bool gemv_supported(const GemvLaunch& l, uint32_t k, uint32_t m);
+// Per-kernel timing: while a pair is set (null to clear), the step-kernel launches of this thread
+// (GEMV, attention, begin, end) stamp `start` and `stop` around their own execution.
+void set_launch_events(hipEvent_t start, hipEvent_t stop);
 
 // Ring attention of one layer for every stream.  In the step it also finishes the new position:
 // qk-RMSNorm and rope of this step's q and k (from the raw q/k/v projection), and the push of the

@@ -12,6 +12,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <hip/hip_ext.h>
+
 #include "dev.h"
 #include "kernels.h"
 
@@ -599,16 +601,31 @@ GemvKernel gemv_pick_m(const GemvLaunch& l, uint32_t k) {
   return {nullptr, 0};
 }
 
+// Timing of the next step-kernel launch of this thread (per-kernel profiles): with a pair set,
+// the launch goes through hipExtLaunchKernel, which stamps both events around the kernel's own
+// execution, so the interval excludes the launch gap.
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+hipError_t launch_timed(const void* fn, dim3 grid, dim3 block, void** params, size_t lds,
+                        hipStream_t s) {
+  if (t_ev_start != nullptr)
+    return hipExtLaunchKernel(fn, grid, block, params, lds, s, t_ev_start, t_ev_stop, 0);
+  return hipLaunchKernel(fn, grid, block, params, lds, s);
+}
+
 template <int HD>
 hipError_t launch_attention_hd(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.n_chunks, a.n_kv_heads, a.m);
+  const void* fn = nullptr;
   switch (a.n_q_heads / a.n_kv_heads) {
-    case 1: hipLaunchKernelGGL((k_attention<HD, 1>), grid, dim3(kWgThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_attention<HD, 2>), grid, dim3(kWgThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_attention<HD, 4>), grid, dim3(kWgThreads), 0, s, a); break;
+    case 1: fn = reinterpret_cast<const void*>(&k_attention<HD, 1>); break;
+    case 2: fn = reinterpret_cast<const void*>(&k_attention<HD, 2>); break;
+    case 4: fn = reinterpret_cast<const void*>(&k_attention<HD, 4>); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  AttnArgs args = a;
+  void* params[] = {&args};
+  return launch_timed(fn, grid, dim3(kWgThreads), params, 0, s);
 }
 
 }  // namespace
@@ -686,7 +703,7 @@ hipError_t launch_gemv(const GemvArgs& a, const GemvLaunch& l, hipStream_t s) {
   if (kern.fn == nullptr) return hipErrorInvalidValue;
   GemvArgs args = a;
   void* params[] = {&args};
-  return hipLaunchKernel(kern.fn, dim3(l.grid), dim3(l.waves_per_wg * kWave), params, kern.lds, s);
+  return launch_timed(kern.fn, dim3(l.grid), dim3(l.waves_per_wg * kWave), params, kern.lds, s);
 }
 
 uint32_t attention_chunk(uint32_t head_dim) {
@@ -703,8 +720,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_begin(const BeginArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_begin, dim3(a.m), dim3(kWgThreads), 0, s, a);
-  return hipGetLastError();
+  BeginArgs args = a;
+  void* params[] = {&args};
+  return launch_timed(reinterpret_cast<const void*>(&k_begin), dim3(a.m), dim3(kWgThreads), params, 0, s);
 }
 
 hipError_t launch_compact_legal(const uint32_t* pos_rings, uint32_t m, uint32_t ring, uint32_t pos,
@@ -715,8 +733,14 @@ hipError_t launch_compact_legal(const uint32_t* pos_rings, uint32_t m, uint32_t 
 }
 
 hipError_t launch_end(const EndArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_end, dim3(a.m), dim3(kWgThreads), 0, s, a);
-  return hipGetLastError();
+  EndArgs args = a;
+  void* params[] = {&args};
+  return launch_timed(reinterpret_cast<const void*>(&k_end), dim3(a.m), dim3(kWgThreads), params, 0, s);
+}
+
+void set_launch_events(hipEvent_t start, hipEvent_t stop) {
+  t_ev_start = start;
+  t_ev_stop = stop;
 }
 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, uint64_t n, hipStream_t s) {

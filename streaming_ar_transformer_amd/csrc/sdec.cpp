@@ -192,15 +192,18 @@ struct Hooks {
   int cap = 0;
 };
 
+// The events of a profiled launch are stamped by the launch itself, around the kernel's execution.
 int hook_pre(Hooks* k, hipStream_t s) {
+  (void)s;
   if (!k) return SDEC_OK;
   if (k->n >= k->cap) return fail(SDEC_E_ARG, "profile event buffer too small");
-  HIP_TRY(hipEventRecord(k->ev[2 * k->n], s));
+  set_launch_events(k->ev[2 * k->n], k->ev[2 * k->n + 1]);
   return SDEC_OK;
 }
 int hook_post(Hooks* k, hipStream_t s, int kind) {
+  (void)s;
   if (!k) return SDEC_OK;
-  HIP_TRY(hipEventRecord(k->ev[2 * k->n + 1], s));
+  set_launch_events(nullptr, nullptr);
   k->kinds[k->n++] = kind;
   return SDEC_OK;
 }
@@ -210,8 +213,10 @@ int hook_post(Hooks* k, hipStream_t s, int kind) {
     int r_ = hook_pre(hooks, stream);                                                   \
     if (r_ != SDEC_OK) return r_;                                                       \
     hipError_t e_ = (call);                                                             \
-    if (e_ != hipSuccess) return fail(SDEC_E_HIP, "launch of %s failed: %s", #kind,     \
-                                      hipGetErrorString(e_));                           \
+    if (e_ != hipSuccess) {                                                             \
+      set_launch_events(nullptr, nullptr);                                              \
+      return fail(SDEC_E_HIP, "launch of %s failed: %s", #kind, hipGetErrorString(e_)); \
+    }                                                                                   \
     r_ = hook_post(hooks, stream, kind);                                                \
     if (r_ != SDEC_OK) return r_;                                                       \
   } while (0)
