@@ -379,7 +379,7 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
   }
-  for (uint32_t i0 = grp;;) {
+  for (uint32_t i0 = grp; i0 < total;) {  // a group past the item's end has nothing to score
     // all UNR scores of the pass first (independent chains), then one softmax update per head
     float sc[UNR][G];
 #pragma unroll

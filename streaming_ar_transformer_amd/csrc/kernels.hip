@@ -97,51 +97,61 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, float4* xs, uint32_t 
 // launch wrote it to x; otherwise it is combined here from the chunk partials (the attention's
 // softmax, finished here): for each head, with M the largest chunk maximum,
 // out = sum_c e^(M_c - M) O_c / sum_c e^(M_c - M) L_c ([talker] GQA_ATTN_SRC; [mimi] attn_src).
-// Run by the whole workgroup.  The legal-slot count comes through the scalar cache, so the row (or
-// every partial of up to IB chunks) is requested before `issue_weights` streams the weights and
-// the combine overlaps them.
-template <int KB, typename F>
-__device__ __forceinline__ void attn_input(const GemvArgs& a, float4 (&xr)[KB], F issue_weights) {
+// Run by the whole workgroup.  The legal-slot count comes through the scalar cache; then the row,
+// or every partial of up to IB chunks, is requested before `issue_weights` streams the weights, so
+// the combine overlaps them.  Every load here is unconditional (indices are clamped to valid
+// entries and unused values are never read): with no branches around them the compiler waits for
+// the partials alone, not for the weights requested after them.
+template <int KB>
+struct CombineSmem {
+  float4 xsh[KB * kWave];
+  float msh[kAttnMaxPartials], lsh[kAttnMaxPartials];
+};
+
+template <int KB, int IB, typename F>
+__device__ __forceinline__ void attn_combine(const GemvArgs& a, uint32_t n_items, float4 (&xr)[KB],
+                                             F issue_weights, CombineSmem<KB>& sm) {
   constexpr int K4 = KB * kWave;
   constexpr int PER = (K4 + kWgThreads - 1) / kWgThreads;  // row float4 per thread
-  constexpr int IB = 16;                                   // chunks per batch
-  __shared__ float4 xsh[K4];
-  __shared__ float msh[kAttnMaxPartials], lsh[kAttnMaxPartials];
+  float4* xsh = sm.xsh;
+  float* msh = sm.msh;
+  float* lsh = sm.lsh;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const uint32_t HD = a.head_dim, hq = a.k / HD, nc = a.n_chunks;
-  typedef const __attribute__((address_space(4))) uint32_t ConstU32;
-  const uint32_t nl = *((ConstU32*)a.n_legal);
-  const uint32_t n_items = min((nl + a.chunk - 1) / a.chunk, nc);
-  if (n_items <= 1) {
-    const float4* x4 = reinterpret_cast<const float4*>(a.x);
-#pragma unroll
-    for (int j = 0; j < KB; ++j) xr[j] = x4[lane + kWave * j];
-    issue_weights();
-    if (a.x_tap != nullptr && blockIdx.x == 0)
-      for (uint32_t c4 = tid; c4 < K4; c4 += kWgThreads)
-        reinterpret_cast<float4*>(a.x_tap)[c4] = x4[c4];
-    return;
-  }
   const float* ml = a.part + static_cast<size_t>(hq) * nc * HD;
+  const uint32_t n_ml = hq * n_items;
   float4 o[PER][IB];
   auto load_batch = [&](uint32_t i0) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const uint32_t c4 = tid + p * kWgThreads, h = 4 * c4 / HD, d = 4 * c4 % HD;
+      const uint32_t c4 = min(static_cast<uint32_t>(tid + p * kWgThreads), static_cast<uint32_t>(K4 - 1));
+      const uint32_t h = 4 * c4 / HD, d = 4 * c4 % HD;
 #pragma unroll
-      for (int i = 0; i < IB; ++i)
-        o[p][i] = c4 < K4 && i0 + i < n_items
-                      ? *reinterpret_cast<const float4*>(a.part + (static_cast<size_t>(h) * nc + i0 + i) * HD + d)
-                      : f4zero();
+      for (int i = 0; i < IB; ++i) {
+        const uint32_t c = min(i0 + i, n_items - 1);
+        o[p][i] = *reinterpret_cast<const float4*>(a.part + (static_cast<size_t>(h) * nc + c) * HD + d);
+      }
     }
   };
   load_batch(0);
-  for (uint32_t e = tid; e < hq * n_items; e += kWgThreads) {
+  constexpr int MLP = (kAttnMaxPartials + kWgThreads - 1) / kWgThreads;
+  float mv[MLP], lv[MLP];
+#pragma unroll
+  for (int k = 0; k < MLP; ++k) {
+    const uint32_t e = min(static_cast<uint32_t>(tid + k * kWgThreads), n_ml - 1);
     const uint32_t h = e / n_items, i = e % n_items;
-    msh[e] = ml[(static_cast<size_t>(h) * nc + i) * 2];
-    lsh[e] = ml[(static_cast<size_t>(h) * nc + i) * 2 + 1];
+    mv[k] = ml[(static_cast<size_t>(h) * nc + i) * 2];
+    lv[k] = ml[(static_cast<size_t>(h) * nc + i) * 2 + 1];
   }
   issue_weights();
+#pragma unroll
+  for (int k = 0; k < MLP; ++k) {
+    const uint32_t e = tid + k * kWgThreads;
+    if (e < n_ml) {
+      msh[e] = mv[k];
+      lsh[e] = lv[k];
+    }
+  }
   __syncthreads();
   for (uint32_t h = tid; h < hq; h += kWgThreads) {  // chunk weights e^(M_c - M) / L
     float mx = -INFINITY;
@@ -164,30 +174,54 @@ __device__ __forceinline__ void attn_input(const GemvArgs& a, float4 (&xr)[KB], 
   for (uint32_t i0 = 0;;) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const uint32_t c4 = tid + p * kWgThreads, h = 4 * c4 / HD;
+      const uint32_t c4 = min(static_cast<uint32_t>(tid + p * kWgThreads), static_cast<uint32_t>(K4 - 1));
+      const uint32_t h = 4 * c4 / HD;
 #pragma unroll
       for (int i = 0; i < IB; ++i) {
-        if (c4 < K4 && i0 + i < n_items) {
-          const float w = msh[h * n_items + i0 + i];
-          acc[p].x = fmaf(w, o[p][i].x, acc[p].x); acc[p].y = fmaf(w, o[p][i].y, acc[p].y);
-          acc[p].z = fmaf(w, o[p][i].z, acc[p].z); acc[p].w = fmaf(w, o[p][i].w, acc[p].w);
-        }
+        const float w = i0 + i < n_items ? msh[h * n_items + i0 + i] : 0.f;
+        acc[p].x = fmaf(w, o[p][i].x, acc[p].x); acc[p].y = fmaf(w, o[p][i].y, acc[p].y);
+        acc[p].z = fmaf(w, o[p][i].z, acc[p].z); acc[p].w = fmaf(w, o[p][i].w, acc[p].w);
       }
     }
     i0 += IB;
     if (i0 >= n_items) break;
-    load_batch(i0);
+    load_batch(i0);  // more than IB chunks: these wait behind the weights
   }
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
     const uint32_t c4 = tid + p * kWgThreads;
-    if (c4 < K4) xsh[c4] = acc[p];
+    if (c4 < static_cast<uint32_t>(K4)) xsh[c4] = acc[p];
   }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < KB; ++j) xr[j] = xsh[lane + kWave * j];
   if (a.x_tap != nullptr && blockIdx.x == 0)
-    for (uint32_t c4 = tid; c4 < K4; c4 += kWgThreads) reinterpret_cast<float4*>(a.x_tap)[c4] = xsh[c4];
+    for (uint32_t c4 = tid; c4 < static_cast<uint32_t>(K4); c4 += kWgThreads)
+      reinterpret_cast<float4*>(a.x_tap)[c4] = xsh[c4];
+}
+
+template <int KB, typename F>
+__device__ __forceinline__ void attn_input(const GemvArgs& a, float4 (&xr)[KB], F issue_weights) {
+  __shared__ CombineSmem<KB> sm;
+  typedef const __attribute__((address_space(4))) uint32_t ConstU32;
+  const uint32_t nl = *((ConstU32*)a.n_legal);
+  const uint32_t n_items = min((nl + a.chunk - 1) / a.chunk, a.n_chunks);
+  if (n_items <= 1) {
+    const float4* x4 = reinterpret_cast<const float4*>(a.x);
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) xr[j] = x4[lane + kWave * j];
+    issue_weights();
+    if (a.x_tap != nullptr && blockIdx.x == 0)
+      for (uint32_t c4 = threadIdx.x; c4 < static_cast<uint32_t>(KB * kWave); c4 += kWgThreads)
+        reinterpret_cast<float4*>(a.x_tap)[c4] = x4[c4];
+  } else if (n_items <= 4) {
+    attn_combine<KB, 4>(a, n_items, xr, issue_weights, sm);
+  } else if (n_items <= 8) {
+    attn_combine<KB, 8>(a, n_items, xr, issue_weights, sm);
+  } else {
+    attn_combine<KB, 16>(a, n_items, xr, issue_weights, sm);
+  }
 }
 
 template <int M, int R, int PRO, int EPI, int KB>
@@ -212,9 +246,15 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
       for (int r = 0; r < R; ++r) w[j][r] = ldw(wr[r] + lane + kWave * j);
   };
   auto load_first = [&]() {
-    if (t < t_end) load_tile(t, w0);
-    if constexpr (kTwo)
+    if constexpr (kTwo) {
+      if (t < t_end) load_tile(t, w0);
       if (t + 1 < t_end) load_tile(t + 1, w1);
+    } else {
+      // unconditional (a wave without a tile loads the last one and never uses it): no branch
+      // here, so waits for loads issued before it need not cover these
+      const uint32_t n_tiles = (a.n_rows + RH - 1) / RH;
+      load_tile(t < t_end ? t : n_tiles - 1, w0);
+    }
   };
 
   float4 xr[M][KB];
