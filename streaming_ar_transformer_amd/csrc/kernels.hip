@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
     for (int m = 0; m < M; ++m)
 #pragma unroll
       for (int j = 0; j < KB; ++j)
-        xr[m][j] = m < static_cast<int>(a.m) ? x4[m * xs4 + lane + kWave * j] : f4zero();
+        xr[m][j] = m == 0 || m < static_cast<int>(a.m) ? x4[m * xs4 + lane + kWave * j] : f4zero();
   }
   float4 gr[PRO == PRO_RMS || PRO == PRO_LN ? KB : 1], br[PRO == PRO_LN ? KB : 1];
   if (PRO == PRO_RMS || PRO == PRO_LN) {
@@ -285,6 +285,9 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
 #pragma unroll
     for (int j = 0; j < KB; ++j) br[j] = b4[lane + kWave * j];
   }
+  // Loads complete in issue order: keep the weight loads after the row and gain loads, so the norm
+  // arithmetic does not wait for the first tile of weights.
+  asm volatile("" ::: "memory");
   if constexpr (PRO != PRO_ATTN) load_first();
 
   if (PRO == PRO_RMS || PRO == PRO_LN) {
