@@ -14,10 +14,40 @@ namespace dev {
 
 constexpr int kWave = 64;
 
+// Cross-lane moves without LDS traffic.  DPP reaches lanes inside a 16-lane row (swap neighbours,
+// swap pairs, mirror halves of 8, mirror the row); gfx950's permlane swaps exchange whole rows
+// between two registers: permlane16 swaps the odd rows of the first with the even rows of the
+// second, permlane32 the upper half of the first with the lower half of the second.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+// Over the row pairs (0,1) and (2,3): the even row of each pair gets a[even] + a[odd], the odd
+// row b[even] + b[odd] (lane by lane).
+__device__ __forceinline__ float rows16_sum(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// Over the two halves of the wave: the lower half gets a[lo] + a[hi], the upper b[lo] + b[hi].
+__device__ __forceinline__ float halves_sum(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// The value of lane l ^ 32.
+__device__ __forceinline__ float partner32(float x, int lane) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((lane & 32) ? p[0] : p[1]);
+}
+
+// Sum over the whole wave, left in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dpp_mov<kDppXor1>(v);
+  v += dpp_mov<kDppXor2>(v);
+  v += dpp_mov<kDppHalfMirror>(v);
+  v += dpp_mov<kDppMirror>(v);
+  v = rows16_sum(v, v);
+  return halves_sum(v, v);
 }
 
 __device__ __forceinline__ float4 f4zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
@@ -55,45 +85,61 @@ __device__ __forceinline__ float dot4(float4 w, float4 x, float acc) {
   return fmaf(w.w, x.w, acc);
 }
 
-// Butterfly reduce-scatter of V per-lane partial sums across the wave.  Each halving step swaps
-// half of the values with the lane `off` away, so after log2(V) steps lane l holds the wave total
-// of value index l / (64 / V); the remaining offsets finish the sum inside each lane group.
+// Butterfly reduce-scatter of V per-lane partial sums across the wave.  Each halving step pairs
+// every lane with one in the other half of its OFF-block and keeps half of the values, so after
+// log2(V) steps lane l holds the wave total of value index l / (64 / V); the remaining steps
+// finish the sum inside each lane group.  Steps across 32 and 16 lanes use the permlane swaps,
+// the rest DPP moves (partners: the mirror lane within 16, within 8, then the quad swaps).
+template <int OFF>
+__device__ __forceinline__ float dpp_partner(float x) {
+  static_assert(OFF == 8 || OFF == 4 || OFF == 2 || OFF == 1, "inside a 16-lane row");
+  if constexpr (OFF == 8) return dpp_mov<kDppMirror>(x);
+  else if constexpr (OFF == 4) return dpp_mov<kDppHalfMirror>(x);
+  else if constexpr (OFF == 2) return dpp_mov<kDppXor2>(x);
+  else return dpp_mov<kDppXor1>(x);
+}
 template <int V, int OFF>
 struct ReduceScatter {
   static __device__ __forceinline__ void run(float* v, int lane) {
     constexpr int H = V / 2;
-    const bool upper = (lane & OFF) != 0;
 #pragma unroll
     for (int i = 0; i < H; ++i) {
-      const float send = upper ? v[i] : v[i + H];
-      const float keep = upper ? v[i + H] : v[i];
-      v[i] = keep + __shfl_xor(send, OFF, kWave);
+      if constexpr (OFF == 32) {
+        v[i] = halves_sum(v[i], v[i + H]);
+      } else if constexpr (OFF == 16) {
+        v[i] = rows16_sum(v[i], v[i + H]);
+      } else {
+        const bool upper = (lane & OFF) != 0;
+        const float send = upper ? v[i] : v[i + H];
+        const float keep = upper ? v[i + H] : v[i];
+        v[i] = keep + dpp_partner<OFF>(send);
+      }
     }
     ReduceScatter<H, OFF / 2>::run(v, lane);
   }
 };
 template <int OFF>
-struct ReduceScatter<1, OFF> {
+struct ReduceScatter<1, OFF> {  // full sums over aligned blocks of 2 * OFF lanes
   static __device__ __forceinline__ void run(float* v, int) {
-#pragma unroll
-    for (int off = OFF; off > 0; off >>= 1) v[0] += __shfl_xor(v[0], off, kWave);
+    float x = v[0];
+    if constexpr (OFF >= 8) x += dpp_partner<8>(x);
+    if constexpr (OFF >= 4) x += dpp_partner<4>(x);
+    if constexpr (OFF >= 2) x += dpp_partner<2>(x);
+    if constexpr (OFF >= 1) x += dpp_partner<1>(x);
+    if constexpr (OFF >= 16) x = rows16_sum(x, x);
+    if constexpr (OFF >= 32) x = halves_sum(x, x);
+    v[0] = x;
   }
 };
 
-// Sum over aligned groups of N lanes (N = 8 or 16), left in every lane of the group: DPP lane
-// moves inside a 16-lane row (swap neighbours, swap pairs, mirror halves of 8, mirror the row), so
-// no LDS traffic is involved.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
-}
+// Sum over aligned groups of N lanes (N = 8 or 16), left in every lane of the group.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
   static_assert(N == 8 || N == 16, "DPP rows hold 16 lanes");
-  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_mov<0x141>(v);  // row_half_mirror
-  if (N == 16) v += dpp_mov<0x140>(v);  // row_mirror
+  v += dpp_mov<kDppXor1>(v);
+  v += dpp_mov<kDppXor2>(v);
+  v += dpp_mov<kDppHalfMirror>(v);
+  if (N == 16) v += dpp_mov<kDppMirror>(v);
   return v;
 }
 
@@ -170,7 +216,7 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, uint32_t t, flo
   const bool owner = (lane % S) == 0;
   const int r = idx / M, m = idx % M;
   if (EPI == EPI_SWIGLU) {
-    const float up = __shfl_xor(val, 32, kWave);
+    const float up = partner32(val, lane);
     const uint32_t i = t * RH + r;
     if (owner && lane < 32 && i < a.n_rows && m < static_cast<int>(a.m))
       put<COH>(a.y + m * a.y_stride + i, silu(val) * up);
