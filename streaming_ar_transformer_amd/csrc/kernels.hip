@@ -230,11 +230,16 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
   static_assert(V <= 64, "tile too large for one wave");
   constexpr int RH = EPI == EPI_SWIGLU ? R / 2 : R;
   const int lane = threadIdx.x & (kWave - 1);
-  uint32_t t, t_end;
-  wave_tiles((a.n_rows + RH - 1) / RH, t, t_end);
+  // Wave w owns tiles w, w + W, w + 2W, ... (W waves in the grid): at any moment the waves stream
+  // neighbouring rows, which the DRAM pages serve better than far-apart contiguous ranges.
+  const uint32_t n_tiles = (a.n_rows + RH - 1) / RH;
+  const uint32_t ts = gridDim.x * (blockDim.x / kWave);
+  uint32_t t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const uint32_t t_end = n_tiles;
 
-  // Two tiles of weight rows in flight: tile t+2 is requested as soon as tile t is reduced (the
-  // attention-combine variant keeps one: its registers hold the chunk partials instead).
+  // Two of the wave's tiles of weight rows in flight: the one after next is requested as soon as a
+  // tile is reduced (the attention-combine variant keeps one: its registers hold the chunk
+  // partials instead).
   constexpr bool kTwo = PRO != PRO_ATTN;
   float4 w0[KB][R], w1[kTwo ? KB : 1][R];
   auto load_tile = [&](uint32_t tt, float4 (&w)[KB][R]) {
@@ -248,11 +253,10 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
   auto load_first = [&]() {
     if constexpr (kTwo) {
       if (t < t_end) load_tile(t, w0);
-      if (t + 1 < t_end) load_tile(t + 1, w1);
+      if (t + ts < t_end) load_tile(t + ts, w1);
     } else {
       // unconditional (a wave without a tile loads the last one and never uses it): no branch
       // here, so waits for loads issued before it need not cover these
-      const uint32_t n_tiles = (a.n_rows + RH - 1) / RH;
       load_tile(t < t_end ? t : n_tiles - 1, w0);
     }
   };
@@ -347,16 +351,16 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
     // ping-pong between the two register buffers (unrolled: registers cannot be indexed)
     while (true) {
       reduce_tile(t, w0);
-      if (t + 2 < t_end) load_tile(t + 2, w0);
-      if (++t >= t_end) break;
+      if (t + 2 * ts < t_end) load_tile(t + 2 * ts, w0);
+      if ((t += ts) >= t_end) break;
       reduce_tile(t, w1);
-      if (t + 2 < t_end) load_tile(t + 2, w1);
-      if (++t >= t_end) break;
+      if (t + 2 * ts < t_end) load_tile(t + 2 * ts, w1);
+      if ((t += ts) >= t_end) break;
     }
   } else {
     while (true) {
       reduce_tile(t, w0);
-      if (++t >= t_end) break;
+      if ((t += ts) >= t_end) break;
       load_tile(t, w0);
     }
   }
