@@ -205,8 +205,29 @@ __device__ __forceinline__ void tile_rows(const GemvArgs& a, uint32_t t, const f
 // Reduce the tile's R*M lane partials and apply the epilogue: store, GELU, SwiGLU (gate row r and
 // up row r + R/2 of the same FFN index sit 32 lanes apart after the reduce-scatter), or the
 // (LayerScale) residual add ([mimi] MV_LS: y += ls * (W x)).
+// The old residual value (and LayerScale) that this lane's output of tile t needs: requested
+// together with the tile's weights, so the residual epilogue does not start a dependent load.
+struct ResPre {
+  float res = 0.f, ls = 1.f;
+};
+template <int M, int R, int EPI>
+__device__ __forceinline__ ResPre residual_prefetch(const GemvArgs& a, uint32_t t, int lane) {
+  ResPre p;
+  if constexpr (EPI == EPI_RESIDUAL) {
+    constexpr int V = R * M;
+    constexpr int S = kWave / V;
+    const int idx = lane / S;
+    const uint32_t r = idx / M, m = min(static_cast<uint32_t>(idx % M), a.m - 1);
+    const uint32_t row = min(t * R + r, a.n_rows - 1);
+    p.res = ((a.res_in ? a.res_in : a.res) + m * a.res_stride)[row];
+    if (a.ls) p.ls = a.ls[row];
+  }
+  return p;
+}
+
 template <int M, int R, int EPI, bool COH = false>
-__device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, uint32_t t, float* acc, int lane) {
+__device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, uint32_t t, float* acc, int lane,
+                                              const ResPre* pre = nullptr) {
   constexpr int V = R * M;
   constexpr int S = kWave / V;
   constexpr int RH = EPI == EPI_SWIGLU ? R / 2 : R;
@@ -229,8 +250,12 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, uint32_t t, flo
         put<COH>(a.y + m * a.y_stride + row, gelu_erf(val));
       } else {
         if (a.tap) a.tap[m * a.tap_stride + row] = val;
-        const float* src = (a.res_in ? a.res_in : a.res) + m * a.res_stride + row;
-        put<COH>(a.res + m * a.res_stride + row, *src + (a.ls ? a.ls[row] * val : val));
+        if (pre) {
+          put<COH>(a.res + m * a.res_stride + row, pre->res + (a.ls ? pre->ls * val : val));
+        } else {
+          const float* src = (a.res_in ? a.res_in : a.res) + m * a.res_stride + row;
+          put<COH>(a.res + m * a.res_stride + row, *src + (a.ls ? a.ls[row] * val : val));
+        }
       }
     }
   }

@@ -242,22 +242,24 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
   // partials instead).
   constexpr bool kTwo = PRO != PRO_ATTN;
   float4 w0[KB][R], w1[kTwo ? KB : 1][R];
-  auto load_tile = [&](uint32_t tt, float4 (&w)[KB][R]) {
+  ResPre p0, p1;
+  auto load_tile = [&](uint32_t tt, float4 (&w)[KB][R], ResPre& p) {
     const float4* wr[R];
     tile_rows<R, EPI>(a, tt, wr);
 #pragma unroll
     for (int j = 0; j < KB; ++j)
 #pragma unroll
       for (int r = 0; r < R; ++r) w[j][r] = ldw(wr[r] + lane + kWave * j);
+    p = residual_prefetch<M, R, EPI>(a, tt, lane);
   };
   auto load_first = [&]() {
     if constexpr (kTwo) {
-      if (t < t_end) load_tile(t, w0);
-      if (t + ts < t_end) load_tile(t + ts, w1);
+      if (t < t_end) load_tile(t, w0, p0);
+      if (t + ts < t_end) load_tile(t + ts, w1, p1);
     } else {
       // unconditional (a wave without a tile loads the last one and never uses it): no branch
       // here, so waits for loads issued before it need not cover these
-      load_tile(t < t_end ? t : n_tiles - 1, w0);
+      load_tile(t < t_end ? t : n_tiles - 1, w0, p0);
     }
   };
 
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
     }
   }
 
-  auto reduce_tile = [&](uint32_t tt, const float4 (&w)[KB][R]) {
+  auto reduce_tile = [&](uint32_t tt, const float4 (&w)[KB][R], const ResPre& p) {
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
@@ -345,23 +347,23 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
       for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r * M + m] = dot4(w[j][r], xr[m][j], acc[r * M + m]);
-    gemv_epilogue<M, R, EPI>(a, tt, acc, lane);
+    gemv_epilogue<M, R, EPI>(a, tt, acc, lane, &p);
   };
   if constexpr (kTwo) {
     // ping-pong between the two register buffers (unrolled: registers cannot be indexed)
     while (true) {
-      reduce_tile(t, w0);
-      if (t + 2 * ts < t_end) load_tile(t + 2 * ts, w0);
+      reduce_tile(t, w0, p0);
+      if (t + 2 * ts < t_end) load_tile(t + 2 * ts, w0, p0);
       if ((t += ts) >= t_end) break;
-      reduce_tile(t, w1);
-      if (t + 2 * ts < t_end) load_tile(t + 2 * ts, w1);
+      reduce_tile(t, w1, p1);
+      if (t + 2 * ts < t_end) load_tile(t + 2 * ts, w1, p1);
       if ((t += ts) >= t_end) break;
     }
   } else {
     while (true) {
-      reduce_tile(t, w0);
+      reduce_tile(t, w0, p0);
       if ((t += ts) >= t_end) break;
-      load_tile(t, w0);
+      load_tile(t, w0, p0);
     }
   }
 }
