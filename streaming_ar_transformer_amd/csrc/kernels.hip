@@ -238,9 +238,10 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
   const uint32_t t_end = n_tiles;
 
   // Two of the wave's tiles of weight rows in flight: the one after next is requested as soon as a
-  // tile is reduced (the attention-combine variant keeps one: its registers hold the chunk
-  // partials instead).
-  constexpr bool kTwo = PRO != PRO_ATTN;
+  // tile is reduced.  The attention-combine variant keeps one (its registers hold the chunk
+  // partials instead), and so do the 6144-wide rows: with one 24 KiB row per wave in flight the
+  // rows reach DRAM in a more orderly stream (measured 10.3 vs 10.7 us for 2048 x 6144).
+  constexpr bool kTwo = PRO != PRO_ATTN && KB != 24;
   float4 w0[KB][R], w1[kTwo ? KB : 1][R];
   ResPre p0, p1;
   auto load_tile = [&](uint32_t tt, float4 (&w)[KB][R], ResPre& p) {
@@ -734,7 +735,8 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern.fn, kWgThreads, kern.lds) !=
           hipSuccess || occ < 1)
     occ = 1;
-  const int cap = env_int("SDEC_GEMV_WGS_PER_CU", 4);
+  // workgroups per CU: at most 4, and 1 for the 6144-wide rows (see k_gemv_rx)
+  const int cap = l.kb == 24 ? 1 : env_int("SDEC_GEMV_WGS_PER_CU", 4);
   if (occ > cap) occ = cap;
   const uint32_t max_wgs = static_cast<uint32_t>(cus * occ);
   uint32_t wgs = (tiles + l.waves_per_wg - 1) / l.waves_per_wg;
