@@ -143,6 +143,16 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(N == 8 || N == 16, "DPP rows hold 16 lanes");
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  if (N == 16) v = fmaxf(v, dpp_mov<kDppMirror>(v));
+  return v;
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));

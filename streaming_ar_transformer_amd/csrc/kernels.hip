@@ -105,7 +105,7 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, float4* xs, uint32_t 
 template <int KB>
 struct CombineSmem {
   float4 xsh[KB * kWave];
-  float msh[kAttnMaxPartials], lsh[kAttnMaxPartials];
+  float msh[kAttnMaxPartials];
 };
 
 template <int KB, int IB, typename F>
@@ -115,11 +115,9 @@ __device__ __forceinline__ void attn_combine(const GemvArgs& a, uint32_t n_items
   constexpr int PER = (K4 + kWgThreads - 1) / kWgThreads;  // row float4 per thread
   float4* xsh = sm.xsh;
   float* msh = sm.msh;
-  float* lsh = sm.lsh;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const uint32_t HD = a.head_dim, hq = a.k / HD, nc = a.n_chunks;
   const float* ml = a.part + static_cast<size_t>(hq) * nc * HD;
-  const uint32_t n_ml = hq * n_items;
   float4 o[PER][IB];
   auto load_batch = [&](uint32_t i0) {
 #pragma unroll
@@ -134,38 +132,45 @@ __device__ __forceinline__ void attn_combine(const GemvArgs& a, uint32_t n_items
     }
   };
   load_batch(0);
-  constexpr int MLP = (kAttnMaxPartials + kWgThreads - 1) / kWgThreads;
-  float mv[MLP], lv[MLP];
+  // chunk weights e^(M_c - M) / L: 16 lanes per head (one DPP row), lane j of the row takes chunks
+  // j, j + 16, ...; the first 16 heads' (max, sum) pairs are requested before the weights
+  constexpr int CPL = kAttnMaxChunks / 16;
+  constexpr uint32_t HPP = kWgThreads / 16;  // heads per pass
+  const uint32_t sub = lane & 15;
+  float mv[CPL], lv[CPL];
+  auto load_ml = [&](uint32_t h) {
+    const uint32_t hc = min(h, hq - 1);
 #pragma unroll
-  for (int k = 0; k < MLP; ++k) {
-    const uint32_t e = min(static_cast<uint32_t>(tid + k * kWgThreads), n_ml - 1);
-    const uint32_t h = e / n_items, i = e % n_items;
-    mv[k] = ml[(static_cast<size_t>(h) * nc + i) * 2];
-    lv[k] = ml[(static_cast<size_t>(h) * nc + i) * 2 + 1];
-  }
+    for (int j = 0; j < CPL; ++j) {
+      const uint32_t i = min(sub + 16u * j, n_items - 1);
+      mv[j] = ml[(static_cast<size_t>(hc) * nc + i) * 2];
+      lv[j] = ml[(static_cast<size_t>(hc) * nc + i) * 2 + 1];
+    }
+  };
+  load_ml(tid / 16);
   issue_weights();
-#pragma unroll
-  for (int k = 0; k < MLP; ++k) {
-    const uint32_t e = tid + k * kWgThreads;
-    if (e < n_ml) {
-      msh[e] = mv[k];
-      lsh[e] = lv[k];
-    }
-  }
-  __syncthreads();
-  for (uint32_t h = tid; h < hq; h += kWgThreads) {  // chunk weights e^(M_c - M) / L
+  for (uint32_t h = tid / 16;;) {  // the 16 lanes of a row share h, so the row shuffles are whole
     float mx = -INFINITY;
-    for (uint32_t i = 0; i < n_items; ++i) mx = fmaxf(mx, msh[h * n_items + i]);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+      if (sub + 16u * j < n_items) mx = fmaxf(mx, mv[j]);
+    mx = group_max<16>(mx);
     float l = 0.f;
-    for (uint32_t i = 0; i < n_items; ++i) {
-      const float mi = msh[h * n_items + i];
-      if (mi != -INFINITY) l = fmaf(expf(mi - mx), lsh[h * n_items + i], l);
-    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+      if (sub + 16u * j < n_items && mv[j] != -INFINITY) l = fmaf(expf(mv[j] - mx), lv[j], l);
+    l = group_sum<16>(l);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    for (uint32_t i = 0; i < n_items; ++i) {
-      const float mi = msh[h * n_items + i];
-      msh[h * n_items + i] = mi != -INFINITY ? expf(mi - mx) * inv : 0.f;
+    if (h < hq) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const uint32_t i = sub + 16u * j;
+        if (i < n_items) msh[h * n_items + i] = mv[j] != -INFINITY ? expf(mv[j] - mx) * inv : 0.f;
+      }
     }
+    h += HPP;
+    if (h >= hq) break;
+    load_ml(h);
   }
   __syncthreads();
   float4 acc[PER];

@@ -8,6 +8,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -475,7 +476,8 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
 
   if (c.m == 1 && static_cast<size_t>(hq) * h->n_chunks <= kAttnMaxPartials) {
     const GemvLaunch fused = plan_gemv(PRO_ATTN, EPI_RESIDUAL, c.d_model, qw, c.m);
-    h->attn_fused = gemv_supported(fused, qw, c.m);
+    const char* fe = std::getenv("SDEC_ATTN_COMBINE_IN_O");  // tuning override: "0" = combine in attention
+    h->attn_fused = gemv_supported(fused, qw, c.m) && !(fe != nullptr && fe[0] == '0');
   }
   for (uint32_t l = 0; l < c.n_layers; ++l) {
     h->plan_qkv.push_back(plan_gemv(c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN, EPI_STORE,
