@@ -375,21 +375,33 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   const float* qkv = a.qkv + static_cast<size_t>(s) * a.qkv_stride;
 
   // 1. this item's share of the step's legal slots; this step's raw queries (and, for the item
-  //    that pushes, the raw key and value)
+  //    that pushes, the raw key and value).  All of them are requested together with the slot
+  //    count, before it is known which are needed: indices are clamped into the buffers and
+  //    values that turn out unused are dropped, so the item waits for one round trip, not two.
+  static_assert(NT >= 2 * HD, "one thread per raw key or value element");
+  constexpr int QPT = (G * HD + NT - 1) / NT;
   const uint32_t nl = a.n_legal[s];
+  const uint32_t c0 = chunk * a.chunk;
+  const uint32_t slot_of = a.legal[static_cast<size_t>(s) * a.ring + min(c0 + tid, a.ring - 1)];
+  float qv[QPT];
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int t = min(tid + j * NT, G * HD - 1);
+    qv[j] = qkv[(h0 + t / HD) * HD + t % HD];
+  }
+  const int kt = tid % (2 * HD);  // raw key element kt, or value element kt - HD
+  const float kvraw = qkv[(kt < HD ? hq + kvh : hq + hkv + kvh) * HD + kt % HD];
   const uint32_t n_items = (nl + a.chunk - 1) / a.chunk;
   if (chunk >= n_items) return;  // no legal slot falls in this item
-  const uint32_t c0 = chunk * a.chunk;
   const uint32_t total = min(a.chunk, nl - c0);
   const bool lead = a.push && a.st != nullptr && chunk == 0;  // list[0] is the slot pushed now
-  if (static_cast<uint32_t>(tid) < total) list[tid] = a.legal[static_cast<size_t>(s) * a.ring + c0 + tid];
-  for (int t = tid; t < G * HD; t += NT) qs[t / HD][t % HD] = qkv[(h0 + t / HD) * HD + t % HD];
-  if (lead) {
-    for (int t = tid; t < HD; t += NT) {
-      sm.ks[t] = qkv[(hq + kvh) * HD + t];
-      sm.vs[t] = qkv[(hq + hkv + kvh) * HD + t];
-    }
+  if (static_cast<uint32_t>(tid) < total) list[tid] = slot_of;
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int t = tid + j * NT;
+    if (t < G * HD) qs[t / HD][t % HD] = qv[j];
   }
+  if (lead && tid < 2 * HD) (kt < HD ? sm.ks : sm.vs)[kt % HD] = kvraw;
   __syncthreads();
 
   // 2. request this group's first pass of key and value rows
