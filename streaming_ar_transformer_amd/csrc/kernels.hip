@@ -456,6 +456,83 @@ __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// Split-k GEMV for one stream with the (LayerScale) residual epilogue, for wide rows (k = 1024*KW;
+// the FFN down projection, [talker] build_step_plan; [mimi] MV_LS).  The workgroup's four waves
+// take the four quarters of each of its RB rows, so a wave keeps only its quarter of the input in
+// registers and the rows of all workgroups are in flight at once; the quarter sums meet in LDS.
+// Row slot rr of workgroup b is row b + rr * G (G workgroups): at any moment the device streams a
+// dense band of whole rows.
+// ------------------------------------------------------------------------------------------------
+template <int KW, int RB>
+__global__ __launch_bounds__(kWgThreads) void k_gemv_ks(GemvArgs a) {
+  constexpr int NW = kWgThreads / kWave;
+  static_assert(NW == 4 && RB <= kWave, "four quarter-row waves");
+  __shared__ float part[NW][RB];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const uint32_t n = a.n_rows, G = gridDim.x, k4 = a.k >> 2;
+  const uint32_t off = static_cast<uint32_t>(wave) * (KW * kWave) + lane;  // float4 in the row
+  const float4* x4 = reinterpret_cast<const float4*>(a.x);
+  float4 xr[KW];
+#pragma unroll
+  for (int j = 0; j < KW; ++j) xr[j] = x4[off + kWave * j];
+  float4 w[RB][KW];
+  auto row_base = [&](uint32_t row) {
+    const float* base = a.w[0];
+    if (row >= a.seg_end[1]) {
+      base = a.w[2];
+      row -= a.seg_end[1];
+    } else if (row >= a.seg_end[0]) {
+      base = a.w[1];
+      row -= a.seg_end[0];
+    }
+    return reinterpret_cast<const float4*>(base + static_cast<size_t>(row) * a.k) + off;
+  };
+  // every thread requests the old residual and LayerScale of row slot tid % RB (unconditional
+  // loads: threads past RB fetch duplicates that are never used)
+  float res_old = 0.f, ls_v = 1.f;
+  auto load = [&](uint32_t r0) {
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const float4* wr = row_base(min(r0 + rr * G, n - 1));
+#pragma unroll
+      for (int j = 0; j < KW; ++j) w[rr][j] = ldw(wr + kWave * j);
+    }
+    const uint32_t row = min(r0 + (tid % RB) * G, n - 1);
+    res_old = (a.res_in ? a.res_in : a.res)[row];
+    if (a.ls) ls_v = a.ls[row];
+  };
+  asm volatile("" ::: "memory");  // the input quarter is requested before the rows
+  uint32_t r0 = blockIdx.x;
+  load(r0);
+  for (;;) {
+    float acc[RB];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      acc[rr] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KW; ++j) acc[rr] = dot4(w[rr][j], xr[j], acc[rr]);
+    }
+    ReduceScatter<RB, 32>::run(acc, lane);  // lane (64/RB)*rr holds row slot rr's quarter sum
+    if (lane % (kWave / RB) == 0) part[wave][lane / (kWave / RB)] = acc[0];
+    __syncthreads();
+    const uint32_t base = r0;
+    const float res_here = res_old, ls_here = ls_v;
+    r0 += G * RB;
+    if (r0 < n) load(r0);  // the next rows stream while this tile's results are written
+    if (tid < RB) {
+      const uint32_t row = base + tid * G;
+      if (row < n) {
+        const float v = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
+        if (a.tap) a.tap[row] = v;
+        a.res[row] = res_here + (a.ls ? ls_here * v : v);
+      }
+    }
+    if (r0 >= n) return;
+    __syncthreads();  // part is rewritten by the next tile
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // Step begin: copy the caller's rows into the residual stream, start fresh streams (every
 // position-ring slot empty), stamp pos into slot pos mod R of each stream's position ring
 // ([mimi] rope_push_src: pr[slot] = pos), and form this position's rope cos/sin in float64
@@ -642,6 +719,14 @@ GemvKernel gemv_pick_m(const GemvLaunch& l, uint32_t k) {
     }
     return {nullptr, 0};
   }
+  if constexpr (M == 1) {
+    if (l.ks > 0) {
+      if (l.prologue != PRO_NONE || l.epilogue != EPI_RESIDUAL || l.rows_per_wave != 4)
+        return {nullptr, 0};
+      if (l.ks == 6) return {reinterpret_cast<const void*>(&k_gemv_ks<6, 4>), 0};
+      return {nullptr, 0};
+    }
+  }
 #define SDEC_KIND(P, E) \
   if (l.prologue == P && l.epilogue == E) return gemv_pick_r<M, P, E>(l, k);
   SDEC_KIND(PRO_NONE, EPI_STORE)
@@ -709,11 +794,31 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
   const int M = round_m(m);
   const uint32_t kb = k % 256 == 0 ? k / 256 : 0;
   l.kb = 0;
+  l.ks = 0;
   if (M <= 2 && (kb == 2 || kb == 8)) l.kb = static_cast<int>(kb);
   if (M == 1 && kb == 24 && epilogue != EPI_SWIGLU) l.kb = 24;
   int dev = 0, cus = 256, occ = 1;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (M == 1 && k == 6144 && prologue == PRO_NONE && epilogue == EPI_RESIDUAL &&
+      env_int("SDEC_GEMV_SPLITK", 1) != 0) {
+    // four quarter-row waves per workgroup, four rows per workgroup, every row in flight at once
+    l.ks = 6;
+    l.kb = 0;
+    l.rows_per_wave = 4;
+    l.waves_per_wg = kWgThreads / kWave;
+    int occ_ks = 1;
+    const GemvKernel kern = gemv_pick(l, k, m);
+    if (kern.fn == nullptr ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_ks, kern.fn, kWgThreads, 0) != hipSuccess ||
+        occ_ks < 1)
+      occ_ks = 1;
+    const uint32_t need = (n_rows + 3) / 4;
+    const uint32_t max_wgs = static_cast<uint32_t>(cus * occ_ks);
+    l.grid = need < max_wgs ? need : max_wgs;
+    if (l.grid < 1) l.grid = 1;
+    return l;
+  }
   if (l.kb > 0) {
     // rows in flight per wave: enough 16-byte loads per lane to cover the HBM latency
     if (epilogue == EPI_SWIGLU) {
