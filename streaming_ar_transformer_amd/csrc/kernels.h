@@ -22,6 +22,7 @@ struct DevState {
 enum GemvPrologue : int { PRO_NONE = 0, PRO_RMS = 1, PRO_LN = 2, PRO_ATTN = 3 };
 constexpr uint32_t kAttnMaxChunks = 64;      // chunks a PRO_ATTN prologue combines
 constexpr uint32_t kAttnMaxPartials = 1024;  // heads x chunks a PRO_ATTN prologue combines
+constexpr uint32_t kAttnMaxHeads = 16;       // query heads a PRO_ATTN prologue combines
 enum GemvEpilogue : int { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2, EPI_GELU = 3 };
 
 // y = x . W^T over up to three row segments (q, k, v share one launch).  With EPI_SWIGLU the

@@ -133,12 +133,14 @@ __device__ __forceinline__ void attn_combine(const GemvArgs& a, uint32_t n_items
   };
   load_batch(0);
   // chunk weights e^(M_c - M) / L: 16 lanes per head (one DPP row), lane j of the row takes chunks
-  // j, j + 16, ...; the first 16 heads' (max, sum) pairs are requested before the weights
+  // j, j + 16, ...; every head's (max, sum) pairs are requested before the weights, in straight
+  // code (a load in a loop would make the wait for them cover the weights as well)
   constexpr int CPL = kAttnMaxChunks / 16;
-  constexpr uint32_t HPP = kWgThreads / 16;  // heads per pass
+  static_assert(kWgThreads / 16 == kAttnMaxHeads, "one DPP row per head");
   const uint32_t sub = lane & 15;
+  const uint32_t h = tid / 16;  // rows past the last head work on a clamped copy, write nothing
   float mv[CPL], lv[CPL];
-  auto load_ml = [&](uint32_t h) {
+  {
     const uint32_t hc = min(h, hq - 1);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -146,10 +148,9 @@ __device__ __forceinline__ void attn_combine(const GemvArgs& a, uint32_t n_items
       mv[j] = ml[(static_cast<size_t>(hc) * nc + i) * 2];
       lv[j] = ml[(static_cast<size_t>(hc) * nc + i) * 2 + 1];
     }
-  };
-  load_ml(tid / 16);
+  }
   issue_weights();
-  for (uint32_t h = tid / 16;;) {  // the 16 lanes of a row share h, so the row shuffles are whole
+  {
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < CPL; ++j)
@@ -168,15 +169,12 @@ __device__ __forceinline__ void attn_combine(const GemvArgs& a, uint32_t n_items
         if (i < n_items) msh[h * n_items + i] = mv[j] != -INFINITY ? expf(mv[j] - mx) * inv : 0.f;
       }
     }
-    h += HPP;
-    if (h >= hq) break;
-    load_ml(h);
   }
   __syncthreads();
   float4 acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) acc[p] = f4zero();
-  for (uint32_t i0 = 0;;) {
+  auto accumulate = [&](uint32_t i0) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const uint32_t c4 = min(static_cast<uint32_t>(tid + p * kWgThreads), static_cast<uint32_t>(K4 - 1));
@@ -188,9 +186,11 @@ __device__ __forceinline__ void attn_combine(const GemvArgs& a, uint32_t n_items
         acc[p].z = fmaf(w, o[p][i].z, acc[p].z); acc[p].w = fmaf(w, o[p][i].w, acc[p].w);
       }
     }
-    i0 += IB;
-    if (i0 >= n_items) break;
+  };
+  accumulate(0);  // the first batch outside the loop: its wait does not cover the weights
+  for (uint32_t i0 = IB; i0 < n_items; i0 += IB) {
     load_batch(i0);  // more than IB chunks: these wait behind the weights
+    accumulate(i0);
   }
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
@@ -239,7 +239,10 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
   // neighbouring rows, which the DRAM pages serve better than far-apart contiguous ranges.
   const uint32_t n_tiles = (a.n_rows + RH - 1) / RH;
   const uint32_t ts = gridDim.x * (blockDim.x / kWave);
-  uint32_t t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  // wave-uniform, and known to be: the row and segment arithmetic stays scalar, so the weight
+  // pointer is never fetched by a vector load (whose wait would also cover every tile in flight)
+  uint32_t t = blockIdx.x * (blockDim.x / kWave) +
+               __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t t_end = n_tiles;
 
   // Two of the wave's tiles of weight rows in flight: the one after next is requested as soon as a
@@ -456,29 +459,43 @@ __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Split-k GEMV for one stream with the (LayerScale) residual epilogue, for wide rows (k = 1024*KW;
-// the FFN down projection, [talker] build_step_plan; [mimi] MV_LS).  The workgroup's four waves
-// take the four quarters of each of its RB rows, so a wave keeps only its quarter of the input in
-// registers and the rows of all workgroups are in flight at once; the quarter sums meet in LDS.
-// Row slot rr of workgroup b is row b + rr * G (G workgroups): at any moment the device streams a
-// dense band of whole rows.
+// Split-k GEMV for one stream (k = 1024*KW), with the norm prologues and every epilogue of the
+// register GEMV ([talker] build_step_plan; [mimi] MV_LS).  The workgroup's four waves take the
+// four quarters of each of its RB rows, so a wave keeps only its quarter of the (normalised) input
+// in registers and the rows of all workgroups are in flight at once; the quarter sums, and the
+// norm statistics, meet in LDS.  Row slot rr of workgroup b is unit b + (rr mod U) * G (G
+// workgroups; a unit is a row, or for SwiGLU a gate row and its up row, U units per workgroup):
+// at any moment the device streams a dense band of whole rows.
 // ------------------------------------------------------------------------------------------------
-template <int KW, int RB>
+template <int KW, int RB, int PRO, int EPI>
 __global__ __launch_bounds__(kWgThreads) void k_gemv_ks(GemvArgs a) {
   constexpr int NW = kWgThreads / kWave;
-  static_assert(NW == 4 && RB <= kWave, "four quarter-row waves");
+  constexpr int U = EPI == EPI_SWIGLU ? RB / 2 : RB;
+  static_assert(NW == 4 && RB <= kWave && (EPI != EPI_SWIGLU || RB % 2 == 0), "tile shape");
   __shared__ float part[NW][RB];
+  __shared__ float stat[2][NW];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const uint32_t n = a.n_rows, G = gridDim.x, k4 = a.k >> 2;
+  const uint32_t n = a.n_rows, G = gridDim.x;
   const uint32_t off = static_cast<uint32_t>(wave) * (KW * kWave) + lane;  // float4 in the row
   const float4* x4 = reinterpret_cast<const float4*>(a.x);
-  float4 xr[KW];
+  float4 xr[KW], gr[PRO == PRO_NONE ? 1 : KW], br[PRO == PRO_LN ? KW : 1];
 #pragma unroll
   for (int j = 0; j < KW; ++j) xr[j] = x4[off + kWave * j];
+  if (PRO != PRO_NONE) {
+#pragma unroll
+    for (int j = 0; j < KW; ++j) gr[j] = reinterpret_cast<const float4*>(a.norm_w)[off + kWave * j];
+  }
+  if (PRO == PRO_LN) {
+#pragma unroll
+    for (int j = 0; j < KW; ++j) br[j] = reinterpret_cast<const float4*>(a.norm_b)[off + kWave * j];
+  }
   float4 w[RB][KW];
-  auto row_base = [&](uint32_t row) {
+  auto row_base = [&](uint32_t u, int rr) {
     const float* base = a.w[0];
-    if (row >= a.seg_end[1]) {
+    uint32_t row = u;
+    if (EPI == EPI_SWIGLU) {
+      base = rr < U ? a.w[0] : a.w[1];
+    } else if (row >= a.seg_end[1]) {
       base = a.w[2];
       row -= a.seg_end[1];
     } else if (row >= a.seg_end[0]) {
@@ -487,23 +504,65 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_ks(GemvArgs a) {
     }
     return reinterpret_cast<const float4*>(base + static_cast<size_t>(row) * a.k) + off;
   };
-  // every thread requests the old residual and LayerScale of row slot tid % RB (unconditional
-  // loads: threads past RB fetch duplicates that are never used)
+  // every thread requests the old residual and LayerScale of unit slot tid % U (unconditional
+  // loads: threads past U fetch duplicates that are never used)
   float res_old = 0.f, ls_v = 1.f;
-  auto load = [&](uint32_t r0) {
+  auto load = [&](uint32_t u0) {
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
-      const float4* wr = row_base(min(r0 + rr * G, n - 1));
+      const float4* wr = row_base(min(u0 + (rr % U) * G, n - 1), rr);
 #pragma unroll
       for (int j = 0; j < KW; ++j) w[rr][j] = ldw(wr + kWave * j);
     }
-    const uint32_t row = min(r0 + (tid % RB) * G, n - 1);
-    res_old = (a.res_in ? a.res_in : a.res)[row];
-    if (a.ls) ls_v = a.ls[row];
+    if (EPI == EPI_RESIDUAL) {
+      const uint32_t u = min(u0 + (tid % U) * G, n - 1);
+      res_old = (a.res_in ? a.res_in : a.res)[u];
+      if (a.ls) ls_v = a.ls[u];
+    }
   };
-  asm volatile("" ::: "memory");  // the input quarter is requested before the rows
-  uint32_t r0 = blockIdx.x;
-  load(r0);
+  asm volatile("" ::: "memory");  // the input quarter (and gains) are requested before the rows
+  uint32_t u0 = blockIdx.x;
+  load(u0);
+
+  if (PRO != PRO_NONE) {  // the norm statistics of the whole row, from the four quarters
+    const float kf = static_cast<float>(a.k);
+    float mean = 0.f;
+    if (PRO == PRO_LN) {
+      float sm = 0.f;
+#pragma unroll
+      for (int j = 0; j < KW; ++j) sm += (xr[j].x + xr[j].y) + (xr[j].z + xr[j].w);
+      sm = wave_sum(sm);
+      if (lane == 0) stat[0][wave] = sm;
+      __syncthreads();
+      mean = ((stat[0][0] + stat[0][1]) + (stat[0][2] + stat[0][3])) / kf;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      float4 d = xr[j];
+      d.x -= mean; d.y -= mean; d.z -= mean; d.w -= mean;
+      ss = dot4(d, d, ss);
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) stat[1][wave] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf(((stat[1][0] + stat[1][1]) + (stat[1][2] + stat[1][3])) / kf + a.eps);
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      float4 v = xr[j];
+      const float4 g = gr[j];
+      if (PRO == PRO_RMS) {
+        v.x = (v.x * inv) * g.x; v.y = (v.y * inv) * g.y;
+        v.z = (v.z * inv) * g.z; v.w = (v.w * inv) * g.w;
+      } else {
+        const float4 b = br[j];
+        v.x = ((v.x - mean) * inv) * g.x + b.x; v.y = ((v.y - mean) * inv) * g.y + b.y;
+        v.z = ((v.z - mean) * inv) * g.z + b.z; v.w = ((v.w - mean) * inv) * g.w + b.w;
+      }
+      xr[j] = v;
+    }
+  }
+
   for (;;) {
     float acc[RB];
 #pragma unroll
@@ -515,19 +574,28 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_ks(GemvArgs a) {
     ReduceScatter<RB, 32>::run(acc, lane);  // lane (64/RB)*rr holds row slot rr's quarter sum
     if (lane % (kWave / RB) == 0) part[wave][lane / (kWave / RB)] = acc[0];
     __syncthreads();
-    const uint32_t base = r0;
+    const uint32_t base = u0;
     const float res_here = res_old, ls_here = ls_v;
-    r0 += G * RB;
-    if (r0 < n) load(r0);  // the next rows stream while this tile's results are written
-    if (tid < RB) {
-      const uint32_t row = base + tid * G;
-      if (row < n) {
+    u0 += G * U;
+    if (u0 < n) load(u0);  // the next rows stream while this tile's results are written
+    if (tid < U) {
+      const uint32_t u = base + tid * G;
+      if (u < n) {
         const float v = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
-        if (a.tap) a.tap[row] = v;
-        a.res[row] = res_here + (a.ls ? ls_here * v : v);
+        if (EPI == EPI_SWIGLU) {
+          const float up = (part[0][tid + U] + part[1][tid + U]) + (part[2][tid + U] + part[3][tid + U]);
+          a.y[u] = silu(v) * up;
+        } else if (EPI == EPI_STORE) {
+          a.y[u] = v;
+        } else if (EPI == EPI_GELU) {
+          a.y[u] = gelu_erf(v);
+        } else {
+          if (a.tap) a.tap[u] = v;
+          a.res[u] = res_here + (a.ls ? ls_here * v : v);
+        }
       }
     }
-    if (r0 >= n) return;
+    if (u0 >= n) return;
     __syncthreads();  // part is rewritten by the next tile
   }
 }
@@ -705,6 +773,24 @@ GemvKernel gemv_rx_attn(int kb) {
   return {nullptr, 0};
 }
 
+// The split-k kernels: k = 1024*ks, rows_per_wave = rows per workgroup tile.
+template <int KW, int RB>
+GemvKernel gemv_ks_kind(const GemvLaunch& l) {
+#define SDEC_KS(P, E) \
+  if (l.prologue == P && l.epilogue == E) return {reinterpret_cast<const void*>(&k_gemv_ks<KW, RB, P, E>), 0};
+  SDEC_KS(PRO_NONE, EPI_RESIDUAL)
+  SDEC_KS(PRO_RMS, EPI_STORE)
+  SDEC_KS(PRO_RMS, EPI_SWIGLU)
+#undef SDEC_KS
+  return {nullptr, 0};
+}
+GemvKernel gemv_ks(const GemvLaunch& l) {
+  if (l.ks == 6 && l.rows_per_wave == 4) return gemv_ks_kind<6, 4>(l);
+  if (l.ks == 2 && l.rows_per_wave == 4) return gemv_ks_kind<2, 4>(l);
+  if (l.ks == 2 && l.rows_per_wave == 8) return gemv_ks_kind<2, 8>(l);
+  return {nullptr, 0};
+}
+
 template <int M>
 GemvKernel gemv_pick_m(const GemvLaunch& l, uint32_t k) {
   if (l.prologue == PRO_ATTN) {
@@ -720,12 +806,7 @@ GemvKernel gemv_pick_m(const GemvLaunch& l, uint32_t k) {
     return {nullptr, 0};
   }
   if constexpr (M == 1) {
-    if (l.ks > 0) {
-      if (l.prologue != PRO_NONE || l.epilogue != EPI_RESIDUAL || l.rows_per_wave != 4)
-        return {nullptr, 0};
-      if (l.ks == 6) return {reinterpret_cast<const void*>(&k_gemv_ks<6, 4>), 0};
-      return {nullptr, 0};
-    }
+    if (l.ks > 0) return gemv_ks(l);
   }
 #define SDEC_KIND(P, E) \
   if (l.prologue == P && l.epilogue == E) return gemv_pick_r<M, P, E>(l, k);

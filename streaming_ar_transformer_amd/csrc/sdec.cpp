@@ -474,7 +474,7 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
     return A.code;
   }
 
-  if (c.m == 1 && static_cast<size_t>(hq) * h->n_chunks <= kAttnMaxPartials) {
+  if (c.m == 1 && hq <= kAttnMaxHeads && static_cast<size_t>(hq) * h->n_chunks <= kAttnMaxPartials) {
     const GemvLaunch fused = plan_gemv(PRO_ATTN, EPI_RESIDUAL, c.d_model, qw, c.m);
     const char* fe = std::getenv("SDEC_ATTN_COMBINE_IN_O");  // tuning override: "0" = combine in attention
     h->attn_fused = gemv_supported(fused, qw, c.m) && !(fe != nullptr && fe[0] == '0');
