@@ -61,6 +61,7 @@ struct GemvLaunch {
   int rows_per_wave;  // R: rows one wave reduces together
   int kb;             // >0: k == 256*kb and the input rows live in registers; 0: generic k
   int ks;             // >0: split-k kernel, k == 1024*ks (each wave takes a quarter of each row)
+  int stream;         // 1: row-stream kernel (one row per wave in flight), k == 256*kb
   int waves_per_wg;
   uint32_t grid;      // workgroups; each wave owns a contiguous, balanced range of row tiles
 };
