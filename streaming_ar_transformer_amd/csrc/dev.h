@@ -391,6 +391,9 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   }
   const int kt = tid % (2 * HD);  // raw key element kt, or value element kt - HD
   const float kvraw = qkv[(kt < HD ? hq + kvh : hq + hkv + kvh) * HD + kt % HD];
+  // keep the compiler from sinking these loads below the early exit, which waits for the count
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   const uint32_t n_items = (nl + a.chunk - 1) / a.chunk;
   if (chunk >= n_items) return;  // no legal slot falls in this item
   const uint32_t total = min(a.chunk, nl - c0);
@@ -410,11 +413,14 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   const float* vb = a.v_ring + static_cast<size_t>(s) * a.ring_stream_stride + kvh * HD + 8 * sub;
   float4 kk[UNR][2], vv[UNR][2];
   auto load_pass = [&](uint32_t i0) {
+    uint32_t slots[UNR];  // every slot index of the pass read from LDS before any load waits
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) slots[u] = list[min(i0 + u * NG, total - 1)];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const uint32_t i = i0 + u * NG;
       if (i < total && !(lead && i == 0)) {
-        const size_t sl = list[i];
+        const size_t sl = slots[u];
         const float4* kp = reinterpret_cast<const float4*>(kb + sl * row);
         const float4* vp = reinterpret_cast<const float4*>(vb + sl * row);
         kk[u][0] = kp[0]; kk[u][1] = kp[1];
