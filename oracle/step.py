@@ -238,6 +238,79 @@ class OracleDecoder:
         if self.unbounded and pos >= self.R:
             raise ValueError(f"position {pos} exceeds the {self.R}-slot ring")
 
+    def prefill(self, xs: np.ndarray, pos: int, first: bool = False):
+        """A block of ``t`` consecutive positions ``pos .. pos+t-1`` of the single stream in one
+        pass; returns every row's output ``[t, d]``.
+
+        [talker] ``TalkerGpu::prefill`` -> ``forward_rows``: the block's rows go through each
+        GEMV together, all of the block's K/V rows are appended to the cache before attention,
+        and row ``r`` (absolute position ``pos + r``) attends causally: to the cache and to the
+        block's rows up to itself.  With a ring this is the legal set at ``pos + r``, provided
+        no append evicts a position an earlier row of the block still attends: required here as
+        ``pos + t <= R`` (no append evicts anything, the talker's case) or ``R >= W + t - 1``.
+        [pocket] ``PocketBackboneGpu``'s doc states the property this must have: feeding the
+        block one position at a time gives the same hidden states."""
+        cfg = self.cfg
+        if cfg.m != 1:
+            raise ValueError("prefill runs on a single-stream stack")
+        pos = int(pos)
+        xs = np.array(xs, dtype=F32).reshape(-1, cfg.d_model)
+        t = xs.shape[0]
+        if t < 1:
+            raise ValueError("empty block")
+        if pos + t > self.R and self.R < self.W + t - 1:
+            raise ValueError(f"a {t}-row block past the first ring turn needs ring >= window + "
+                             f"{t - 1}")
+        self._check(pos, first)
+        if self.unbounded and pos + t - 1 >= self.R:
+            raise ValueError(f"position {pos + t - 1} exceeds the {self.R}-slot ring")
+        if first:
+            self.P[:] = INVALID_POS
+        positions = pos + np.arange(t)
+        slots = positions % self.R
+        self.P[0, slots] = positions.astype(np.uint32)
+        hq, hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+        tables = [rope_cos_sin(int(p), hd, cfg.rope_theta) for p in positions]
+
+        def norm(v, w, b):
+            if cfg.norm == NORM_RMS:
+                return rms_norm(v, w, cfg.norm_eps)
+            return layer_norm(v, w, b, cfg.norm_eps)
+
+        def rope_rows(v):  # v [t, heads, hd]: row r rotated by position pos + r
+            return np.stack([apply_rope(v[r], tables[r][0], tables[r][1], cfg.rope)
+                             for r in range(t)])
+
+        x = xs
+        for l, lw in enumerate(self.layers):
+            n = norm(x, lw["attn_norm_w"], lw.get("attn_norm_b"))
+            q = gemv(lw["wq"], n).reshape(t, hq, hd)
+            k = gemv(lw["wk"], n).reshape(t, hkv, hd)
+            v = gemv(lw["wv"], n).reshape(t, hkv, hd)
+            if cfg.qk_norm:
+                q = rms_norm(q, lw["q_norm"], cfg.qk_norm_eps)
+                k = rms_norm(k, lw["k_norm"], cfg.qk_norm_eps)
+            q, k = rope_rows(q), rope_rows(k)
+            self.K[0, l, slots] = k  # the whole block is appended before any row attends
+            self.V[0, l, slots] = v
+            o = np.stack([
+                attend(q[r], self.K[0, l], self.V[0, l], self.P[0], int(positions[r]), self.W,
+                       hkv, normalize_weights_first=(cfg.family == "T"))
+                for r in range(t)]).reshape(t, hq * hd)
+            a_proj = gemv(lw["wo"], o)
+            x = x + (lw["ls1"] * a_proj if cfg.layer_scale else a_proj)
+            n = norm(x, lw["ffn_norm_w"], lw.get("ffn_norm_b"))
+            if cfg.ffn == FFN_SWIGLU:
+                act = silu_mul(gemv(lw["w_gate"], n), gemv(lw["w_up"], n))
+            else:
+                act = gelu_erf(gemv(lw["w_up"], n))
+            f_proj = gemv(lw["w_down"], act)
+            x = x + (lw["ls2"] * f_proj if cfg.layer_scale else f_proj)
+        if cfg.final_norm:
+            x = norm(x, self.final["norm_w"], self.final.get("norm_b"))
+        self.next_pos = pos + t
+        return x
+
     def step(self, x: np.ndarray, pos: int, first: bool = False, taps: dict | None = None):
         """Advance every stream by one position; returns the output rows ``[m, d]``.
 

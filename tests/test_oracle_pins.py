@@ -308,6 +308,66 @@ def test_step_matches_brute_force(family, kw):
         np.testing.assert_allclose(y[0], ref, rtol=2e-5, atol=2e-5, err_msg=f"pos {p}")
 
 
+@pytest.mark.parametrize("family,kw,blocks", [
+    ("T", {}, [5, 1, 3, 3]),
+    ("C", dict(ring=7, window=4), [4, 2, 4, 1, 3, 4, 2]),  # wraps the 7-slot ring several times
+])
+def test_prefill_blocks_match_brute_force(family, kw, blocks):
+    # A block of t positions in one pass ([talker] forward_rows: append the block's K/V, then
+    # causal attention) equals the float64 brute force fed one position at a time.
+    cfg = tiny(family, **kw)
+    layers, final = wl.make_weights(cfg)
+    xs = wl.make_inputs(cfg, sum(blocks))
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    bru = BruteDecoder(cfg, layers, final, cfg.window)
+    p = 0
+    for t in blocks:
+        y = orc.prefill(xs[p:p + t, 0], p, first=(p == 0))
+        assert y.shape == (t, cfg.d_model)
+        for r in range(t):
+            ref = np.array(bru.step(xs[p + r, 0], p + r))
+            np.testing.assert_allclose(y[r], ref, rtol=2e-5, atol=2e-5, err_msg=f"pos {p + r}")
+        p += t
+    assert orc.next_pos == p
+
+
+def test_prefill_equals_single_steps_and_keeps_the_ring():
+    # Chunk invariance ([pocket] PocketBackboneGpu doc): blocks and single steps give the same
+    # outputs and leave the same rings, and a decode continues from a prefilled ring.
+    cfg = tiny("C", ring=9, window=6)
+    layers, final = wl.make_weights(cfg)
+    xs = wl.make_inputs(cfg, 30)
+    a = oracle.OracleDecoder(cfg, layers, final)
+    b = oracle.OracleDecoder(cfg, layers, final)
+    p = 0
+    for t in (4, 4, 1, 3, 4, 2):
+        ya = a.prefill(xs[p:p + t, 0], p, first=(p == 0))
+        yb = np.concatenate([b.step(xs[p + r], p + r, first=(p + r == 0)) for r in range(t)])
+        np.testing.assert_allclose(ya, yb, rtol=1e-5, atol=1e-6)
+        p += t
+    np.testing.assert_array_equal(a.P, b.P)
+    np.testing.assert_allclose(a.K, b.K, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(a.V, b.V, rtol=1e-5, atol=1e-6)
+    for q in range(p, 30):
+        np.testing.assert_allclose(a.step(xs[q], q), b.step(xs[q], q), rtol=1e-5, atol=1e-6)
+
+
+def test_prefill_argument_errors():
+    cfg = tiny("C", ring=5, window=4)
+    layers, final = wl.make_weights(cfg)
+    xs = wl.make_inputs(cfg, 8)
+    d = oracle.OracleDecoder(cfg, layers, final)
+    d.prefill(xs[:3, 0], 0, first=True)  # inside the first ring turn nothing is evicted
+    with pytest.raises(ValueError, match="window"):
+        d.prefill(xs[3:6, 0], 3)  # position 5 evicts 0, which row 3 (pos 3, window 4) attends
+    d.prefill(xs[3:5, 0], 3)       # 5 slots >= window 4 + 1
+    with pytest.raises(ValueError, match="contiguous"):
+        d.prefill(xs[5:7, 0], 6)
+    multi = oracle.OracleDecoder(tiny("C", m=2), *wl.make_weights(tiny("C", m=2)))
+    with pytest.raises(ValueError, match="single-stream"):
+        multi.prefill(xs[:1, 0], 0, first=True)
+
+
 def test_ring_bookkeeping_closed_form():
     # After step p of a stream that started at p0: P[s] = max{p' <= p : p' = s mod R, p' >= p0}.
     cfg = tiny("C", ring=5, window=4)
