@@ -71,6 +71,9 @@ typedef struct sdec_config {
   uint32_t unbounded;   /* nonzero: the stack refuses pos >= ring_slots instead of wrapping
                            (the talker's cache and the FlowLM ring); requires window == ring */
   uint32_t flags;       /* SDEC_FLAG_* */
+  uint32_t max_prefill; /* positions one sdec_prefill call may carry: 0 or 1 = none beyond a
+                           single step, at most 8; above 1 the stack must have m == 1
+                           ([talker] TalkerGpu::load: max_m bounds the prefill block width) */
 } sdec_config;
 
 /* One layer's parameters: device pointers, float32, borrowed (the caller keeps them alive and
@@ -121,6 +124,17 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
  * `stream` and returns; x must stay valid until the work completes. */
 int sdec_step(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stream);
 
+/* Cached prefill of a block of t consecutive positions pos .. pos+t-1 of a single-stream stack
+ * ([talker] TalkerGpu::prefill and forward_rows: the block's K/V rows are appended to the cache,
+ * every row attends causally to the cache and to the earlier rows of the block, and every row's
+ * output is returned).  x: device [t][d_model] float32 input rows, overwritten with the t output
+ * rows.  The result equals t sdec_step calls at pos, pos+1, ... (first applies to the first of
+ * them).  Requires m == 1 and 1 <= t <= max_prefill (SDEC_E_ARG); that no row's push evicts a
+ * position an earlier row of the block attends: pos + t <= ring_slots (nothing is evicted) or
+ * ring_slots >= window + t - 1; and for an unbounded stack pos + t <= ring_slots
+ * (SDEC_E_CAPACITY).  Launches kernels one by one (no
+ * graph); asynchronous on `stream`.  Taps are not written. */
+int sdec_prefill(sdec_handle* h, float* x, uint32_t pos, uint32_t t, uint32_t first, void* stream);
 /* Fresh session on `stream`: zero the K/V rings, set every position-ring slot to empty and
  * forget the next position ([mimi] MimiGpu::reset; [pocket] PocketCodecGpu::reset). */
 int sdec_reset(sdec_handle* h, void* stream);

@@ -373,6 +373,7 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   const uint32_t hq = a.n_q_heads, hkv = a.n_kv_heads;
   const uint32_t h0 = kvh * G;
   const float* qkv = a.qkv + static_cast<size_t>(s) * a.qkv_stride;
+  const float* cs = a.cs ? a.cs + static_cast<size_t>(s) * a.cs_stride : nullptr;
 
   // 1. this item's share of the step's legal slots; this step's raw queries (and, for the item
   //    that pushes, the raw key and value).  All of them are requested together with the slot
@@ -440,7 +441,7 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   if (prep) {
     for (int g = wave; g < G; g += NWV) {
       float va = lane < HALF ? qs[g][ia] : 0.f, vb2 = lane < HALF ? qs[g][ib] : 0.f;
-      norm_rope_pair<HD>(va, vb2, lane, a.q_norm, a.eps, a.cs, a.rope_style);
+      norm_rope_pair<HD>(va, vb2, lane, a.q_norm, a.eps, cs, a.rope_style);
       if (lane < HALF) {
         qs[g][ia] = va;
         qs[g][ib] = vb2;
@@ -449,7 +450,7 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   }
   if (lead && wave == NWV - 1) {
     float va = lane < HALF ? sm.ks[ia] : 0.f, vb2 = lane < HALF ? sm.ks[ib] : 0.f;
-    norm_rope_pair<HD>(va, vb2, lane, a.k_norm, a.eps, a.cs, a.rope_style);
+    norm_rope_pair<HD>(va, vb2, lane, a.k_norm, a.eps, cs, a.rope_style);
     const uint32_t ps = a.st->slot;
     const size_t roff = static_cast<size_t>(s) * a.ring_stream_stride +
                         (static_cast<size_t>(ps) * hkv + kvh) * HD;

@@ -86,6 +86,7 @@ struct AttnArgs {
   float eps;
   int rope_style;        // 0 rotate_half, 1 interleaved
   const float* cs;       // [hd/2] cos then [hd/2] sin of this position; null: q used as given
+  uint32_t cs_stride;    // floats between the tables of consecutive streams (0: one shared table)
   int push;              // nonzero: push this step's k/v into the rings
   float* k_ring;         // stream 0 of this layer: [R][Hkv][hd]
   float* v_ring;
@@ -122,6 +123,29 @@ struct BeginArgs {
   DevState* st;
 };
 hipError_t launch_begin(const BeginArgs& a, hipStream_t s);
+// Multi-position begin ([talker] TalkerGpu::prefill / forward_rows): the m rows are positions
+// pos .. pos+m-1 of ONE stream whose position ring is pos_rings[0..R).  Stamps every row's slot
+// first, then forms row i's legal list (its own slot first) and its rope cos/sin (cs + i*head_dim).
+// Needs pos + m <= R or R >= window + m - 1, so no row's push overwrites a slot an earlier row
+// still attends.
+hipError_t launch_begin_rows(const BeginArgs& a, hipStream_t s);
+
+// Key/value push of m rows at positions pos .. pos+m-1 of one stream ([talker] forward_rows: the
+// block's K/V rows are appended before attention): per row and kv head, the raw key gets the
+// per-head RMSNorm (if any) and rope with that row's cos/sin, and key and value are written into
+// ring slot (pos + row) mod R.
+struct PushArgs {
+  const float* qkv;      // [m][qkv_stride] raw q, k, v
+  uint32_t qkv_stride;
+  const float* k_norm;   // [hd] or null
+  float eps;
+  int rope_style;
+  const float* cs;       // [m][hd]: cos then sin per row
+  float* k_ring;         // this layer's rings [R][Hkv][hd]
+  float* v_ring;
+  uint32_t m, n_q_heads, n_kv_heads, head_dim, ring, pos;
+};
+hipError_t launch_push(const PushArgs& a, hipStream_t s);
 
 struct EndArgs {
   const float* xres;     // [m][d]

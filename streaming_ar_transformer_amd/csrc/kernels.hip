@@ -763,6 +763,74 @@ __global__ __launch_bounds__(kWgThreads) void k_begin(BeginArgs a) {
   }
 }
 
+// Multi-position begin ([talker] TalkerGpu::prefill → forward_rows): the m rows are positions
+// pos .. pos+m-1 of one stream.  Every row's slot is stamped before any row's legal list is formed;
+// with pos + m <= R or R >= window + m - 1 no stamp removes a position an earlier row of the
+// block may attend, so row r's list is exactly the one a single step at pos + r would form.
+// One workgroup.
+__global__ __launch_bounds__(kWgThreads) void k_begin_rows(BeginArgs a) {
+  __shared__ uint32_t scan[kWgThreads];
+  const int tid = threadIdx.x;
+  const uint32_t rows = a.m;
+  const float4* src = reinterpret_cast<const float4*>(a.x_in);
+  float4* dst = reinterpret_cast<float4*>(a.xres);
+  for (uint32_t i = tid; i < rows * (a.d >> 2); i += kWgThreads) dst[i] = src[i];
+  uint32_t* P = a.pos_rings;
+  const uint32_t base_slot = a.pos % a.ring;
+  if (a.first) {
+    for (uint32_t j = tid; j < a.ring; j += kWgThreads) {
+      const uint32_t r = (j + a.ring - base_slot) % a.ring;  // the row whose slot j is, if any
+      P[j] = r < rows ? a.pos + r : kInvalidPos;
+    }
+  } else {
+    for (uint32_t r = tid; r < rows; r += kWgThreads) P[(base_slot + r) % a.ring] = a.pos + r;
+  }
+  __syncthreads();
+  for (uint32_t r = 0; r < rows; ++r) {
+    compact_legal<kWgThreads, false>(P, a.ring, a.pos + r, a.window,
+                                     static_cast<int>((base_slot + r) % a.ring),
+                                     a.legal + static_cast<size_t>(r) * a.ring, a.n_legal + r, scan);
+    __syncthreads();  // the scan buffer is reused by the next row
+  }
+  const uint32_t half = a.head_dim >> 1;
+  for (uint32_t i = tid; i < rows * half; i += kWgThreads) {
+    const uint32_t r = i / half, j = i % half;
+    const double inv_freq = pow(a.theta, -2.0 * static_cast<double>(j) /
+                                             static_cast<double>(a.head_dim));
+    const double ang = static_cast<double>(a.pos + r) * inv_freq;
+    a.cs[static_cast<size_t>(r) * a.head_dim + j] = static_cast<float>(cos(ang));
+    a.cs[static_cast<size_t>(r) * a.head_dim + half + j] = static_cast<float>(sin(ang));
+  }
+  if (tid == 0 && a.st != nullptr) {
+    a.st->pos = a.pos + rows - 1;
+    a.st->slot = (base_slot + rows - 1) % a.ring;
+  }
+}
+
+// Key/value push of a block of rows: one wave per (row, kv head); lane j owns rope pair j, as in
+// the attention item that pushes a single step's key ([talker] QK_NORM_SRC, ROPE_SRC, append).
+template <int HD>
+__global__ __launch_bounds__(kWave) void k_push(PushArgs a) {
+  constexpr int HALF = HD / 2;
+  const uint32_t r = blockIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x;
+  const float* row = a.qkv + static_cast<size_t>(r) * a.qkv_stride;
+  const float* k = row + static_cast<size_t>(a.n_q_heads + g) * HD;
+  const float* v = row + static_cast<size_t>(a.n_q_heads + a.n_kv_heads + g) * HD;
+  const int ia = a.rope_style == 0 ? lane : 2 * lane;
+  const int ib = a.rope_style == 0 ? lane + HALF : 2 * lane + 1;
+  float va = lane < HALF ? k[ia] : 0.f, vb = lane < HALF ? k[ib] : 0.f;
+  norm_rope_pair<HD>(va, vb, lane, a.k_norm, a.eps, a.cs + static_cast<size_t>(r) * HD,
+                     a.rope_style);
+  const uint32_t slot = (a.pos % a.ring + r) % a.ring;
+  const size_t roff = (static_cast<size_t>(slot) * a.n_kv_heads + g) * HD;
+  if (lane < HALF) {
+    a.k_ring[roff + ia] = va;
+    a.k_ring[roff + ib] = vb;
+  }
+  for (int d = lane; d < HD; d += kWave) a.v_ring[roff + d] = v[d];
+}
+
 // The legal-slot lists of m streams (one workgroup per stream) for the one-shot attention call.
 __global__ __launch_bounds__(kWgThreads) void k_compact_legal(const uint32_t* pos_rings,
                                                               uint32_t ring, uint32_t pos,
@@ -1123,6 +1191,22 @@ hipError_t launch_begin(const BeginArgs& a, hipStream_t s) {
   BeginArgs args = a;
   void* params[] = {&args};
   return launch_timed(reinterpret_cast<const void*>(&k_begin), dim3(a.m), dim3(kWgThreads), params, 0, s);
+}
+
+hipError_t launch_begin_rows(const BeginArgs& a, hipStream_t s) {
+  BeginArgs args = a;
+  void* params[] = {&args};
+  return launch_timed(reinterpret_cast<const void*>(&k_begin_rows), dim3(1), dim3(kWgThreads), params, 0, s);
+}
+
+hipError_t launch_push(const PushArgs& a, hipStream_t s) {
+  const void* fn = a.head_dim == 128 ? reinterpret_cast<const void*>(&k_push<128>)
+                   : a.head_dim == 64 ? reinterpret_cast<const void*>(&k_push<64>)
+                                      : nullptr;
+  if (fn == nullptr || a.m == 0 || a.n_kv_heads == 0) return hipErrorInvalidValue;
+  PushArgs args = a;
+  void* params[] = {&args};
+  return launch_timed(fn, dim3(a.m, a.n_kv_heads), dim3(kWave), params, 0, s);
 }
 
 hipError_t launch_compact_legal(const uint32_t* pos_rings, uint32_t m, uint32_t ring, uint32_t pos,

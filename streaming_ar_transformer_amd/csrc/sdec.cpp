@@ -47,6 +47,7 @@ struct sdec_handle {
   std::vector<sdec_layer_weights> layers;
   sdec_final_weights fin{};
   uint32_t ring = 0;
+  uint32_t rows = 0;          // scratch rows: max(m, max_prefill)
   uint32_t n_chunks = 0;
   uint32_t chunk = 0;
   int device = 0;
@@ -135,6 +136,10 @@ int validate_config(const sdec_config* c, uint32_t ring) {
   if (group != 1 && group != 2 && group != 4)
     return fail(SDEC_E_ARG, "GQA group %u unsupported (1, 2 or 4)", group);
   if (c->m < 1 || c->m > kMaxM) return fail(SDEC_E_ARG, "m must be in [1, %d]", kMaxM);
+  if (c->max_prefill > static_cast<uint32_t>(kMaxM))
+    return fail(SDEC_E_ARG, "max_prefill must be in [0, %d]", kMaxM);
+  if (c->max_prefill > 1 && c->m != 1)
+    return fail(SDEC_E_ARG, "a stack with max_prefill > 1 must have one stream (m == 1)");
   if (c->norm > SDEC_NORM_LAYER) return fail(SDEC_E_ARG, "bad norm kind");
   if (c->rope > SDEC_ROPE_INTERLEAVED) return fail(SDEC_E_ARG, "bad rope kind");
   if (c->ffn > SDEC_FFN_GELU_ERF) return fail(SDEC_E_ARG, "bad ffn kind");
@@ -144,9 +149,10 @@ int validate_config(const sdec_config* c, uint32_t ring) {
     return fail(SDEC_E_ARG, "window %u must be in [1, ring_slots=%u]", c->window, ring);
   if (c->unbounded && c->window != ring)
     return fail(SDEC_E_ARG, "an unbounded stack needs window == ring_slots");
-  const uint32_t mp = c->m <= 1 ? 1 : c->m <= 2 ? 2 : c->m <= 4 ? 4 : 8;
+  const uint32_t rows = c->m > c->max_prefill ? c->m : c->max_prefill;
+  const uint32_t mp = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : 8;
   if (static_cast<uint64_t>(mp) * c->d_model * sizeof(float) > 65536)
-    return fail(SDEC_E_ARG, "m=%u rows of d_model=%u exceed the 64 KiB staging tile", c->m,
+    return fail(SDEC_E_ARG, "%u rows of d_model=%u exceed the 64 KiB staging tile", rows,
                 c->d_model);
   return SDEC_OK;
 }
@@ -333,13 +339,96 @@ int enqueue_end(sdec_handle* h, float* x, hipStream_t s, Hooks* hk) {
   return SDEC_OK;
 }
 
+// A prefill block of t rows at positions pos .. pos+t-1 of stream 0 ([talker] TalkerGpu::prefill
+// → forward_rows): the rows share stream 0's rings, every row's K/V is pushed before attention,
+// and the attention launch treats the rows as t streams with their own legal lists and rope
+// tables over one ring.
+int enqueue_prefill(sdec_handle* h, float* x, uint32_t pos, uint32_t t, uint32_t first,
+                    hipStream_t s, Hooks* hk) {
+  const sdec_config& c = h->cfg;
+  const uint32_t hd = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads;
+  const uint32_t qw = hq * hd, kw = hkv * hd, nqkv = qw + 2 * kw;
+  const int pro = c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN;
+  BeginArgs b{};
+  b.x_in = x; b.xres = h->xres; b.d = c.d_model; b.pos_rings = h->pos_rings;
+  b.legal = h->legal; b.n_legal = h->n_legal;
+  b.m = t; b.ring = h->ring; b.window = c.window; b.pos = pos; b.first = first ? 1u : 0u;
+  b.cs = h->cs; b.head_dim = hd; b.theta = c.rope_theta; b.st = h->st;
+  LAUNCH(hk, s, SDEC_K_BEGIN, launch_begin_rows(b, s));
+  const GemvLaunch p_qkv = plan_gemv(pro, EPI_STORE, nqkv, c.d_model, t);
+  const GemvLaunch p_o = plan_gemv(PRO_NONE, EPI_RESIDUAL, c.d_model, qw, t);
+  const GemvLaunch p_up = plan_gemv(pro, c.ffn == SDEC_FFN_SWIGLU ? EPI_SWIGLU : EPI_GELU, c.d_ff,
+                                    c.d_model, t);
+  const GemvLaunch p_down = plan_gemv(PRO_NONE, EPI_RESIDUAL, c.d_model, c.d_ff, t);
+  for (uint32_t l = 0; l < c.n_layers; ++l) {
+    const sdec_layer_weights& w = h->layers[l];
+    GemvArgs g{};
+    g.w[0] = w.wq; g.w[1] = w.wk; g.w[2] = w.wv;
+    g.seg_end[0] = qw; g.seg_end[1] = qw + kw; g.seg_end[2] = nqkv;
+    g.n_rows = nqkv; g.k = c.d_model; g.m = t;
+    g.x = h->xres; g.x_stride = c.d_model;
+    g.norm_w = w.attn_norm_w; g.norm_b = w.attn_norm_b; g.eps = c.norm_eps;
+    g.y = h->qkv; g.y_stride = nqkv;
+    LAUNCH(hk, s, SDEC_K_QKV, launch_gemv(g, p_qkv, s));
+    PushArgs pa{};
+    pa.qkv = h->qkv; pa.qkv_stride = nqkv;
+    pa.k_norm = c.qk_norm ? w.k_norm : nullptr; pa.eps = c.qk_norm_eps;
+    pa.rope_style = c.rope == SDEC_ROPE_HALF ? 0 : 1; pa.cs = h->cs;
+    pa.k_ring = ring_at(h, h->k_rings, 0, l); pa.v_ring = ring_at(h, h->v_rings, 0, l);
+    pa.m = t; pa.n_q_heads = hq; pa.n_kv_heads = hkv; pa.head_dim = hd; pa.ring = h->ring;
+    pa.pos = pos;
+    LAUNCH(hk, s, SDEC_K_ATTENTION, launch_push(pa, s));
+    AttnArgs aa{};
+    aa.qkv = h->qkv; aa.qkv_stride = nqkv;
+    aa.q_norm = c.qk_norm ? w.q_norm : nullptr; aa.k_norm = nullptr;
+    aa.eps = c.qk_norm_eps; aa.rope_style = pa.rope_style; aa.cs = h->cs; aa.cs_stride = hd;
+    aa.push = 0;
+    aa.k_ring = pa.k_ring; aa.v_ring = pa.v_ring;
+    aa.ring_stream_stride = 0;  // every row reads stream 0's rings
+    aa.legal = h->legal; aa.n_legal = h->n_legal;
+    aa.out = h->attn_out; aa.part = h->part; aa.counters = h->counters;
+    aa.m = t; aa.n_q_heads = hq; aa.n_kv_heads = hkv; aa.head_dim = hd; aa.ring = h->ring;
+    aa.chunk = h->chunk; aa.n_chunks = h->n_chunks; aa.st = nullptr; aa.partials_only = 0;
+    LAUNCH(hk, s, SDEC_K_ATTENTION, launch_attention(aa, s));
+    GemvArgs o{};
+    o.w[0] = o.w[1] = o.w[2] = w.wo;
+    o.seg_end[0] = o.seg_end[1] = o.seg_end[2] = c.d_model;
+    o.n_rows = c.d_model; o.k = qw; o.m = t; o.x = h->attn_out; o.x_stride = qw;
+    o.res = h->xres; o.res_stride = c.d_model; o.ls = c.layer_scale ? w.ls1 : nullptr;
+    LAUNCH(hk, s, SDEC_K_O, launch_gemv(o, p_o, s));
+    GemvArgs u{};
+    if (c.ffn == SDEC_FFN_SWIGLU) {
+      u.w[0] = w.w_gate; u.w[1] = w.w_up; u.w[2] = w.w_up;
+    } else {
+      u.w[0] = u.w[1] = u.w[2] = w.w_up;
+    }
+    u.seg_end[0] = u.seg_end[1] = u.seg_end[2] = c.d_ff;
+    u.n_rows = c.d_ff; u.k = c.d_model; u.m = t; u.x = h->xres; u.x_stride = c.d_model;
+    u.norm_w = w.ffn_norm_w; u.norm_b = w.ffn_norm_b; u.eps = c.norm_eps;
+    u.y = h->act; u.y_stride = c.d_ff;
+    LAUNCH(hk, s, SDEC_K_FFN_UP, launch_gemv(u, p_up, s));
+    GemvArgs dn{};
+    dn.w[0] = dn.w[1] = dn.w[2] = w.w_down;
+    dn.seg_end[0] = dn.seg_end[1] = dn.seg_end[2] = c.d_model;
+    dn.n_rows = c.d_model; dn.k = c.d_ff; dn.m = t; dn.x = h->act; dn.x_stride = c.d_ff;
+    dn.res = h->xres; dn.res_stride = c.d_model; dn.ls = c.layer_scale ? w.ls2 : nullptr;
+    LAUNCH(hk, s, SDEC_K_FFN_DOWN, launch_gemv(dn, p_down, s));
+  }
+  EndArgs e{};
+  e.xres = h->xres; e.x_out = x; e.m = t; e.d = c.d_model;
+  e.norm = c.final_norm ? (c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN) : -1;
+  e.w = h->fin.norm_w; e.b = h->fin.norm_b; e.eps = c.norm_eps;
+  LAUNCH(hk, s, SDEC_K_END, launch_end(e, s));
+  return SDEC_OK;
+}
+
 int clear_state(sdec_handle* h, hipStream_t s) {
   const sdec_config& c = h->cfg;
   const uint64_t nkv = static_cast<uint64_t>(c.m) * c.n_layers * h->ring * c.n_kv_heads * c.head_dim;
   HIP_TRY(launch_fill_f32(h->k_rings, 0.f, nkv, s));
   HIP_TRY(launch_fill_f32(h->v_rings, 0.f, nkv, s));
   HIP_TRY(launch_fill_u32(h->pos_rings, kInvalidPos, static_cast<uint64_t>(c.m) * h->ring, s));
-  HIP_TRY(launch_fill_u32(h->counters, 0u, static_cast<uint64_t>(c.m) * c.n_kv_heads, s));
+  HIP_TRY(launch_fill_u32(h->counters, 0u, static_cast<uint64_t>(h->rows) * c.n_kv_heads, s));
   if (h->persistent) {
     for (uint32_t l = 0; l < c.n_layers; ++l) {
       // the counters sit inside the per-layer hand-off block; see setup_persistent
@@ -450,19 +539,24 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
   h->ring_stream_stride = h->ring_layer_stride * c.n_layers;
   const bool taps = (c.flags & SDEC_FLAG_TAPS) != 0;
 
+  // per-row scratch serves m streams of a step or the rows of a prefill block
+  h->rows = c.m > c.max_prefill ? c.m : c.max_prefill;
+  const size_t rows = h->rows;
   Alloc A;
   h->k_rings = A.get<float>(h->ring_stream_stride * c.m);
   h->v_rings = A.get<float>(h->ring_stream_stride * c.m);
   h->pos_rings = A.get<uint32_t>(static_cast<size_t>(c.m) * ring_slots);
-  h->legal = A.get<uint32_t>(static_cast<size_t>(c.m) * ring_slots);
-  h->n_legal = A.get<uint32_t>(static_cast<size_t>(c.m));
-  h->xres = A.get<float>(static_cast<size_t>(c.m) * c.d_model);
-  h->qkv = A.get<float>(static_cast<size_t>(c.m) * (qw + 2 * kw));
-  h->attn_out = A.get<float>(static_cast<size_t>(c.m) * qw * (taps ? c.n_layers : 1));
-  h->act = A.get<float>(static_cast<size_t>(c.m) * c.d_ff);
-  h->part = A.get<float>(static_cast<size_t>(c.m) * hq * h->n_chunks * (hd + 2));
-  h->counters = A.get<uint32_t>(static_cast<size_t>(c.m) * hkv);
-  h->cs = A.get<float>(hd);
+  h->legal = A.get<uint32_t>(rows * ring_slots);
+  h->n_legal = A.get<uint32_t>(rows);
+  h->xres = A.get<float>(rows * c.d_model);
+  h->qkv = A.get<float>(rows * (qw + 2 * kw));
+  const size_t att_rows = taps && static_cast<size_t>(c.m) * c.n_layers > rows
+                              ? static_cast<size_t>(c.m) * c.n_layers : rows;
+  h->attn_out = A.get<float>(att_rows * qw);
+  h->act = A.get<float>(rows * c.d_ff);
+  h->part = A.get<float>(rows * hq * h->n_chunks * (hd + 2));
+  h->counters = A.get<uint32_t>(rows * hkv);
+  h->cs = A.get<float>(rows * hd);
   h->st = A.get<DevState>(1);
   if (taps) {
     h->tap_attn_proj = A.get<float>(static_cast<size_t>(c.n_layers) * c.m * c.d_model);
@@ -556,6 +650,34 @@ int sdec_step(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stre
   if (r != SDEC_OK) return r;
   h->has_next = true;
   h->next_pos = pos + 1;
+  return SDEC_OK;
+}
+
+int sdec_prefill(sdec_handle* h, float* x, uint32_t pos, uint32_t t, uint32_t first,
+                 void* stream) {
+  if (!h) return fail(SDEC_E_ARG, "null handle");
+  const sdec_config& c = h->cfg;
+  if (c.m != 1) return fail(SDEC_E_ARG, "prefill needs a single-stream stack (m == 1)");
+  const uint32_t cap = c.max_prefill > 1 ? c.max_prefill : 1;
+  if (t < 1 || t > cap) return fail(SDEC_E_ARG, "t=%u must be in [1, max_prefill=%u]", t, cap);
+  int r = check_step(h, x, pos, first);
+  if (r != SDEC_OK) return r;
+  if (static_cast<uint64_t>(pos) + t - 1 >= kInvalidPos)
+    return fail(SDEC_E_ARG, "positions up to %u + %u overflow the position ring", pos, t);
+  // an append evicts position p - R; row r of the block still attends positions > pos + r - W
+  if (static_cast<uint64_t>(pos) + t > h->ring &&
+      static_cast<uint64_t>(h->ring) + 1 < static_cast<uint64_t>(c.window) + t)
+    return fail(SDEC_E_CAPACITY,
+                "a %u-row block past the first ring turn needs ring_slots >= window + %u = %u "
+                "(ring_slots = %u)", t, t - 1, c.window + t - 1, h->ring);
+  if (c.unbounded && static_cast<uint64_t>(pos) + t > h->ring)
+    return fail(SDEC_E_CAPACITY, "positions up to %u exceed the %u-slot ring of an unbounded stack",
+                pos + t - 1, h->ring);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r = enqueue_prefill(h, x, pos, t, first, s, nullptr);
+  if (r != SDEC_OK) return r;
+  h->has_next = true;
+  h->next_pos = pos + t;
   return SDEC_OK;
 }
 

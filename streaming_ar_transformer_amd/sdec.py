@@ -23,7 +23,7 @@ K_NAMES = ["begin", "qkv", "attention", "o_proj", "ffn_up", "ffn_down", "end"]
 # Every symbol include/sdec.h declares.
 EXPORTS = ["sdec_create", "sdec_step", "sdec_reset", "sdec_destroy", "sdec_last_error",
            "sdec_kv_view", "sdec_set_next_position", "sdec_tap_view", "sdec_step_profile",
-           "sdec_gemv", "sdec_ring_attention", "sdec_status", "sdec_step_trace"]
+           "sdec_gemv", "sdec_ring_attention", "sdec_status", "sdec_step_trace", "sdec_prefill"]
 
 
 class SdecError(RuntimeError):
@@ -41,7 +41,8 @@ class Config(ctypes.Structure):
                 ("rope", ctypes.c_uint32), ("rope_theta", ctypes.c_double),
                 ("ffn", ctypes.c_uint32), ("layer_scale", ctypes.c_uint32),
                 ("final_norm", ctypes.c_uint32), ("window", ctypes.c_uint32),
-                ("unbounded", ctypes.c_uint32), ("flags", ctypes.c_uint32)]
+                ("unbounded", ctypes.c_uint32), ("flags", ctypes.c_uint32),
+                ("max_prefill", ctypes.c_uint32)]
 
 
 _LAYER_FIELDS = ["attn_norm_w", "attn_norm_b", "wq", "wk", "wv", "wo", "q_norm", "k_norm", "ls1",
@@ -72,6 +73,7 @@ def lib():
             "sdec_create": (i32, [ctypes.POINTER(Config), ctypes.POINTER(LayerWeights),
                                   ctypes.POINTER(FinalWeights), u32, ctypes.POINTER(vp)]),
             "sdec_step": (i32, [vp, vp, u32, u32, vp]),
+            "sdec_prefill": (i32, [vp, vp, u32, u32, u32, vp]),
             "sdec_reset": (i32, [vp, vp]),
             "sdec_destroy": (None, [vp]),
             "sdec_last_error": (ctypes.c_char_p, []),
@@ -118,7 +120,7 @@ def _ptr(t):
 
 
 def make_config(cfg, window=None, unbounded=None, eager=False, taps=False,
-                persistent=False) -> Config:
+                persistent=False, max_prefill=0) -> Config:
     """Fill the C struct from a ``workloads.StepConfig``-like object."""
     c = Config()
     c.n_layers, c.d_model = cfg.n_layers, cfg.d_model
@@ -132,6 +134,7 @@ def make_config(cfg, window=None, unbounded=None, eager=False, taps=False,
     c.unbounded = int((cfg.family == "T") if unbounded is None else unbounded)
     c.flags = (FLAG_EAGER if eager else 0) | (FLAG_TAPS if taps else 0) | \
         (FLAG_PERSISTENT if persistent else 0)
+    c.max_prefill = max_prefill
     return c
 
 
@@ -142,11 +145,11 @@ class Decoder:
     they are borrowed (this object keeps references so they outlive the handle)."""
 
     def __init__(self, cfg, layers, final=None, ring=None, window=None, unbounded=None,
-                 eager=False, taps=False, persistent=False):
+                 eager=False, taps=False, persistent=False, max_prefill=0):
         self.cfg = cfg
         self.ring = cfg.ring if ring is None else ring
         self.c = make_config(cfg, window=window, unbounded=unbounded, eager=eager, taps=taps,
-                             persistent=persistent)
+                             persistent=persistent, max_prefill=max_prefill)
         self._keep = (layers, final)
         arr = (LayerWeights * cfg.n_layers)()
         for i, lw in enumerate(layers):
@@ -162,6 +165,12 @@ class Decoder:
 
     def step(self, x, pos: int, first: bool = False, stream=None):
         _check(lib().sdec_step(self.h, _ptr(x), int(pos), int(bool(first)), _stream(stream)))
+        return x
+
+    def prefill(self, x, pos: int, first: bool = False, stream=None):
+        """Block of ``x.shape[0]`` consecutive positions from ``pos`` (``sdec_prefill``)."""
+        _check(lib().sdec_prefill(self.h, _ptr(x), int(pos), int(x.shape[0]), int(bool(first)),
+                                  _stream(stream)))
         return x
 
     def step_profile(self, x, pos: int, first: bool = False, stream=None, into=None):

@@ -83,6 +83,7 @@ def _create(c, layers, ring, final=None):
     ("window", 0, "window"),
     ("norm", 7, "norm"),
     ("n_layers", 0, "n_layers"),
+    ("max_prefill", 9, "max_prefill"),
 ])
 def test_create_rejects_bad_config(field, value, msg):
     cfg = wl.CONFIGS[1]
@@ -111,6 +112,15 @@ def test_create_rejects_unbounded_window_and_bad_weights():
     rc, err = _create(c, (sdec.LayerWeights * 1)(_fake_layer(cfg)), 2048,
                       final=sdec.FinalWeights(0, 0))
     assert rc == sdec.E_ARG and "final" in err
+
+
+def test_prefill_needs_one_stream():
+    cfg = wl.CONFIGS[1].replace(m=2)
+    c = sdec.make_config(cfg, max_prefill=4)
+    arr = (sdec.LayerWeights * cfg.n_layers)(_fake_layer(cfg))
+    rc, err = _create(c, arr, cfg.ring)
+    assert rc == sdec.E_ARG and "one stream" in err
+    assert sdec.lib().sdec_prefill(None, 16, 0, 1, 1, None) == sdec.E_ARG
 
 
 def test_one_shot_entry_points_reject_bad_arguments():
