@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-timed", action="store_true",
                     help="warmup + timed steps only (for running under a profiler)")
+    ap.add_argument("--prefill-block", type=int, default=8,
+                    help="rows per sdec_prefill call in the prefill measurement (0: skip it)")
+    ap.add_argument("--prefill-blocks", type=int, default=32,
+                    help="timed prefill calls, positions from 0")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes three times (the "
                          "known-size kernel that calibrates HBM byte counters)")
@@ -67,6 +71,20 @@ def step_bytes(cfg, pos, ring, window):
     kv_row = 2 * 4 * cfg.kv_width
     per_stream = cfg.n_layers * (kv_row * live + kv_row + 4 * ring) + 2 * 4 * cfg.d_model
     return w + cfg.m * per_stream
+
+
+def weight_bytes(cfg):
+    w = cfg.n_layers * layer_weight_bytes(cfg)
+    if cfg.final_norm:
+        w += 4 * cfg.d_model * (2 if cfg.norm == 1 else 1)
+    return w
+
+
+def block_bytes(cfg, pos, t, ring, window):
+    """Algorithmic HBM bytes of one prefill block of t rows from `pos`: every weight once for the
+    block, plus per row what a single step at that position moves besides the weights."""
+    w = weight_bytes(cfg)
+    return w + sum(step_bytes(cfg, pos + r, ring, window) - w for r in range(t))
 
 
 def ffn_up_bytes(cfg):
@@ -231,6 +249,40 @@ def main():
                     "bytes_per_launch": up_bytes, "mean_launch_us": round(up_us, 2)}
     dec.close()
 
+    # prefill: blocks of `prefill_block` positions of one stream per sdec_prefill call
+    prefill = None
+    tb = args.prefill_block
+    if tb > 1 and cfg.m == 1:
+        nb = args.prefill_blocks
+        if unbounded:
+            nb = min(nb, ring // tb)
+        pdec = sdec.Decoder(cfg, dl, df, max_prefill=tb)
+        xb = torch.empty((nb, tb, cfg.d_model), device="cuda")
+        src = torch.from_numpy(np.ascontiguousarray(xs_host[:tb, 0])).cuda()
+        for i in range(nb):
+            xb[i].copy_(src)
+        for i in range(2):  # warmup blocks
+            pdec.prefill(xb[i], i * tb, first=(i == 0), stream=stream)
+        for i in range(nb):
+            xb[i].copy_(src)
+        pdec.reset(stream=stream)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(nb):
+            pdec.prefill(xb[i], i * tb, first=(i == 0), stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        pms = start.elapsed_time(end) / nb
+        pbytes = float(np.mean([block_bytes(cfg, i * tb, tb, ring, window) for i in range(nb)]))
+        pgbs = pbytes / (pms * 1e-3) / 1e9
+        prefill = {"block": tb, "positions": f"0..{nb * tb - 1}", "ms_per_block": round(pms, 4),
+                   "tokens_per_s": round(tb * 1000.0 / pms, 1), "hbm_gbs": round(pgbs, 1),
+                   "hbm_frac": round(pgbs / PEAK_HBM_GBS, 4), "bytes_per_block": int(pbytes),
+                   "mode": "eager"}
+        print(f"prefill {nb} blocks of {tb}: {pms * 1e3:.1f} us/block, "
+              f"{tb * 1000.0 / pms:.0f} tokens/s, {pgbs:.0f} GB/s", file=sys.stderr, flush=True)
+        pdec.close()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, layers, final, xs_host, args.cpu_seconds)
@@ -247,7 +299,7 @@ def main():
                    "mode": mode},
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": int(bytes_avg),
-        "roofline": roofline, "eager_kernels": kernels, "cpu_baseline": cpu,
+        "roofline": roofline, "eager_kernels": kernels, "prefill": prefill, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

@@ -583,6 +583,184 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rows(GemvArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// Split-k GEMV for M input rows (m streams, or the rows of a prefill block), k = NW*256*KW: the
+// workgroup's NW waves take the NW slices of k, so a wave keeps only its slice of all M input
+// rows in registers (M*KW float4 per lane) and every weight float4 it loads meets all M rows
+// there: the M-row step reads each weight once ([talker] MATVEC_SRC loops the m rows per weight
+// read; [mimi] MV_LS).  Row slot rr of workgroup b is unit b + (rr mod U) * G as in k_gemv_ks; the
+// slice sums and the per-row norm statistics meet in LDS.
+// ------------------------------------------------------------------------------------------------
+template <int M, int NW, int KW, int RB, int PRO, int EPI>
+__global__ __launch_bounds__(NW * kWave) void k_gemv_ksm(GemvArgs a) {
+  constexpr int U = EPI == EPI_SWIGLU ? RB / 2 : RB;
+  constexpr int V = RB * M;
+  static_assert(V <= kWave && kWave % V == 0 && (EPI != EPI_SWIGLU || RB % 2 == 0), "tile");
+  __shared__ float part[NW][V];
+  __shared__ float stat[2][M][NW];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const uint32_t n = a.n_rows, G = gridDim.x, mv = a.m;
+  const uint32_t off = static_cast<uint32_t>(wave) * (KW * kWave) + lane;  // float4 in the row
+  const float4* x4 = reinterpret_cast<const float4*>(a.x);
+  const uint32_t xs4 = a.x_stride >> 2;
+  float4 xr[M][KW], gr[PRO == PRO_NONE ? 1 : KW], br[PRO == PRO_LN ? KW : 1];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int j = 0; j < KW; ++j) xr[m][j] = x4[min(static_cast<uint32_t>(m), mv - 1) * xs4 + off + kWave * j];
+  if (PRO != PRO_NONE) {
+#pragma unroll
+    for (int j = 0; j < KW; ++j) gr[j] = reinterpret_cast<const float4*>(a.norm_w)[off + kWave * j];
+  }
+  if (PRO == PRO_LN) {
+#pragma unroll
+    for (int j = 0; j < KW; ++j) br[j] = reinterpret_cast<const float4*>(a.norm_b)[off + kWave * j];
+  }
+  float4 w[RB][KW];
+  auto row_base = [&](uint32_t u, int rr) {
+    const float* base = a.w[0];
+    uint32_t row = u;
+    if (EPI == EPI_SWIGLU) {
+      base = rr < U ? a.w[0] : a.w[1];
+    } else if (row >= a.seg_end[1]) {
+      base = a.w[2];
+      row -= a.seg_end[1];
+    } else if (row >= a.seg_end[0]) {
+      base = a.w[1];
+      row -= a.seg_end[0];
+    }
+    return reinterpret_cast<const float4*>(base + static_cast<size_t>(row) * a.k) + off;
+  };
+  // thread tid writes output (unit slot tid / M, row tid % M) when tid < U*M; every thread requests
+  // the old residual and LayerScale of slot tid % (U*M) (unconditional, duplicates unused)
+  const uint32_t es = static_cast<uint32_t>(tid) % (U * M);
+  const uint32_t e_u = es / M, e_m = es % M;
+  float res_old = 0.f, ls_v = 1.f;
+  auto load = [&](uint32_t u0) {
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const float4* wr = row_base(min(u0 + (rr % U) * G, n - 1), rr);
+#pragma unroll
+      for (int j = 0; j < KW; ++j) w[rr][j] = ldw(wr + kWave * j);
+    }
+    if (EPI == EPI_RESIDUAL) {
+      const uint32_t u = min(u0 + e_u * G, n - 1);
+      res_old = (a.res_in ? a.res_in : a.res)[min(e_m, mv - 1) * a.res_stride + u];
+      if (a.ls) ls_v = a.ls[u];
+    }
+  };
+  asm volatile("" ::: "memory");  // the input slices (and gains) are requested before the rows
+  uint32_t u0 = blockIdx.x;
+  load(u0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  if (PRO != PRO_NONE) {  // per input row: statistics of the whole row from the NW slices
+    const float kf = static_cast<float>(a.k);
+    float mean[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) mean[m] = 0.f;
+    if (PRO == PRO_LN) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float sm = 0.f;
+#pragma unroll
+        for (int j = 0; j < KW; ++j) sm += (xr[m][j].x + xr[m][j].y) + (xr[m][j].z + xr[m][j].w);
+        sm = wave_sum(sm);
+        if (lane == 0) stat[0][m][wave] = sm;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float tot = 0.f;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) tot += stat[0][m][q];
+        mean[m] = tot / kf;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < KW; ++j) {
+        float4 d = xr[m][j];
+        d.x -= mean[m]; d.y -= mean[m]; d.z -= mean[m]; d.w -= mean[m];
+        ss = dot4(d, d, ss);
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) stat[1][m][wave] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float tot = 0.f;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) tot += stat[1][m][q];
+      const float inv = 1.0f / sqrtf(tot / kf + a.eps);
+#pragma unroll
+      for (int j = 0; j < KW; ++j) {
+        float4 v = xr[m][j];
+        const float4 g = gr[j];
+        if (PRO == PRO_RMS) {
+          v.x = (v.x * inv) * g.x; v.y = (v.y * inv) * g.y;
+          v.z = (v.z * inv) * g.z; v.w = (v.w * inv) * g.w;
+        } else {
+          const float4 b = br[j];
+          v.x = ((v.x - mean[m]) * inv) * g.x + b.x; v.y = ((v.y - mean[m]) * inv) * g.y + b.y;
+          v.z = ((v.z - mean[m]) * inv) * g.z + b.z; v.w = ((v.w - mean[m]) * inv) * g.w + b.w;
+        }
+        xr[m][j] = v;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m)  // rows past the valid ones contribute nothing
+#pragma unroll
+    for (int j = 0; j < KW; ++j) xr[m][j] = static_cast<uint32_t>(m) < mv ? xr[m][j] : f4zero();
+
+  for (;;) {
+    float acc[V];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float d = 0.f;
+#pragma unroll
+        for (int j = 0; j < KW; ++j) d = dot4(w[rr][j], xr[m][j], d);
+        acc[rr * M + m] = d;
+      }
+    ReduceScatter<V, 32>::run(acc, lane);  // lane (64/V)*i holds value i's slice sum
+    if (lane % (kWave / V) == 0) part[wave][lane / (kWave / V)] = acc[0];
+    __syncthreads();
+    const uint32_t base = u0;
+    const float res_here = res_old, ls_here = ls_v;
+    u0 += G * U;
+    if (u0 < n) load(u0);  // the next rows stream while this tile's results are written
+    if (static_cast<uint32_t>(tid) < U * M) {
+      const uint32_t u = base + e_u * G;
+      if (u < n && e_m < mv) {
+        float v = 0.f;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) v += part[q][e_u * M + e_m];
+        if (EPI == EPI_SWIGLU) {
+          float up = 0.f;
+#pragma unroll
+          for (int q = 0; q < NW; ++q) up += part[q][(e_u + U) * M + e_m];
+          a.y[e_m * a.y_stride + u] = silu(v) * up;
+        } else if (EPI == EPI_STORE) {
+          a.y[e_m * a.y_stride + u] = v;
+        } else if (EPI == EPI_GELU) {
+          a.y[e_m * a.y_stride + u] = gelu_erf(v);
+        } else {
+          if (a.tap) a.tap[e_m * a.tap_stride + u] = v;
+          a.res[e_m * a.res_stride + u] = res_here + (a.ls ? ls_here * v : v);
+        }
+      }
+    }
+    if (u0 >= n) return;
+    __syncthreads();  // part is rewritten by the next tile
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // Split-k GEMV for one stream (k = 1024*KW), with the norm prologues and every epilogue of the
 // register GEMV ([talker] build_step_plan; [mimi] MV_LS).  The workgroup's four waves take the
 // four quarters of each of its RB rows, so a wave keeps only its quarter of the (normalised) input
@@ -966,6 +1144,31 @@ GemvKernel gemv_rx_attn(int kb) {
   return {nullptr, 0};
 }
 
+// The multi-row split-k kernels: ks = KW (float4 per lane per row slice), waves_per_wg = NW,
+// rows_per_wave = rows per workgroup tile.
+template <int M, int NW, int KW, int RB>
+GemvKernel gemv_ksm_kind(const GemvLaunch& l) {
+#define SDEC_KSM(P, E) \
+  if (l.prologue == P && l.epilogue == E) \
+    return {reinterpret_cast<const void*>(&k_gemv_ksm<M, NW, KW, RB, P, E>), 0};
+  SDEC_KSM(PRO_NONE, EPI_STORE)
+  SDEC_KSM(PRO_NONE, EPI_RESIDUAL)
+  SDEC_KSM(PRO_RMS, EPI_STORE)
+  SDEC_KSM(PRO_LN, EPI_STORE)
+  SDEC_KSM(PRO_RMS, EPI_SWIGLU)
+  SDEC_KSM(PRO_RMS, EPI_GELU)
+  SDEC_KSM(PRO_LN, EPI_SWIGLU)
+  SDEC_KSM(PRO_LN, EPI_GELU)
+#undef SDEC_KSM
+  return {nullptr, 0};
+}
+template <int M>
+GemvKernel gemv_ksm(const GemvLaunch& l) {
+  if (l.waves_per_wg == 4 && l.ks == 2 && l.rows_per_wave == 4) return gemv_ksm_kind<M, 4, 2, 4>(l);
+  if (l.waves_per_wg == 8 && l.ks == 3 && l.rows_per_wave == 2) return gemv_ksm_kind<M, 8, 3, 2>(l);
+  return {nullptr, 0};
+}
+
 // The row-stream kernels: k = 256*kb.
 template <int KB>
 GemvKernel gemv_stream_kb(const GemvLaunch& l) {
@@ -1022,6 +1225,8 @@ GemvKernel gemv_pick_m(const GemvLaunch& l, uint32_t k) {
   if constexpr (M == 1) {
     if (l.ks > 0) return gemv_ks(l);
     if (l.stream) return gemv_stream(l);
+  } else {
+    if (l.ks > 0) return gemv_ksm<M>(l);
   }
 #define SDEC_KIND(P, E) \
   if (l.prologue == P && l.epilogue == E) return gemv_pick_r<M, P, E>(l, k);
@@ -1115,6 +1320,27 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
     l.grid = need < max_wgs ? need : max_wgs;
     if (l.grid < 1) l.grid = 1;
     return l;
+  }
+  if (M >= 2 && (k == 2048 || k == 6144) && prologue != PRO_ATTN &&
+      env_int("SDEC_GEMV_SPLITK", 1) != 0) {
+    // the NW waves of a workgroup take the NW slices of k; all M input rows of a slice in registers
+    l.ks = k == 2048 ? 2 : 3;
+    l.kb = 0;
+    l.waves_per_wg = k == 2048 ? 4 : 8;
+    l.rows_per_wave = k == 2048 ? 4 : 2;
+    const int units_per_wg = epilogue == EPI_SWIGLU ? l.rows_per_wave / 2 : l.rows_per_wave;
+    int occ_m = 1;
+    const GemvKernel kern = gemv_pick(l, k, m);
+    if (kern.fn == nullptr ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_m, kern.fn, l.waves_per_wg * kWave, 0) !=
+            hipSuccess || occ_m < 1)
+      occ_m = 1;
+    const uint32_t need = (n_rows + units_per_wg - 1) / units_per_wg;
+    const uint32_t max_wgs = static_cast<uint32_t>(cus * occ_m);
+    l.grid = need < max_wgs ? need : max_wgs;
+    if (l.grid < 1) l.grid = 1;
+    if (kern.fn != nullptr) return l;
+    l.ks = 0;  // no such kernel: the register GEMV below
   }
   if (M == 1 && l.kb == 8 && epilogue == EPI_SWIGLU && env_int("SDEC_GEMV_STREAM", 1) != 0 &&
       n_rows % (4u * static_cast<uint32_t>(cus)) == 0 && n_rows / (4u * static_cast<uint32_t>(cus)) <= 64) {
