@@ -47,6 +47,8 @@ def parse():
                     help="rows per sdec_prefill call in the prefill measurement (0: skip it)")
     ap.add_argument("--prefill-blocks", type=int, default=32,
                     help="timed prefill calls, positions from 0")
+    ap.add_argument("--no-variant", action="store_true",
+                    help="skip the FlowLM-variant measurement (workload 6)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes three times (the "
                          "known-size kernel that calibrates HBM byte counters)")
@@ -156,7 +158,7 @@ def main():
     torch.cuda.set_device(0)
     cfg = wl.CONFIGS[args.config]
     ring, window = cfg.ring, cfg.window
-    unbounded = cfg.family == "T"
+    unbounded = cfg.is_unbounded
     t0 = time.perf_counter()
     layers, final = wl.make_weights(cfg)
     dl, df = upload_weights(layers, final)
@@ -283,6 +285,36 @@ def main():
               f"{tb * 1000.0 / pms:.0f} tokens/s, {pgbs:.0f} GB/s", file=sys.stderr, flush=True)
         pdec.close()
 
+    # the FlowLM backbone variant of the same step (workload 6), graph path, a fresh stream
+    variant = None
+    if not args.no_variant and args.config == 4:
+        vcfg = wl.CONFIGS[6]
+        vl, vf = wl.make_weights(vcfg)
+        vdl, vdf = upload_weights(vl, vf)
+        vhost = wl.make_inputs(vcfg, vcfg.ring)
+        vx = to_device(vhost)
+        vdec = sdec.Decoder(vcfg, vdl, vdf)
+        for i in range(32):
+            vdec.step(vx[i], i, first=(i == 0), stream=stream)
+        vx.copy_(torch.from_numpy(vhost))
+        vdec.reset(stream=stream)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(vcfg.ring):
+            vdec.step(vx[i], i, first=(i == 0), stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        vms = start.elapsed_time(end) / vcfg.ring
+        vbytes = float(np.mean([step_bytes(vcfg, i, vcfg.ring, vcfg.window)
+                                for i in range(vcfg.ring)]))
+        vgbs = vbytes / (vms * 1e-3) / 1e9
+        variant = {"workload": vcfg.name, "positions": f"0..{vcfg.ring - 1}",
+                   "steps_per_s": round(1000.0 / vms, 1), "ms_per_step": round(vms, 5),
+                   "hbm_gbs": round(vgbs, 1), "hbm_frac": round(vgbs / PEAK_HBM_GBS, 4),
+                   "bytes_per_step": int(vbytes), "mode": "hipgraph"}
+        print(f"{vcfg.name}: {vms * 1e3:.1f} us/step, {vgbs:.0f} GB/s", file=sys.stderr, flush=True)
+        vdec.close()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, layers, final, xs_host, args.cpu_seconds)
@@ -299,7 +331,8 @@ def main():
                    "mode": mode},
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": int(bytes_avg),
-        "roofline": roofline, "eager_kernels": kernels, "prefill": prefill, "cpu_baseline": cpu,
+        "roofline": roofline, "eager_kernels": kernels, "prefill": prefill, "variant": variant,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

@@ -202,7 +202,7 @@ class OracleDecoder:
         self.W = cfg.window if window is None else window
         # The talker's cache (and the FlowLM ring) refuses positions past its capacity
         # ([talker] ``TalkerGpu::step``; [pocket] ``PocketBackboneGpu::step``); a codec ring wraps.
-        self.unbounded = (cfg.family == "T") if unbounded is None else unbounded
+        self.unbounded = cfg.is_unbounded if unbounded is None else unbounded
         if self.W > self.R or self.W < 1:
             raise ValueError("window must be in [1, ring]")
         m, L, hkv, hd = cfg.m, cfg.n_layers, cfg.n_kv_heads, cfg.head_dim

@@ -131,7 +131,7 @@ def make_config(cfg, window=None, unbounded=None, eager=False, taps=False,
     c.rope, c.rope_theta = cfg.rope, cfg.rope_theta
     c.ffn, c.layer_scale, c.final_norm = cfg.ffn, int(cfg.layer_scale), int(cfg.final_norm)
     c.window = cfg.window if window is None else window
-    c.unbounded = int((cfg.family == "T") if unbounded is None else unbounded)
+    c.unbounded = int(cfg.is_unbounded if unbounded is None else unbounded)
     c.flags = (FLAG_EAGER if eager else 0) | (FLAG_TAPS if taps else 0) | \
         (FLAG_PERSISTENT if persistent else 0)
     c.max_prefill = max_prefill

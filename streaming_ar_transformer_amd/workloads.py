@@ -65,6 +65,12 @@ class StepConfig:
     weight_std: float | None = None  # fixed std, or None for 1/sqrt(k)
     bf16_round: bool = False
     weight_seed: int | None = None  # cfg_id whose weights this stack shares (None: its own)
+    unbounded: bool | None = None  # refuse positions past the ring (None: the talker family does)
+    eos: bool = False  # an EOS logit row [1, d_model] (+ scalar bias) reads the output row
+
+    @property
+    def is_unbounded(self) -> bool:
+        return (self.family == "T") if self.unbounded is None else self.unbounded
 
     @property
     def q_width(self) -> int:
@@ -96,6 +102,20 @@ def _talker(name, cfg_id, m, ring, steps, start_pos, weight_seed=None):
         start_pos=start_pos, weight_std=None, bf16_round=True, weight_seed=weight_seed)
 
 
+def _flowlm(name, cfg_id, ring, steps):
+    # [pocket] PocketBackboneGpu::new: the codec builder's layer (LayerNorm eps 1e-5, packed
+    # in_proj, interleaved rope, GELU FFN) with no LayerScale and no window (window == ring ==
+    # max_positions), then the output LayerNorm and the EOS logit.  6 layers, d1024, 16 heads as
+    # the page states; the FFN width (4 * d) and the rope base (the codec builder's 1e4) are
+    # readings.
+    return StepConfig(
+        name=name, cfg_id=cfg_id, family="C", n_layers=6, d_model=1024, n_q_heads=16,
+        n_kv_heads=16, head_dim=64, d_ff=4096, m=1, norm=NORM_LAYER, norm_eps=1e-5,
+        qk_norm=False, qk_norm_eps=0.0, rope=ROPE_INTERLEAVED, rope_theta=10000.0,
+        ffn=FFN_GELU, layer_scale=False, layer_scale_init=1.0, final_norm=True, ring=ring,
+        window=ring, steps=steps, weight_std=0.02, unbounded=True, eos=True)
+
+
 # The five workloads.  Ring/window readings: a ring that holds exactly the window is exact at one
 # position per step; config 2 keeps the codec plan's "window + positions per call" capacity so the
 # window mask, not the overwrite, is what hides the oldest slot.
@@ -106,6 +126,9 @@ CONFIGS = {
     4: _talker("talker28_h2048_m1", 4, 1, 2048, 2048, 0),
     # The m=8 workload runs the same talker as config 4, so it shares config 4's weights.
     5: _talker("talker28_h2048_m8_prefill4096", 5, 8, 4352, 256, 4096, weight_seed=4),
+    # Next to the five: the FlowLM backbone variant of the same step (unbounded, no LayerScale,
+    # final LayerNorm and an EOS logit).
+    6: _flowlm("flowlm6_d1024_r512", 6, 512, 512),
 }
 
 
@@ -193,6 +216,14 @@ def make_weights(cfg: StepConfig, threads: int = 8):
             lw["wk"] = lw["in_proj"][qw:qw + kw]
             lw["wv"] = lw["in_proj"][qw + kw:]
     return layers, final
+
+
+def make_eos(cfg: StepConfig):
+    """The EOS logit row ``[1, d_model]`` (std 0.02) and its scalar bias (N(0, 1)), seeded
+    ``[cfg_id, 3]``; the bias is applied on the host ([pocket] PocketBackboneGpu: ``eos_bias``)."""
+    w = _normal([cfg.cfg_id, 3, 0], (1, cfg.d_model), 0.02)
+    b = float(_normal([cfg.cfg_id, 3, 1], (1,), 1.0)[0])
+    return w, b
 
 
 def make_inputs(cfg: StepConfig, steps: int | None = None) -> np.ndarray:
