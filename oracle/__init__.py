@@ -9,3 +9,4 @@ from .step import (  # noqa: F401
     OracleDecoder, apply_rope, attend, gelu_erf, gemv, layer_norm, rms_norm, rope_cos_sin,
     rope_pairs, seq_sum, silu_mul, valid_slots,
 )
+from .rvq import OracleRVQ, emb_sum, nearest, sq_distances  # noqa: F401,E402

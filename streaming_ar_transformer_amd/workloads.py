@@ -263,3 +263,40 @@ def small_config(family: str = "T", **kw) -> StepConfig:
     base = CONFIGS[4] if family == "T" else CONFIGS[1]
     base = base.replace(name=f"small_{family}", cfg_id=100 + (1 if family == "T" else 0))
     return base.replace(**kw)
+
+
+@dataclasses.dataclass(frozen=True)
+class RVQConfig:
+    """Split RVQ geometry ([mimi] ``MimiGpu``: latent DIM 512, VQ_DIM 256, 2048-bin codebooks, one
+    first codebook and NQ - 1 rest codebooks) and the frames drawn for it."""
+
+    name: str
+    seed: int
+    dim: int = 512
+    vq: int = 256
+    bins: int = 2048
+    nq: int = 8
+    frames: int = 64
+
+    def replace(self, **kw) -> "RVQConfig":
+        return dataclasses.replace(self, **kw)
+
+
+RVQ_CONFIGS = {1: RVQConfig("rvq8_d512_v256_b2048", 7)}
+
+
+def make_rvq(cfg: RVQConfig):
+    """Projections N(0, 1/sqrt(k)), codebooks N(0, 1), latent frames N(0, 1), seeded
+    ``[seed, 4, part]``.  Returns a dict of float32 arrays."""
+    d, v, b, nq = cfg.dim, cfg.vq, cfg.bins, cfg.nq
+    s = cfg.seed
+    return {
+        "in_first": _normal([s, 4, 0], (v, d), 1.0 / np.sqrt(d)),
+        "in_rest": _normal([s, 4, 1], (v, d), 1.0 / np.sqrt(d)),
+        "out_first": _normal([s, 4, 2], (d, v), 1.0 / np.sqrt(v)),
+        "out_rest": _normal([s, 4, 3], (d, v), 1.0 / np.sqrt(v)),
+        "cb_first": _normal([s, 4, 4], (1, b, v), 1.0),
+        "cb_rest": _normal([s, 4, 5], (nq - 1, b, v), 1.0),
+        "latents": _normal([s, 4, 6], (cfg.frames, d), 1.0),
+    }
+

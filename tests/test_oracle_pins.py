@@ -464,3 +464,105 @@ def test_page_facts():
         c = wl.CONFIGS[i]
         assert c.rope_theta == facts["talker_rope_theta"]["value"]
         assert c.head_dim <= facts["talker_max_head_dim"]["value"]
+
+
+# ---------------------------------------------------------------------------------------------
+# split RVQ ([mimi] NEAREST, SUB_EMB, EMB_SUM and the encode / decode plans)
+# ---------------------------------------------------------------------------------------------
+
+def test_rvq_distances_exact_on_small_integers():
+    # |cb|, |r| <= 8 integers: every difference, square and partial sum is exact in float32.
+    rng = np.random.default_rng(30)
+    cb = rng.integers(-8, 9, size=(300, 64)).astype(F32)
+    r = rng.integers(-8, 9, size=64).astype(F32)
+    exact = ((cb.astype(np.int64) - r.astype(np.int64)) ** 2).sum(axis=1)
+    np.testing.assert_array_equal(oracle.sq_distances(cb, r), exact.astype(F32))
+
+
+def test_rvq_distances_sequential_order_no_fma():
+    # The float32 sum runs over c in ascending order with the square rounded first: equal to an
+    # explicit scalar loop, and different from a float64 sum on data where order matters.
+    rng = np.random.default_rng(31)
+    cb = (rng.standard_normal((40, 256)) * 100).astype(F32)
+    r = rng.standard_normal(256).astype(F32)
+    d = oracle.sq_distances(cb, r)
+    for b in (0, 17, 39):
+        acc = F32(0)
+        for c in range(256):
+            df = F32(cb[b, c] - r[c])
+            acc = F32(acc + F32(df * df))
+        assert d[b] == acc
+    d64 = ((cb.astype(np.float64) - r.astype(np.float64)) ** 2).sum(axis=1)
+    np.testing.assert_allclose(d, d64, rtol=1e-5)
+
+
+def test_rvq_nearest_first_wins_and_brute_force():
+    rng = np.random.default_rng(32)
+    cb = rng.standard_normal((256, 32)).astype(F32)
+    r = rng.standard_normal(32).astype(F32)
+    d64 = ((cb.astype(np.float64) - r) ** 2).sum(axis=1)
+    assert oracle.nearest(cb, r) == int(np.argmin(d64))
+    # exact ties: duplicated rows (and an exactly equidistant pair) go to the lower bin
+    cb2 = cb.copy()
+    best = oracle.nearest(cb, r)
+    cb2[3] = cb[best]
+    cb2[200] = cb[best]
+    assert oracle.nearest(cb2, r) == min(3, best)
+    cbi = np.array([[2, 0], [0, 2], [-2, 0], [1, 1]], F32)  # distances 4, 4, 4, 2 from (0, 0)
+    assert oracle.nearest(cbi, np.zeros(2, F32)) == 3
+    assert oracle.nearest(cbi[:3], np.zeros(2, F32)) == 0
+
+
+def test_rvq_emb_sum_order_and_values():
+    cbs = np.zeros((3, 4, 2), F32)
+    cbs[0, 1] = [1e8, 1.0]
+    cbs[1, 2] = [1.0, 2.0]
+    cbs[2, 3] = [-1e8, 3.0]
+    acc = oracle.emb_sum(cbs, [1, 2, 3])
+    # sequential: (1e8 + 1) rounds to 1e8, then - 1e8 -> 0 (a pairwise sum would give 1)
+    assert acc[0] == F32(0.0) and acc[1] == F32(6.0)
+
+
+def _rvq_identity(nq=4, vq=16, bins=32, seed=33):
+    # identity projections (dim == vq) and well-separated codebooks: codes are recoverable
+    rng = np.random.default_rng(seed)
+    eye = np.eye(vq, dtype=F32)
+    cb_first = (rng.standard_normal((1, bins, vq)) * 4).astype(F32)
+    cb_rest = (rng.standard_normal((nq - 1, bins, vq)) * 4 / np.arange(1, nq)[:, None, None]).astype(F32)
+    return oracle.OracleRVQ(eye, eye, eye, eye, cb_first, cb_rest), cb_first, cb_rest
+
+
+def test_rvq_encode_recovers_planted_codes_and_decode_inverts():
+    # latent = cb_rest[0][a] + cb_rest[1][b] + cb_rest[2][c] (shrinking scales) with identity
+    # projections: the rest chain finds a, b, c in turn; the first codebook sees the latent itself.
+    q, cb_first, cb_rest = _rvq_identity()
+    planted = [5, 17, 30]
+    x = (cb_rest[0, 5] + cb_rest[1, 17] + cb_rest[2, 30]).astype(F32)
+    codes = q.encode(x)
+    assert list(codes[1:]) == planted
+    assert codes[0] == oracle.nearest(cb_first[0], x)
+    y = q.decode(codes)
+    want = (cb_first[0, codes[0]] + (cb_rest[0, 5] + cb_rest[1, 17] + cb_rest[2, 30]))
+    np.testing.assert_allclose(y, want, rtol=1e-6, atol=1e-6)
+
+
+def test_rvq_last_level_skips_the_residual_update():
+    # nq = 2: one rest level; quantise never subtracts after it (changing the rest codebook's
+    # rows other than the chosen one cannot change the result)
+    q, _, cb_rest = _rvq_identity(nq=2)
+    x = cb_rest[0, 9].copy()
+    codes, margins = q.quantise(x, x)
+    assert codes[1] == 9 and len(margins) == 2
+
+
+def test_rvq_workload_margins_exceed_rounding():
+    # Every decision of the seeded RVQ workload has a relative margin far above what rounding in
+    # the projections can move a distance by, so the GPU must reproduce the codes bit for bit.
+    cfg = wl.RVQ_CONFIGS[1]
+    R = wl.make_rvq(cfg.replace(frames=16))
+    q = oracle.OracleRVQ(R["in_first"], R["in_rest"], R["out_first"], R["out_rest"],
+                         R["cb_first"], R["cb_rest"])
+    for f in range(16):
+        _, margins = q.quantise(*q.project(R["latents"][f]))
+        for best, second in margins:
+            assert (second - best) / best > 1e-6
