@@ -212,6 +212,50 @@ int sdec_ring_attention(const float* q, const float* k_ring, const float* v_ring
                         uint32_t n_kv_heads, uint32_t head_dim, uint32_t ring_slots,
                         uint32_t window, uint32_t pos, void* stream);
 
+/* Split residual vector quantiser ([mimi] inferencelayer 0.2.1, src/mimi_gpu.rs: the NEAREST,
+ * SUB_EMB and EMB_SUM kernels and MimiGpu's encode / decode plans).  A latent frame [dim] is
+ * projected twice (in_first, in_rest: [vq][dim]); code 0 is the nearest bin of codebook
+ * cb_first to the first projection; codes 1 .. nq-1 quantise the second projection with the
+ * nq-1 rest codebooks in turn, each subtracting its chosen code vector from the running residual
+ * before the next.  "Nearest" is the smallest squared distance sum_c (cb[b][c] - r[c])^2 summed
+ * over c in ascending order in float32 with no fused multiply-add; ties go to the lower bin.
+ * Decoding sums each group's chosen code vectors (in level order) and returns
+ * out_first . sum_first + out_rest . sum_rest (out_*: [dim][vq]).  Codebooks: cb_first
+ * [bins][vq], cb_rest [nq-1][bins][vq].  All weights are borrowed device pointers, 16-byte
+ * aligned, unchanged until sdec_rvq_destroy; the library keeps a transposed copy of the
+ * codebooks. */
+typedef struct sdec_rvq_config {
+  uint32_t dim;        /* latent width; multiple of 4 */
+  uint32_t vq;         /* quantiser width; multiple of 64, at most 1024 */
+  uint32_t bins;       /* bins per codebook; multiple of 64, at least 64 */
+  uint32_t nq;         /* codebooks: 1 first + nq-1 rest; at least 2 */
+  uint32_t max_frames; /* frames one call may carry; 1 .. 65535 */
+} sdec_rvq_config;
+typedef struct sdec_rvq_weights {
+  const float* in_first;  /* [vq][dim] */
+  const float* in_rest;   /* [vq][dim] */
+  const float* out_first; /* [dim][vq] */
+  const float* out_rest;  /* [dim][vq] */
+  const float* cb_first;  /* [bins][vq] */
+  const float* cb_rest;   /* [nq-1][bins][vq] */
+} sdec_rvq_weights;
+typedef struct sdec_rvq sdec_rvq;
+/* Validate, allocate the working buffers and the transposed codebooks.  Synchronous. */
+int sdec_rvq_create(const sdec_rvq_config* cfg, const sdec_rvq_weights* w, sdec_rvq** out);
+/* Encode `frames` latent frames: latent device [frames][dim] float32 -> codes device
+ * [frames][nq] uint32.  Asynchronous on `stream`. */
+int sdec_rvq_encode(sdec_rvq* q, const float* latent, uint32_t frames, uint32_t* codes,
+                    void* stream);
+/* The quantiser alone, from given projections r_first, r_rest (device [frames][vq] each). */
+int sdec_rvq_quantise(sdec_rvq* q, const float* r_first, const float* r_rest, uint32_t frames,
+                      uint32_t* codes, void* stream);
+/* Decode codes device [frames][nq] (each < bins; a larger value reads bin bins-1) into latent
+ * device [frames][dim] float32.  Asynchronous on `stream`. */
+int sdec_rvq_decode(sdec_rvq* q, const uint32_t* codes, uint32_t frames, float* latent,
+                    void* stream);
+/* Release the buffers the library owns (synchronizes the device first).  NULL is accepted. */
+void sdec_rvq_destroy(sdec_rvq* q);
+
 #ifdef __cplusplus
 }
 #endif

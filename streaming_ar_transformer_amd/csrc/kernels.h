@@ -158,6 +158,38 @@ struct EndArgs {
 };
 hipError_t launch_end(const EndArgs& a, hipStream_t s);
 
+// Split RVQ (rvq.hip; [mimi] NEAREST, SUB_EMB, EMB_SUM).  One quantiser level for every frame:
+// optionally resolve the previous level's code from its per-wave candidates (and write it), then
+// optionally subtract that code's vector from the running residual (prev_cb), then let every
+// wave of 64 bins leave its first-wins candidate (distance, bin).
+constexpr int kRvqMaxVq = 1024;
+struct RvqLevelArgs {
+  const float* cbT;            // this level's codebook, transposed [vq][bins]
+  const float* r_in;           // [frames][r_stride] residual entering the level
+  uint32_t r_stride;
+  float* r_out;                // [frames][vq] the residual this level quantises (null: not kept)
+  const float* prev_cb;        // previous level's codebook rows [bins][vq]: subtract its code
+  const float* prev_cand_d;    // previous level's candidates [frames][groups] (null: none)
+  const uint32_t* prev_cand_i;
+  uint32_t prev_level;         // code index of the previous level
+  float* cand_d;               // this level's candidates [frames][groups]
+  uint32_t* cand_i;
+  uint32_t* codes;             // [frames][nq]
+  uint32_t nq, bins, vq, groups;
+};
+struct RvqEmbArgs {
+  const uint32_t* codes;       // [frames][nq]
+  const float* cb_first;       // [bins][vq]
+  const float* cb_rest;        // [nq-1][bins][vq]
+  float* acc;                  // [frames][2][vq]: first-group sum, rest-group sum
+  uint32_t nq, bins, vq;
+};
+hipError_t launch_rvq_transpose(const float* src, float* dst, uint32_t levels, uint32_t bins,
+                                uint32_t vq, hipStream_t s);
+hipError_t launch_rvq_level(const RvqLevelArgs& a, uint32_t frames, hipStream_t s);
+hipError_t launch_rvq_final(const RvqLevelArgs& a, uint32_t frames, hipStream_t s);
+hipError_t launch_rvq_emb_sum(const RvqEmbArgs& a, uint32_t frames, hipStream_t s);
+
 // Persistent step kernel (step.hip): one cooperative launch per step for a single stream.
 struct StepLayer {
   const float *attn_norm_w, *attn_norm_b, *wq, *wk, *wv, *wo, *q_norm, *k_norm, *ls1;

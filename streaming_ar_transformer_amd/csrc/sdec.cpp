@@ -893,3 +893,200 @@ int sdec_ring_attention(const float* q, const float* k_ring, const float* v_ring
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------------------------------------
+// Split RVQ ([mimi] NEAREST, SUB_EMB, EMB_SUM; MimiGpu's encode and decode plans).
+// ------------------------------------------------------------------------------------------------
+struct sdec_rvq {
+  sdec_rvq_config cfg{};
+  sdec_rvq_weights w{};
+  uint32_t groups = 0;
+  float* cbT = nullptr;       // [nq][vq][bins]: level 0 = first, 1.. = rest
+  float* proj = nullptr;      // [max_frames][2 vq]
+  float* res = nullptr;       // [2][max_frames][vq] running residual (ping-pong)
+  float* cand_d = nullptr;    // [nq][max_frames][groups]
+  uint32_t* cand_i = nullptr;
+  float* acc = nullptr;       // [max_frames][2 vq]
+};
+
+namespace {
+
+void rvq_free(sdec_rvq* q) {
+  void* ps[] = {q->cbT, q->proj, q->res, q->cand_d, q->cand_i, q->acc};
+  for (void* p : ps)
+    if (p) (void)hipFree(p);
+}
+
+int rvq_check_frames(const sdec_rvq* q, uint32_t frames) {
+  if (!q) return fail(SDEC_E_ARG, "null rvq handle");
+  if (frames < 1 || frames > q->cfg.max_frames)
+    return fail(SDEC_E_ARG, "frames=%u must be in [1, max_frames=%u]", frames, q->cfg.max_frames);
+  return SDEC_OK;
+}
+
+// GEMV rows in blocks of at most kMaxM frames.
+template <class F>
+int rvq_row_blocks(uint32_t frames, F body) {
+  for (uint32_t f0 = 0; f0 < frames; f0 += static_cast<uint32_t>(kMaxM)) {
+    const uint32_t n = frames - f0 < static_cast<uint32_t>(kMaxM) ? frames - f0 : kMaxM;
+    int r = body(f0, n);
+    if (r != SDEC_OK) return r;
+  }
+  return SDEC_OK;
+}
+
+int rvq_quantise_levels(sdec_rvq* q, const float* r_first, uint32_t sf, const float* r_rest,
+                        uint32_t sr, uint32_t frames, uint32_t* codes, hipStream_t s) {
+  const sdec_rvq_config& c = q->cfg;
+  const size_t level_cb = static_cast<size_t>(c.vq) * c.bins;
+  const size_t level_cand = static_cast<size_t>(c.max_frames) * q->groups;
+  const size_t res_half = static_cast<size_t>(c.max_frames) * c.vq;
+  for (uint32_t l = 0; l < c.nq; ++l) {
+    RvqLevelArgs a{};
+    a.cbT = q->cbT + l * level_cb;
+    a.cand_d = q->cand_d + l * level_cand;
+    a.cand_i = q->cand_i + l * level_cand;
+    a.codes = codes; a.nq = c.nq; a.bins = c.bins; a.vq = c.vq; a.groups = q->groups;
+    if (l == 0) {
+      a.r_in = r_first; a.r_stride = sf;
+    } else {
+      a.prev_cand_d = q->cand_d + (l - 1) * level_cand;
+      a.prev_cand_i = q->cand_i + (l - 1) * level_cand;
+      a.prev_level = l - 1;
+      a.r_out = q->res + (l % 2) * res_half;
+      if (l == 1) {  // the rest chain starts from the second projection
+        a.r_in = r_rest; a.r_stride = sr;
+      } else {       // SUB_EMB of the previous rest level's code
+        a.r_in = q->res + ((l - 1) % 2) * res_half; a.r_stride = c.vq;
+        a.prev_cb = q->w.cb_rest + static_cast<size_t>(l - 2) * c.bins * c.vq;
+      }
+    }
+    HIP_TRY(launch_rvq_level(a, frames, s));
+  }
+  RvqLevelArgs fin{};
+  fin.prev_cand_d = q->cand_d + (c.nq - 1) * level_cand;
+  fin.prev_cand_i = q->cand_i + (c.nq - 1) * level_cand;
+  fin.prev_level = c.nq - 1; fin.codes = codes; fin.nq = c.nq; fin.groups = q->groups;
+  HIP_TRY(launch_rvq_final(fin, frames, s));
+  return SDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdec_rvq_create(const sdec_rvq_config* cfg, const sdec_rvq_weights* w, sdec_rvq** out) {
+  g_err.clear();
+  if (!cfg || !w || !out) return fail(SDEC_E_ARG, "null argument");
+  const sdec_rvq_config c = *cfg;
+  if (c.dim == 0 || c.dim % 4) return fail(SDEC_E_ARG, "dim must be a positive multiple of 4");
+  if (c.vq == 0 || c.vq % 64 || c.vq > static_cast<uint32_t>(kRvqMaxVq))
+    return fail(SDEC_E_ARG, "vq must be a multiple of 64 in [64, %d]", kRvqMaxVq);
+  if (c.bins < 64 || c.bins % 64 || c.bins / 64 > 65535)
+    return fail(SDEC_E_ARG, "bins must be a multiple of 64, at least 64");
+  if (c.nq < 2) return fail(SDEC_E_ARG, "nq must be at least 2 (one first and one rest codebook)");
+  if (c.max_frames < 1 || c.max_frames > 65535)
+    return fail(SDEC_E_ARG, "max_frames must be in [1, 65535]");
+  const float* ptrs[] = {w->in_first, w->in_rest, w->out_first, w->out_rest, w->cb_first, w->cb_rest};
+  const char* names[] = {"in_first", "in_rest", "out_first", "out_rest", "cb_first", "cb_rest"};
+  for (int i = 0; i < 6; ++i)
+    if (!ptrs[i] || !aligned16(ptrs[i]))
+      return fail(SDEC_E_ARG, "%s must be a 16-byte aligned device pointer", names[i]);
+  sdec_rvq* q = new sdec_rvq();
+  q->cfg = c; q->w = *w; q->groups = c.bins / 64;
+  Alloc A;
+  const size_t level_cb = static_cast<size_t>(c.vq) * c.bins;
+  q->cbT = A.get<float>(level_cb * c.nq);
+  q->proj = A.get<float>(static_cast<size_t>(c.max_frames) * 2 * c.vq);
+  q->res = A.get<float>(static_cast<size_t>(2) * c.max_frames * c.vq);
+  q->cand_d = A.get<float>(static_cast<size_t>(c.nq) * c.max_frames * q->groups);
+  q->cand_i = A.get<uint32_t>(static_cast<size_t>(c.nq) * c.max_frames * q->groups);
+  q->acc = A.get<float>(static_cast<size_t>(c.max_frames) * 2 * c.vq);
+  if (A.code != SDEC_OK) {
+    for (void* p : A.ptrs) (void)hipFree(p);
+    delete q;
+    return A.code;
+  }
+  hipError_t e = launch_rvq_transpose(w->cb_first, q->cbT, 1, c.bins, c.vq, nullptr);
+  if (e == hipSuccess)
+    e = launch_rvq_transpose(w->cb_rest, q->cbT + level_cb, c.nq - 1, c.bins, c.vq, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    rvq_free(q);
+    delete q;
+    return fail(SDEC_E_HIP, "codebook transpose: %s", hipGetErrorString(e));
+  }
+  *out = q;
+  return SDEC_OK;
+}
+
+int sdec_rvq_quantise(sdec_rvq* q, const float* r_first, const float* r_rest, uint32_t frames,
+                      uint32_t* codes, void* stream) {
+  int r = rvq_check_frames(q, frames);
+  if (r != SDEC_OK) return r;
+  if (!r_first || !r_rest || !codes) return fail(SDEC_E_ARG, "null device pointer");
+  return rvq_quantise_levels(q, r_first, q->cfg.vq, r_rest, q->cfg.vq, frames, codes,
+                             static_cast<hipStream_t>(stream));
+}
+
+int sdec_rvq_encode(sdec_rvq* q, const float* latent, uint32_t frames, uint32_t* codes,
+                    void* stream) {
+  int r = rvq_check_frames(q, frames);
+  if (r != SDEC_OK) return r;
+  if (!latent || !aligned16(latent) || !codes)
+    return fail(SDEC_E_ARG, "latent (16-byte aligned) and codes must be device pointers");
+  const sdec_rvq_config& c = q->cfg;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  r = rvq_row_blocks(frames, [&](uint32_t f0, uint32_t n) -> int {
+    GemvArgs g{};
+    g.w[0] = q->w.in_first; g.w[1] = q->w.in_rest; g.w[2] = q->w.in_rest;
+    g.seg_end[0] = c.vq; g.seg_end[1] = 2 * c.vq; g.seg_end[2] = 2 * c.vq;
+    g.n_rows = 2 * c.vq; g.k = c.dim; g.m = n;
+    g.x = latent + static_cast<size_t>(f0) * c.dim; g.x_stride = c.dim;
+    g.y = q->proj + static_cast<size_t>(f0) * 2 * c.vq; g.y_stride = 2 * c.vq;
+    HIP_TRY(launch_gemv(g, plan_gemv(PRO_NONE, EPI_STORE, 2 * c.vq, c.dim, n), s));
+    return SDEC_OK;
+  });
+  if (r != SDEC_OK) return r;
+  return rvq_quantise_levels(q, q->proj, 2 * c.vq, q->proj + c.vq, 2 * c.vq, frames, codes, s);
+}
+
+int sdec_rvq_decode(sdec_rvq* q, const uint32_t* codes, uint32_t frames, float* latent,
+                    void* stream) {
+  int r = rvq_check_frames(q, frames);
+  if (r != SDEC_OK) return r;
+  if (!latent || !aligned16(latent) || !codes)
+    return fail(SDEC_E_ARG, "codes and latent (16-byte aligned) must be device pointers");
+  const sdec_rvq_config& c = q->cfg;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RvqEmbArgs e{};
+  e.codes = codes; e.cb_first = q->w.cb_first; e.cb_rest = q->w.cb_rest; e.acc = q->acc;
+  e.nq = c.nq; e.bins = c.bins; e.vq = c.vq;
+  HIP_TRY(launch_rvq_emb_sum(e, frames, s));
+  return rvq_row_blocks(frames, [&](uint32_t f0, uint32_t n) -> int {
+    float* y = latent + static_cast<size_t>(f0) * c.dim;
+    const float* acc = q->acc + static_cast<size_t>(f0) * 2 * c.vq;
+    GemvArgs g{};
+    g.w[0] = g.w[1] = g.w[2] = q->w.out_first;
+    g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = c.dim;
+    g.n_rows = c.dim; g.k = c.vq; g.m = n; g.x = acc; g.x_stride = 2 * c.vq;
+    g.y = y; g.y_stride = c.dim;
+    HIP_TRY(launch_gemv(g, plan_gemv(PRO_NONE, EPI_STORE, c.dim, c.vq, n), s));
+    GemvArgs h{};  // the second projection accumulates into the first ([mimi] decode plan)
+    h.w[0] = h.w[1] = h.w[2] = q->w.out_rest;
+    h.seg_end[0] = h.seg_end[1] = h.seg_end[2] = c.dim;
+    h.n_rows = c.dim; h.k = c.vq; h.m = n; h.x = acc + c.vq; h.x_stride = 2 * c.vq;
+    h.res = y; h.res_stride = c.dim;
+    HIP_TRY(launch_gemv(h, plan_gemv(PRO_NONE, EPI_RESIDUAL, c.dim, c.vq, n), s));
+    return SDEC_OK;
+  });
+}
+
+void sdec_rvq_destroy(sdec_rvq* q) {
+  if (!q) return;
+  (void)hipDeviceSynchronize();
+  rvq_free(q);
+  delete q;
+}
+
+}  // extern "C"

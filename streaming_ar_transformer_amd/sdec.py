@@ -23,7 +23,9 @@ K_NAMES = ["begin", "qkv", "attention", "o_proj", "ffn_up", "ffn_down", "end"]
 # Every symbol include/sdec.h declares.
 EXPORTS = ["sdec_create", "sdec_step", "sdec_reset", "sdec_destroy", "sdec_last_error",
            "sdec_kv_view", "sdec_set_next_position", "sdec_tap_view", "sdec_step_profile",
-           "sdec_gemv", "sdec_ring_attention", "sdec_status", "sdec_step_trace", "sdec_prefill"]
+           "sdec_gemv", "sdec_ring_attention", "sdec_status", "sdec_step_trace", "sdec_prefill",
+           "sdec_rvq_create", "sdec_rvq_encode", "sdec_rvq_quantise", "sdec_rvq_decode",
+           "sdec_rvq_destroy"]
 
 
 class SdecError(RuntimeError):
@@ -55,6 +57,18 @@ class LayerWeights(ctypes.Structure):
 
 class FinalWeights(ctypes.Structure):
     _fields_ = [("norm_w", ctypes.c_void_p), ("norm_b", ctypes.c_void_p)]
+
+
+class RVQConfig(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_uint32), ("vq", ctypes.c_uint32), ("bins", ctypes.c_uint32),
+                ("nq", ctypes.c_uint32), ("max_frames", ctypes.c_uint32)]
+
+
+_RVQ_FIELDS = ["in_first", "in_rest", "out_first", "out_rest", "cb_first", "cb_rest"]
+
+
+class RVQWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _RVQ_FIELDS]
 
 
 _lib = None
@@ -89,6 +103,12 @@ def lib():
                                       ctypes.POINTER(ctypes.c_double)]),
             "sdec_ring_attention": (i32, [vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, u32, u32,
                                           vp]),
+            "sdec_rvq_create": (i32, [ctypes.POINTER(RVQConfig), ctypes.POINTER(RVQWeights),
+                                      ctypes.POINTER(vp)]),
+            "sdec_rvq_encode": (i32, [vp, vp, u32, vp, vp]),
+            "sdec_rvq_quantise": (i32, [vp, vp, vp, u32, vp, vp]),
+            "sdec_rvq_decode": (i32, [vp, vp, u32, vp, vp]),
+            "sdec_rvq_destroy": (None, [vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -283,3 +303,46 @@ def copy_to_device(ptr: int, arr):
                        ctypes.c_size_t(arr.nbytes), 1)  # hipMemcpyHostToDevice
     if rc != 0:
         raise RuntimeError(f"hipMemcpy H2D failed: {rc}")
+
+
+class RVQ:
+    """Split RVQ behind ``sdec_rvq_*``.  ``weights`` maps the ``sdec_rvq_weights`` names to
+    device float32 tensors (borrowed: this object keeps references); codes are int32 tensors
+    ``[frames, nq]`` holding the uint32 codes."""
+
+    def __init__(self, dim, vq, bins, nq, max_frames, weights):
+        self.c = RVQConfig(dim, vq, bins, nq, max_frames)
+        self._keep = weights
+        w = RVQWeights()
+        for n in _RVQ_FIELDS:
+            setattr(w, n, _ptr(weights[n]))
+        h = ctypes.c_void_p()
+        _check(lib().sdec_rvq_create(ctypes.byref(self.c), ctypes.byref(w), ctypes.byref(h)))
+        self.h = h
+
+    def encode(self, latent, codes, stream=None):
+        _check(lib().sdec_rvq_encode(self.h, _ptr(latent), int(latent.shape[0]), _ptr(codes),
+                                     _stream(stream)))
+        return codes
+
+    def quantise(self, r_first, r_rest, codes, stream=None):
+        _check(lib().sdec_rvq_quantise(self.h, _ptr(r_first), _ptr(r_rest),
+                                       int(r_first.shape[0]), _ptr(codes), _stream(stream)))
+        return codes
+
+    def decode(self, codes, latent, stream=None):
+        _check(lib().sdec_rvq_decode(self.h, _ptr(codes), int(codes.shape[0]), _ptr(latent),
+                                     _stream(stream)))
+        return latent
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().sdec_rvq_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+

@@ -38,6 +38,8 @@ def test_struct_layout_matches_header(tmp_path):
         "sdec_config": [f for f, _ in sdec.Config._fields_],
         "sdec_layer_weights": [f for f, _ in sdec.LayerWeights._fields_],
         "sdec_final_weights": [f for f, _ in sdec.FinalWeights._fields_],
+        "sdec_rvq_config": [f for f, _ in sdec.RVQConfig._fields_],
+        "sdec_rvq_weights": [f for f, _ in sdec.RVQWeights._fields_],
     }
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "sdec.h"', "int main(void){"]
     for st, fs in fields.items():
@@ -53,7 +55,8 @@ def test_struct_layout_matches_header(tmp_path):
     got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True,
                                                  text=True).stdout.splitlines())
     for st, cls in (("sdec_config", sdec.Config), ("sdec_layer_weights", sdec.LayerWeights),
-                    ("sdec_final_weights", sdec.FinalWeights)):
+                    ("sdec_final_weights", sdec.FinalWeights), ("sdec_rvq_config", sdec.RVQConfig),
+                    ("sdec_rvq_weights", sdec.RVQWeights)):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f, _ in cls._fields_:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, f"{st}.{f}"
@@ -121,6 +124,26 @@ def test_prefill_needs_one_stream():
     rc, err = _create(c, arr, cfg.ring)
     assert rc == sdec.E_ARG and "one stream" in err
     assert sdec.lib().sdec_prefill(None, 16, 0, 1, 1, None) == sdec.E_ARG
+
+
+def test_rvq_rejects_bad_config():
+    L = sdec.lib()
+    w = sdec.RVQWeights(*[0x10000 + 256 * i for i in range(6)])
+    for kw, msg in ((dict(vq=100), "vq"), (dict(bins=100), "bins"), (dict(nq=1), "nq"),
+                    (dict(dim=6), "dim"), (dict(max_frames=0), "max_frames")):
+        c = dict(dim=512, vq=256, bins=2048, nq=8, max_frames=4)
+        c.update(kw)
+        h = ctypes.c_void_p()
+        rc = L.sdec_rvq_create(ctypes.byref(sdec.RVQConfig(**c)), ctypes.byref(w), ctypes.byref(h))
+        assert rc == sdec.E_ARG and msg in L.sdec_last_error().decode()
+    w.cb_rest = 0x10004
+    h = ctypes.c_void_p()
+    rc = L.sdec_rvq_create(ctypes.byref(sdec.RVQConfig(512, 256, 2048, 8, 4)), ctypes.byref(w),
+                           ctypes.byref(h))
+    assert rc == sdec.E_ARG and "cb_rest" in L.sdec_last_error().decode()
+    assert L.sdec_rvq_encode(None, 16, 1, 32, None) == sdec.E_ARG
+    assert L.sdec_rvq_decode(None, 16, 1, 32, None) == sdec.E_ARG
+    L.sdec_rvq_destroy(None)
 
 
 def test_one_shot_entry_points_reject_bad_arguments():
