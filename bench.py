@@ -49,6 +49,8 @@ def parse():
                     help="timed prefill calls, positions from 0")
     ap.add_argument("--no-variant", action="store_true",
                     help="skip the FlowLM-variant measurement (workload 6)")
+    ap.add_argument("--no-rvq", action="store_true",
+                    help="skip the split-RVQ measurement (64 frames, 8 codebooks of 2048 bins)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes three times (the "
                          "known-size kernel that calibrates HBM byte counters)")
@@ -315,6 +317,44 @@ def main():
         print(f"{vcfg.name}: {vms * 1e3:.1f} us/step, {vgbs:.0f} GB/s", file=sys.stderr, flush=True)
         vdec.close()
 
+    # split RVQ: encode and decode of a batch of latent frames
+    rvq = None
+    if not args.no_rvq and args.config == 4:
+        rc = wl.RVQ_CONFIGS[1]
+        R = wl.make_rvq(rc)
+        dev = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in R.items()
+               if k != "latents"}
+        lat = torch.from_numpy(R["latents"]).cuda()
+        q = sdec.RVQ(rc.dim, rc.vq, rc.bins, rc.nq, rc.frames, dev)
+        codes = torch.empty((rc.frames, rc.nq), dtype=torch.int32, device="cuda")
+        out = torch.empty((rc.frames, rc.dim), device="cuda")
+        reps = 20
+        for _ in range(3):
+            q.encode(lat, codes, stream=stream)
+            q.decode(codes, out, stream=stream)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(reps):
+            q.encode(lat, codes, stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        enc_ms = start.elapsed_time(end) / reps
+        start.record(stream)
+        for _ in range(reps):
+            q.decode(codes, out, stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = start.elapsed_time(end) / reps
+        cb_bytes = 4 * rc.nq * rc.bins * rc.vq
+        rvq = {"workload": rc.name, "frames": rc.frames,
+               "encode_ms": round(enc_ms, 4), "encode_frames_per_s": round(rc.frames * 1e3 / enc_ms, 1),
+               "decode_ms": round(dec_ms, 4), "decode_frames_per_s": round(rc.frames * 1e3 / dec_ms, 1),
+               "codebook_bytes": cb_bytes,
+               "encode_codebook_gbs": round(cb_bytes / (enc_ms * 1e-3) / 1e9, 1)}
+        print(f"{rc.name}: encode {enc_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us per "
+              f"{rc.frames} frames", file=sys.stderr, flush=True)
+        q.close()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, layers, final, xs_host, args.cpu_seconds)
@@ -332,6 +372,7 @@ def main():
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": int(bytes_avg),
         "roofline": roofline, "eager_kernels": kernels, "prefill": prefill, "variant": variant,
+        "rvq": rvq,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
