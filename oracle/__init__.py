@@ -10,3 +10,6 @@ from .step import (  # noqa: F401
     rope_pairs, seq_sum, silu_mul, valid_slots,
 )
 from .rvq import OracleRVQ, emb_sum, nearest, sq_distances  # noqa: F401,E402
+from .conv import (  # noqa: F401,E402
+    causal_conv1d, conv_transpose1d_full, elu, streamed_conv_transpose1d,
+)

@@ -566,3 +566,57 @@ def test_rvq_workload_margins_exceed_rounding():
         _, margins = q.quantise(*q.project(R["latents"][f]))
         for best, second in margins:
             assert (second - best) / best > 1e-6
+
+
+# ---------------------------------------------------------------------------------------------
+# streaming codec convolutions, offline ([mimi] CONV1D, convtr_src, ELU_IP, REPLICATE)
+# ---------------------------------------------------------------------------------------------
+
+def test_elu_closed_forms():
+    v = np.array([0.0, 1.0, -1.0, -50.0, 3.5], F32)
+    np.testing.assert_array_equal(oracle.elu(v)[[0, 1, 4]], v[[0, 1, 4]])
+    assert oracle.elu(v)[2] == F32(math.exp(-1.0) - 1.0)
+    assert oracle.elu(v)[3] == F32(-1.0)
+
+
+@pytest.mark.parametrize("stride,k,groups,replicate,pre_elu", [
+    (1, 7, 1, False, False), (2, 4, 1, True, False), (1, 3, 1, False, True),
+    (4, 8, 1, True, True), (1, 5, 6, False, False),
+])
+def test_causal_conv1d_is_the_library_convolution(stride, k, groups, replicate, pre_elu):
+    torch = pytest.importorskip("torch")
+    torch_f = torch.nn.functional
+    rng = np.random.default_rng(40 + k)
+    cin, cout, T = 6, 6 if groups > 1 else 5, 24
+    x = rng.standard_normal((cin, T)).astype(F32)
+    w = rng.standard_normal((cout, cin // groups, k)).astype(F32)
+    b = rng.standard_normal(cout).astype(F32)
+    y = oracle.causal_conv1d(x, w, b, stride, replicate=replicate, pre_elu=pre_elu, groups=groups)
+    xt = torch.from_numpy(x)[None].double()
+    xt = torch_f.pad(xt, (k - stride, 0), mode="replicate" if replicate else "constant")
+    if pre_elu:
+        xt = torch_f.elu(xt)
+    ref = torch_f.conv1d(xt, torch.from_numpy(w).double(), torch.from_numpy(b).double(),
+                         stride=stride, groups=groups)[0].numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("stride,k,groups,pre_elu", [(4, 8, 1, False), (2, 4, 6, True),
+                                                     (3, 3, 1, True), (16, 32, 6, False)])
+def test_conv_transpose1d_is_the_library_convolution(stride, k, groups, pre_elu):
+    torch = pytest.importorskip("torch")
+    torch_f = torch.nn.functional
+    rng = np.random.default_rng(50 + k)
+    cin, T = 6, 5
+    cout = cin if groups > 1 else 4
+    x = rng.standard_normal((cin, T)).astype(F32)
+    w = rng.standard_normal((cin, cout // groups, k)).astype(F32)
+    b = rng.standard_normal(cout).astype(F32)
+    y = oracle.conv_transpose1d_full(x, w, b, stride, pre_elu=pre_elu, groups=groups)
+    xt = torch.from_numpy(x)[None].double()
+    if pre_elu:
+        xt = torch_f.elu(xt)
+    ref = torch_f.conv_transpose1d(xt, torch.from_numpy(w).double(), torch.from_numpy(b).double(),
+                                   stride=stride, groups=groups)[0].numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-6, atol=1e-6)
+    assert oracle.streamed_conv_transpose1d(x, w, b, stride, pre_elu, groups).shape == (cout, T * stride)
