@@ -256,6 +256,42 @@ int sdec_rvq_decode(sdec_rvq* q, const uint32_t* codes, uint32_t frames, float* 
 /* Release the buffers the library owns (synchronizes the device first).  NULL is accepted. */
 void sdec_rvq_destroy(sdec_rvq* q);
 
+/* Streaming codec convolution ([mimi] inferencelayer 0.2.1, src/mimi_gpu.rs: CONV1D with the
+ * input prefix carried between frames by WRITE_XA / CARRY (REPLICATE on the first frame), and
+ * the gather-form transposed conv of convtr_src whose overlap tail TRP_ADD / TR_OUT / TR_CARRY
+ * carry bias-subtracted; the ELU of ELU_IP can be folded into the input reads).  Frames are fed
+ * one at a time; concatenated, the outputs equal the offline convolution of the concatenated
+ * input:
+ *   conv (transposed == 0): the input is left-padded by kernel - stride columns (zeros, or
+ *     copies of the first column when replicate_first), y[o][t] = b[o] + sum_{i,k}
+ *     w[o][i][k] * f(xp[i][t*stride + k]) with w [out_ch][in_ch/groups][kernel]; a frame of
+ *     t_in columns (a multiple of stride) gives t_in/stride columns; accumulate adds them to y.
+ *   transposed conv: w [in_ch][out_ch/groups][kernel]; a frame of t_in columns gives
+ *     t_in*stride columns, the first ones of the full transposed convolution not yet emitted
+ *     (the last kernel - stride wait for the next frame's overlap).
+ * f is ELU (v > 0 ? v : exp(v) - 1) when pre_elu, else the identity.  groups is 1 or
+ * in_ch == out_ch (channel-wise).  kernel >= stride >= 1.  Weights are borrowed device pointers.
+ * x is device [in_ch][t_in], y device [out_ch][t_out] (channel-major, as the pages' buffers). */
+typedef struct sdec_conv_config {
+  uint32_t in_ch;
+  uint32_t out_ch;
+  uint32_t kernel;
+  uint32_t stride;
+  uint32_t groups;
+  uint32_t transposed;
+  uint32_t pre_elu;
+  uint32_t replicate_first; /* conv only */
+  uint32_t accumulate;      /* conv only: y += conv(x) */
+  uint32_t max_t_in;        /* largest frame, in input columns */
+} sdec_conv_config;
+typedef struct sdec_conv sdec_conv;
+int sdec_conv_create(const sdec_conv_config* cfg, const float* w, const float* b, sdec_conv** out);
+/* One frame.  first != 0 starts a fresh stream (the carried state is ignored).  Asynchronous. */
+int sdec_conv_step(sdec_conv* c, const float* x, uint32_t t_in, float* y, uint32_t first,
+                   void* stream);
+/* Release the state buffers (synchronizes the device first).  NULL is accepted. */
+void sdec_conv_destroy(sdec_conv* c);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,7 +6,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsdec.so")
-SOURCES = [os.path.join(PKG, "csrc", n) for n in ("kernels.hip", "step.hip", "rvq.hip", "sdec.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", n) for n in ("kernels.hip", "step.hip", "rvq.hip", "conv.hip", "sdec.cpp")]
 ARCH = os.environ.get("SDEC_OFFLOAD_ARCH", "gfx950")
 
 

@@ -190,6 +190,30 @@ hipError_t launch_rvq_level(const RvqLevelArgs& a, uint32_t frames, hipStream_t 
 hipError_t launch_rvq_final(const RvqLevelArgs& a, uint32_t frames, hipStream_t s);
 hipError_t launch_rvq_emb_sum(const RvqEmbArgs& a, uint32_t frames, hipStream_t s);
 
+// Streaming codec convolutions (conv.hip; [mimi] CONV1D, convtr_src, the prefix and tail carries).
+struct SConvArgs {
+  const float* w;          // [c_out][c_in / groups][k]
+  const float* b;          // [c_out]
+  const float* x;          // [c_in][t_in] this frame
+  const float* prefix;     // [c_in][pad] carried input columns (pad = k - stride)
+  float* prefix_out;       // [c_in][pad] the next frame's prefix
+  float* y;                // [c_out][t_in / stride]
+  uint32_t c_in, c_out, k, stride, groups, t_in, pad;
+  int pre_elu, replicate_first, first, accumulate;
+};
+hipError_t launch_sconv(const SConvArgs& a, hipStream_t s);
+struct SConvTrArgs {
+  const float* w;          // [c_in][c_out / groups][k]
+  const float* b;          // [c_out]
+  const float* x;          // [c_in][t_in]
+  const float* tail;       // [c_out][tl] carried pending columns, bias subtracted (tl = k - stride)
+  float* tail_out;         // [c_out][tl]
+  float* y;                // [c_out][t_in * stride]
+  uint32_t c_in, c_out, k, stride, groups, t_in, tl;
+  int pre_elu, first;
+};
+hipError_t launch_sconvtr(const SConvTrArgs& a, hipStream_t s);
+
 // Persistent step kernel (step.hip): one cooperative launch per step for a single stream.
 struct StepLayer {
   const float *attn_norm_w, *attn_norm_b, *wq, *wk, *wv, *wo, *q_norm, *k_norm, *ls1;

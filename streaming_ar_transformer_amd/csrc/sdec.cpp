@@ -1090,3 +1090,87 @@ void sdec_rvq_destroy(sdec_rvq* q) {
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------------------------------------
+// Streaming codec convolutions ([mimi] CONV1D, convtr_src and their carries).
+// ------------------------------------------------------------------------------------------------
+struct sdec_conv {
+  sdec_conv_config cfg{};
+  const float* w = nullptr;
+  const float* b = nullptr;
+  float* state[2] = {nullptr, nullptr};  // prefix [in_ch][k - s] or tail [out_ch][k - s]
+  int cur = 0;
+  bool started = false;
+};
+
+extern "C" {
+
+int sdec_conv_create(const sdec_conv_config* cfg, const float* w, const float* b, sdec_conv** out) {
+  g_err.clear();
+  if (!cfg || !out) return fail(SDEC_E_ARG, "null argument");
+  const sdec_conv_config c = *cfg;
+  if (!w || !b) return fail(SDEC_E_ARG, "w and b must be device pointers");
+  if (c.in_ch < 1 || c.out_ch < 1 || c.out_ch > 65535)
+    return fail(SDEC_E_ARG, "channels must be in [1, 65535]");
+  if (c.stride < 1 || c.kernel < c.stride) return fail(SDEC_E_ARG, "need kernel >= stride >= 1");
+  if (!(c.groups == 1 || (c.groups == c.in_ch && c.in_ch == c.out_ch)))
+    return fail(SDEC_E_ARG, "groups must be 1 or in_ch == out_ch (channel-wise)");
+  if (c.max_t_in < 1) return fail(SDEC_E_ARG, "max_t_in must be >= 1");
+  if (c.transposed && (c.replicate_first || c.accumulate))
+    return fail(SDEC_E_ARG, "replicate_first and accumulate apply to the forward conv only");
+  sdec_conv* h = new sdec_conv();
+  h->cfg = c; h->w = w; h->b = b;
+  const size_t n = static_cast<size_t>(c.transposed ? c.out_ch : c.in_ch) * (c.kernel - c.stride);
+  Alloc A;
+  h->state[0] = A.get<float>(n);
+  h->state[1] = A.get<float>(n);
+  if (A.code != SDEC_OK) {
+    for (void* p : A.ptrs) (void)hipFree(p);
+    delete h;
+    return A.code;
+  }
+  *out = h;
+  return SDEC_OK;
+}
+
+int sdec_conv_step(sdec_conv* h, const float* x, uint32_t t_in, float* y, uint32_t first,
+                   void* stream) {
+  if (!h) return fail(SDEC_E_ARG, "null conv handle");
+  const sdec_conv_config& c = h->cfg;
+  if (!x || !y) return fail(SDEC_E_ARG, "x and y must be device pointers");
+  if (t_in < 1 || t_in > c.max_t_in)
+    return fail(SDEC_E_ARG, "t_in=%u must be in [1, max_t_in=%u]", t_in, c.max_t_in);
+  if (!first && !h->started) return fail(SDEC_E_POS, "the first frame of a stream needs first != 0");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t carry = c.kernel - c.stride;
+  if (c.transposed) {
+    SConvTrArgs a{};
+    a.w = h->w; a.b = h->b; a.x = x; a.tail = h->state[h->cur]; a.tail_out = h->state[h->cur ^ 1];
+    a.y = y; a.c_in = c.in_ch; a.c_out = c.out_ch; a.k = c.kernel; a.stride = c.stride;
+    a.groups = c.groups; a.t_in = t_in; a.tl = carry; a.pre_elu = c.pre_elu ? 1 : 0;
+    a.first = first ? 1 : 0;
+    HIP_TRY(launch_sconvtr(a, s));
+  } else {
+    if (t_in % c.stride) return fail(SDEC_E_ARG, "t_in=%u is not a multiple of stride %u", t_in, c.stride);
+    SConvArgs a{};
+    a.w = h->w; a.b = h->b; a.x = x; a.prefix = h->state[h->cur]; a.prefix_out = h->state[h->cur ^ 1];
+    a.y = y; a.c_in = c.in_ch; a.c_out = c.out_ch; a.k = c.kernel; a.stride = c.stride;
+    a.groups = c.groups; a.t_in = t_in; a.pad = carry; a.pre_elu = c.pre_elu ? 1 : 0;
+    a.replicate_first = c.replicate_first ? 1 : 0; a.first = first ? 1 : 0;
+    a.accumulate = c.accumulate ? 1 : 0;
+    HIP_TRY(launch_sconv(a, s));
+  }
+  h->cur ^= 1;
+  h->started = true;
+  return SDEC_OK;
+}
+
+void sdec_conv_destroy(sdec_conv* h) {
+  if (!h) return;
+  (void)hipDeviceSynchronize();
+  for (float* p : h->state)
+    if (p) (void)hipFree(p);
+  delete h;
+}
+
+}  // extern "C"

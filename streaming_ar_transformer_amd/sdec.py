@@ -25,7 +25,7 @@ EXPORTS = ["sdec_create", "sdec_step", "sdec_reset", "sdec_destroy", "sdec_last_
            "sdec_kv_view", "sdec_set_next_position", "sdec_tap_view", "sdec_step_profile",
            "sdec_gemv", "sdec_ring_attention", "sdec_status", "sdec_step_trace", "sdec_prefill",
            "sdec_rvq_create", "sdec_rvq_encode", "sdec_rvq_quantise", "sdec_rvq_decode",
-           "sdec_rvq_destroy"]
+           "sdec_rvq_destroy", "sdec_conv_create", "sdec_conv_step", "sdec_conv_destroy"]
 
 
 class SdecError(RuntimeError):
@@ -71,6 +71,12 @@ class RVQWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _RVQ_FIELDS]
 
 
+class ConvConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in ("in_ch", "out_ch", "kernel", "stride", "groups",
+                                               "transposed", "pre_elu", "replicate_first",
+                                               "accumulate", "max_t_in")]
+
+
 _lib = None
 
 
@@ -109,6 +115,9 @@ def lib():
             "sdec_rvq_quantise": (i32, [vp, vp, vp, u32, vp, vp]),
             "sdec_rvq_decode": (i32, [vp, vp, u32, vp, vp]),
             "sdec_rvq_destroy": (None, [vp]),
+            "sdec_conv_create": (i32, [ctypes.POINTER(ConvConfig), vp, vp, ctypes.POINTER(vp)]),
+            "sdec_conv_step": (i32, [vp, vp, u32, vp, u32, vp]),
+            "sdec_conv_destroy": (None, [vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -338,6 +347,46 @@ class RVQ:
     def close(self):
         if getattr(self, "h", None):
             lib().sdec_rvq_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class StreamConv:
+    """One streaming (transposed) conv behind ``sdec_conv_*``: ``w`` and ``b`` are device float32
+    tensors (borrowed); frames are device ``[in_ch, t_in]`` tensors."""
+
+    def __init__(self, w, b, stride, transposed=False, groups=1, pre_elu=False,
+                 replicate_first=False, accumulate=False, max_t_in=1024):
+        if transposed:
+            in_ch, opg, k = w.shape
+            out_ch = opg * groups
+        else:
+            out_ch, ipg, k = w.shape
+            in_ch = ipg * groups
+        self.c = ConvConfig(in_ch, out_ch, k, stride, groups, int(transposed), int(pre_elu),
+                            int(replicate_first), int(accumulate), max_t_in)
+        self._keep = (w, b)
+        self.stride, self.transposed, self.out_ch = stride, transposed, out_ch
+        h = ctypes.c_void_p()
+        _check(lib().sdec_conv_create(ctypes.byref(self.c), _ptr(w), _ptr(b), ctypes.byref(h)))
+        self.h = h
+
+    def out_cols(self, t_in: int) -> int:
+        return t_in * self.stride if self.transposed else t_in // self.stride
+
+    def step(self, x, y, first=False, stream=None):
+        _check(lib().sdec_conv_step(self.h, _ptr(x), int(x.shape[1]), _ptr(y), int(bool(first)),
+                                    _stream(stream)))
+        return y
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().sdec_conv_destroy(self.h)
             self.h = None
 
     def __del__(self):

@@ -40,6 +40,7 @@ def test_struct_layout_matches_header(tmp_path):
         "sdec_final_weights": [f for f, _ in sdec.FinalWeights._fields_],
         "sdec_rvq_config": [f for f, _ in sdec.RVQConfig._fields_],
         "sdec_rvq_weights": [f for f, _ in sdec.RVQWeights._fields_],
+        "sdec_conv_config": [f for f, _ in sdec.ConvConfig._fields_],
     }
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "sdec.h"', "int main(void){"]
     for st, fs in fields.items():
@@ -56,7 +57,7 @@ def test_struct_layout_matches_header(tmp_path):
                                                  text=True).stdout.splitlines())
     for st, cls in (("sdec_config", sdec.Config), ("sdec_layer_weights", sdec.LayerWeights),
                     ("sdec_final_weights", sdec.FinalWeights), ("sdec_rvq_config", sdec.RVQConfig),
-                    ("sdec_rvq_weights", sdec.RVQWeights)):
+                    ("sdec_rvq_weights", sdec.RVQWeights), ("sdec_conv_config", sdec.ConvConfig)):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f, _ in cls._fields_:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, f"{st}.{f}"
@@ -144,6 +145,22 @@ def test_rvq_rejects_bad_config():
     assert L.sdec_rvq_encode(None, 16, 1, 32, None) == sdec.E_ARG
     assert L.sdec_rvq_decode(None, 16, 1, 32, None) == sdec.E_ARG
     L.sdec_rvq_destroy(None)
+
+
+def test_conv_rejects_bad_config():
+    L = sdec.lib()
+    base = dict(in_ch=8, out_ch=8, kernel=4, stride=2, groups=1, transposed=0, pre_elu=0,
+                replicate_first=0, accumulate=0, max_t_in=16)
+    for kw, msg in ((dict(kernel=1), "kernel >= stride"), (dict(groups=4), "groups"),
+                    (dict(max_t_in=0), "max_t_in"), (dict(transposed=1, accumulate=1), "forward"),
+                    (dict(out_ch=0), "channels")):
+        c = dict(base)
+        c.update(kw)
+        h = ctypes.c_void_p()
+        rc = L.sdec_conv_create(ctypes.byref(sdec.ConvConfig(**c)), 16, 32, ctypes.byref(h))
+        assert rc == sdec.E_ARG and msg in L.sdec_last_error().decode()
+    assert L.sdec_conv_step(None, 16, 4, 32, 1, None) == sdec.E_ARG
+    L.sdec_conv_destroy(None)
 
 
 def test_one_shot_entry_points_reject_bad_arguments():
