@@ -27,13 +27,23 @@ def elu(v: np.ndarray) -> np.ndarray:
     return np.where(v > 0, v, (np.exp(v.astype(np.float64)) - 1.0).astype(F32)).astype(F32)
 
 
+def _group_matmul(w_k: np.ndarray, x: np.ndarray, groups: int) -> np.ndarray:
+    """``out[o] = sum_i w_k[o, i] * x[g(o) * ipg + i]`` for one kernel tap (float64)."""
+    c_out, ipg = w_k.shape
+    opg = c_out // groups
+    out = np.empty((c_out, x.shape[1]), np.float64)
+    for g in range(groups):
+        out[g * opg:(g + 1) * opg] = w_k[g * opg:(g + 1) * opg] @ x[g * ipg:(g + 1) * ipg]
+    return out
+
+
 def causal_conv1d(x, w, b, stride: int, replicate: bool = False, pre_elu: bool = False,
                   groups: int = 1) -> np.ndarray:
     """Offline causal conv: the input is left-padded by ``K - stride`` columns (zeros, or copies
     of the first sample: [mimi] ``REPLICATE``), then ``y[o, t] = b[o] + sum_{i, k}
     w[o, i, k] * f(xp[i, t*stride + k])`` with f = ELU when ``pre_elu`` (applied to every read
-    value, padding included).  ``T`` must be a multiple of ``stride``.  Sums in float64, rounded
-    once to float32."""
+    value, padding included).  ``T`` must be a multiple of ``stride``.  One matrix product per
+    kernel tap, in float64, rounded once to float32."""
     x = np.asarray(x, F32)
     w = np.asarray(w, F32)
     c_in, T = x.shape
@@ -46,13 +56,10 @@ def causal_conv1d(x, w, b, stride: int, replicate: bool = False, pre_elu: bool =
         xp = elu(xp)
     xp = xp.astype(np.float64)
     t_out = T // stride
-    y = np.zeros((c_out, t_out), np.float64)
-    opg = c_out // groups
-    for o in range(c_out):
-        g = o // opg
-        for t in range(t_out):
-            win = xp[g * ipg:(g + 1) * ipg, t * stride:t * stride + K]
-            y[o, t] = float(b[o]) + float(np.sum(w[o].astype(np.float64) * win))
+    y = np.repeat(np.asarray(b, np.float64)[:, None], t_out, axis=1)
+    for k in range(K):
+        cols = xp[:, k:k + (t_out - 1) * stride + 1:stride]  # xp[:, t*stride + k] for every t
+        y += _group_matmul(w[:, :, k].astype(np.float64), cols, groups)
     return y.astype(F32)
 
 
@@ -60,7 +67,8 @@ def conv_transpose1d_full(x, w, b, stride: int, pre_elu: bool = False,
                           groups: int = 1) -> np.ndarray:
     """Offline transposed conv, all ``(T - 1) * stride + K`` output columns:
     ``y[o, t*stride + k] += w[i, o', k] * f(x[i, t])`` over the input channels i of o's group
-    (o' = o within the group), plus ``b[o]``.  Sums in float64, rounded once."""
+    (o' = o within the group), plus ``b[o]``.  One matrix product per kernel tap, in float64,
+    rounded once."""
     x = np.asarray(x, F32)
     w = np.asarray(w, F32)
     if pre_elu:
@@ -70,14 +78,14 @@ def conv_transpose1d_full(x, w, b, stride: int, pre_elu: bool = False,
     c_out = opg * groups
     ipg = c_in // groups
     L = (T - 1) * stride + K
-    y = np.zeros((c_out, L), np.float64)
-    for i in range(c_in):
-        g = i // ipg
-        for oo in range(opg):
-            o = g * opg + oo
-            for t in range(T):
-                y[o, t * stride:t * stride + K] += w[i, oo].astype(np.float64) * float(x[i, t])
-    y += np.asarray(b, np.float64)[:, None]
+    y = np.repeat(np.asarray(b, np.float64)[:, None], L, axis=1)
+    x64 = x.astype(np.float64)
+    for k in range(K):
+        # tap k of input column t lands on output column t*stride + k
+        wk = np.empty((c_out, ipg), np.float64)
+        for g in range(groups):
+            wk[g * opg:(g + 1) * opg] = w[g * ipg:(g + 1) * ipg, :, k].astype(np.float64).T
+        y[:, k:k + (T - 1) * stride + 1:stride] += _group_matmul(wk, x64, groups)
     return y.astype(F32)
 
 
