@@ -51,6 +51,8 @@ def parse():
                     help="skip the FlowLM-variant measurement (workload 6)")
     ap.add_argument("--no-rvq", action="store_true",
                     help="skip the split-RVQ measurement (64 frames, 8 codebooks of 2048 bins)")
+    ap.add_argument("--no-seanet", action="store_true",
+                    help="skip the streaming SEANet-decoder measurement")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes three times (the "
                          "known-size kernel that calibrates HBM byte counters)")
@@ -355,6 +357,31 @@ def main():
               f"{rc.frames} frames", file=sys.stderr, flush=True)
         q.close()
 
+    # streaming SEANet-style codec decoder: 16 latent columns -> 1920 samples per frame
+    seanet = None
+    if not args.no_seanet and args.config == 4:
+        from streaming_ar_transformer_amd.seanet import SEANetDecoder
+        scfg = wl.SEANET_CONFIGS[1]
+        sw, sx = wl.make_seanet(scfg)
+        sdev = {k: torch.from_numpy(v).cuda() for k, v in sw.items()}
+        xf = torch.from_numpy(sx[0]).cuda()
+        sdec_ = SEANetDecoder(scfg, sdev)
+        n = 32
+        for i in range(4):
+            sdec_.step(xf, first=(i == 0), stream=stream)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(n):
+            sdec_.step(xf, stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        sms = start.elapsed_time(end) / n
+        seanet = {"workload": scfg.name, "frames": n, "ms_per_frame": round(sms, 4),
+                  "frames_per_s": round(1000.0 / sms, 1), "samples_per_frame": 1920,
+                  "realtime_factor_24khz": round(80.0 / sms, 1), "mode": "eager"}
+        print(f"{scfg.name}: {sms * 1e3:.1f} us/frame", file=sys.stderr, flush=True)
+        sdec_.close()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, layers, final, xs_host, args.cpu_seconds)
@@ -372,7 +399,7 @@ def main():
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": int(bytes_avg),
         "roofline": roofline, "eager_kernels": kernels, "prefill": prefill, "variant": variant,
-        "rvq": rvq,
+        "rvq": rvq, "seanet": seanet,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -300,3 +300,53 @@ def make_rvq(cfg: RVQConfig):
         "latents": _normal([s, 4, 6], (cfg.frames, d), 1.0),
     }
 
+
+@dataclasses.dataclass(frozen=True)
+class SEANetConfig:
+    """A streaming SEANet-style codec decoder ([pocket] module doc: conv k7, then per ratio ELU,
+    transposed conv and a residual block, then ELU and conv k3; 16 input columns per 80 ms frame
+    become 16 * 6 * 5 * 4 = 1920 samples).  Channels halve at each transposed conv (kernel
+    2 * ratio); a residual block is ELU, conv k3 to half the channels, ELU, conv k1 back, plus
+    the block's input.  The channel counts are readings."""
+
+    name: str
+    seed: int
+    channels: int = 512
+    ratios: tuple = (6, 5, 4)
+    frame_cols: int = 16
+    frames: int = 4
+
+    def replace(self, **kw) -> "SEANetConfig":
+        return dataclasses.replace(self, **kw)
+
+
+SEANET_CONFIGS = {1: SEANetConfig("seanet_c512_r654", 11)}
+
+
+def seanet_layers(cfg: SEANetConfig):
+    """(name, kind, weight shape, stride) in execution order: kind "conv" (weights [out][in][k]),
+    "convtr" ([in][out][k]), "res0"/"res1" (the residual block's two convs)."""
+    c = cfg.channels
+    out = [("conv_in", "conv", (c, c, 7), 1)]
+    for s, r in enumerate(cfg.ratios):
+        d = c // 2
+        out += [(f"up{s}", "convtr", (c, d, 2 * r), r),
+                (f"res{s}_0", "res0", (d // 2, d, 3), 1),
+                (f"res{s}_1", "res1", (d, d // 2, 1), 1)]
+        c = d
+    out.append(("conv_out", "conv", (1, c, 3), 1))
+    return out
+
+
+def make_seanet(cfg: SEANetConfig):
+    """Weights N(0, 1/fan_in) per layer (``[seed, 5, layer, 0]``), biases N(0, 0.1)
+    (``[seed, 5, layer, 1]``), input frames N(0, 1) ``[frames][channels][frame_cols]``."""
+    w = {}
+    for i, (name, kind, shape, _) in enumerate(seanet_layers(cfg)):
+        fan = shape[0] * shape[2] if kind == "convtr" else shape[1] * shape[2]
+        w[name + ".w"] = _normal([cfg.seed, 5, i, 0], shape, 1.0 / np.sqrt(fan))
+        n_out = shape[1] if kind == "convtr" else shape[0]
+        w[name + ".b"] = _normal([cfg.seed, 5, i, 1], (n_out,), 0.1)
+    x = _normal([cfg.seed, 5, 999, 0], (cfg.frames, cfg.channels, cfg.frame_cols), 1.0)
+    return w, x
+

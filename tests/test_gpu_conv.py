@@ -114,3 +114,43 @@ def test_accumulating_conv_and_errors(sd):
         c2.step(torch.zeros((16, 4), device="cuda"), y)  # a stream must start with first
     assert e.value.code == sd.E_POS
     c2.close()
+
+
+def offline_seanet(cfg, w, X):
+    from streaming_ar_transformer_amd import workloads as wl
+    h = None
+    for name, kind, shape, stride in wl.seanet_layers(cfg):
+        W, B = w[name + ".w"], w[name + ".b"]
+        if kind == "conv":
+            h = oracle.causal_conv1d(X if h is None else h, W, B, stride,
+                                     pre_elu=(name != "conv_in"))
+        elif kind == "convtr":
+            h = oracle.streamed_conv_transpose1d(h, W, B, stride, pre_elu=True)
+        elif kind == "res0":
+            block_in, h = h, oracle.causal_conv1d(h, W, B, 1, pre_elu=True)
+        else:
+            h = (block_in + oracle.causal_conv1d(h, W, B, 1, pre_elu=True)).astype(np.float32)
+    return h
+
+
+def test_seanet_decoder_streaming_equals_offline(sd):
+    # conv k7 -> (ELU, convtr, residual block) x [6, 5, 4] -> ELU, conv k3: 16 columns per frame
+    # become 1920 samples; frame by frame through the library == offline over all frames
+    from streaming_ar_transformer_amd import workloads as wl
+    from streaming_ar_transformer_amd.seanet import SEANetDecoder
+    from tests.gpu_helpers import assert_close_rows
+    cfg = wl.SEANET_CONFIGS[1]
+    w, x = wl.make_seanet(cfg)
+    dev = {k: torch.from_numpy(v).cuda() for k, v in w.items()}
+    dec = SEANetDecoder(cfg, dev)
+    outs = []
+    for f in range(cfg.frames):
+        print(f"seanet frame {f}", flush=True)
+        y = dec.step(torch.from_numpy(x[f]).cuda(), first=(f == 0))
+        outs.append(y.cpu().numpy())
+    got = np.concatenate(outs, axis=1)
+    want = offline_seanet(cfg, w, np.concatenate(list(x), axis=1))
+    assert got.shape == want.shape == (1, cfg.frames * 1920)
+    cos, mx = assert_close_rows(got, want, "seanet")
+    dec.close()
+    log(f"{cfg.name}: {cfg.frames} frames x 1920 samples, cos {cos:.9f} max|d| {mx:.2e}")
