@@ -84,12 +84,131 @@ __global__ __launch_bounds__(64) void k_sconvtr(SConvTrArgs a) {
   }
 }
 
+// Tiled forms for groups == 1: a workgroup of 256 threads owns oc_t output channels x t_t output
+// columns (oc_t * t_t == 256, one output per thread) and walks the input channels in blocks of
+// icb, staging the block's input window (ELU applied once per sample) and weights in LDS, so the
+// inner loop reads only LDS.  Per output the sum runs over input channels, then taps, as in the
+// one-thread-per-output kernels above.
+constexpr uint32_t kConvTileThreads = 256;
+
+__global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, uint32_t oc_t,
+                                                                  uint32_t t_t, uint32_t icb) {
+  extern __shared__ float lds[];
+  const uint32_t t_out = a.t_in / a.stride;
+  const uint32_t oc0 = blockIdx.y * oc_t, col0 = blockIdx.x * t_t;
+  const uint32_t xw = t_t * a.stride + a.pad;  // padded-stream columns the tile reads
+  float* X = lds;
+  float* W = lds + icb * xw;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t ocl = tid / t_t, otl = tid % t_t;
+  const uint32_t oc = oc0 + ocl, ot = col0 + otl;
+  const bool live = oc < a.c_out && ot < t_out;
+  float acc = live ? a.b[oc] : 0.f;
+  for (uint32_t ic0 = 0; ic0 < a.c_in; ic0 += icb) {
+    const uint32_t nb = min(icb, a.c_in - ic0);
+    __syncthreads();  // the previous block is consumed
+    for (uint32_t e = tid; e < nb * xw; e += kConvTileThreads) {
+      const uint32_t i = e / xw, j = e % xw, col = col0 * a.stride + j;
+      float v = col < a.t_in + a.pad ? sconv_sample(a, ic0 + i, col) : 0.f;
+      if (a.pre_elu) v = elu_f(v);
+      X[e] = v;
+    }
+    for (uint32_t e = tid; e < oc_t * nb * a.k; e += kConvTileThreads) {
+      const uint32_t o = e / (nb * a.k), r = e % (nb * a.k);
+      W[o * icb * a.k + r] = oc0 + o < a.c_out
+                                 ? a.w[(static_cast<size_t>(oc0 + o) * a.c_in + ic0) * a.k + r]
+                                 : 0.f;
+    }
+    __syncthreads();
+    if (live) {
+      const float* wr = W + ocl * icb * a.k;
+      for (uint32_t i = 0; i < nb; ++i) {
+        const float* xr = X + i * xw + otl * a.stride;
+        for (uint32_t k = 0; k < a.k; ++k) acc = fmaf(wr[i * a.k + k], xr[k], acc);
+      }
+    }
+  }
+  if (live) {
+    float* y = a.y + static_cast<size_t>(oc) * t_out + ot;
+    *y = a.accumulate ? *y + acc : acc;
+  }
+}
+
+__global__ __launch_bounds__(kConvTileThreads) void k_sconvtr_tiled(SConvTrArgs a, uint32_t oc_t,
+                                                                    uint32_t t_t, uint32_t icb) {
+  extern __shared__ float lds[];
+  const uint32_t emit = a.t_in * a.stride, len = emit + a.tl;
+  const uint32_t i0 = blockIdx.x * t_t, oc0 = blockIdx.y * oc_t;
+  // input columns that reach output columns [i0, i0 + t_t)
+  const uint32_t lo = i0 + 1 > a.k ? (i0 + 1 - a.k + a.stride - 1) / a.stride : 0;
+  const uint32_t hi = min(a.t_in - 1, (i0 + t_t - 1) / a.stride);
+  const uint32_t xw = hi >= lo ? hi - lo + 1 : 0;
+  const uint32_t xcap = t_t / a.stride + a.k / a.stride + 2;  // LDS columns per channel
+  float* X = lds;
+  float* W = lds + icb * xcap;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t ocl = tid / t_t, il = tid % t_t;
+  const uint32_t oc = oc0 + ocl, i = i0 + il;
+  const bool live = oc < a.c_out && i < len;
+  float acc = live ? a.b[oc] : 0.f;
+  for (uint32_t ic0 = 0; ic0 < a.c_in; ic0 += icb) {
+    const uint32_t nb = min(icb, a.c_in - ic0);
+    __syncthreads();
+    for (uint32_t e = tid; e < nb * xw; e += kConvTileThreads) {
+      const uint32_t c = e / xw, j = e % xw;
+      float v = a.x[static_cast<size_t>(ic0 + c) * a.t_in + lo + j];
+      if (a.pre_elu) v = elu_f(v);
+      X[c * xcap + j] = v;
+    }
+    for (uint32_t e = tid; e < nb * oc_t * a.k; e += kConvTileThreads) {
+      const uint32_t c = e / (oc_t * a.k), r = e % (oc_t * a.k), o = r / a.k, k = r % a.k;
+      W[(c * oc_t + o) * a.k + k] = oc0 + o < a.c_out
+                                        ? a.w[(static_cast<size_t>(ic0 + c) * a.c_out + oc0 + o) * a.k + k]
+                                        : 0.f;
+    }
+    __syncthreads();
+    if (live) {
+      for (uint32_t k = i % a.stride; k < a.k && k <= i; k += a.stride) {
+        const uint32_t ti = (i - k) / a.stride;
+        if (ti >= a.t_in) continue;
+        const float* xr = X + (ti - lo);
+        const float* wr = W + ocl * a.k + k;
+        for (uint32_t c = 0; c < nb; ++c) acc = fmaf(wr[c * oc_t * a.k], xr[c * xcap], acc);
+      }
+    }
+  }
+  if (!live) return;
+  const float old = (!a.first && i < a.tl) ? a.tail[static_cast<size_t>(oc) * a.tl + i] : 0.f;
+  if (i < emit) {
+    a.y[static_cast<size_t>(oc) * emit + i] = acc + old;
+  } else {
+    a.tail_out[static_cast<size_t>(oc) * a.tl + (i - emit)] = (acc - a.b[oc]) + old;
+  }
+}
+
+// Output tile: t_t columns (a power of two, 16..64, covering short frames) x 256/t_t channels.
+void conv_tile(uint32_t cols, uint32_t& oc_t, uint32_t& t_t) {
+  t_t = cols <= 16 ? 16 : cols <= 32 ? 32 : 64;
+  oc_t = kConvTileThreads / t_t;
+}
+constexpr uint32_t kConvIcb = 32;
+
 }  // namespace
 
 hipError_t launch_sconv(const SConvArgs& a, hipStream_t s) {
   const uint32_t t_out = a.t_in / a.stride;
   if (t_out == 0 || a.c_out == 0 || a.c_out > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_sconv, dim3((t_out + 63) / 64, a.c_out), dim3(64), 0, s, a);
+  if (a.groups == 1) {
+    uint32_t oc_t, t_t;
+    conv_tile(t_out, oc_t, t_t);
+    const uint32_t xw = t_t * a.stride + a.pad;
+    const size_t lds = (static_cast<size_t>(kConvIcb) * xw + static_cast<size_t>(oc_t) * kConvIcb * a.k) * sizeof(float);
+    if (lds > 64 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_sconv_tiled, dim3((t_out + t_t - 1) / t_t, (a.c_out + oc_t - 1) / oc_t),
+                       dim3(kConvTileThreads), lds, s, a, oc_t, t_t, kConvIcb);
+  } else {
+    hipLaunchKernelGGL(k_sconv, dim3((t_out + 63) / 64, a.c_out), dim3(64), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.pad == 0) return e;
   hipLaunchKernelGGL(k_sconv_carry, dim3((a.c_in * a.pad + 255) / 256), dim3(256), 0, s, a);
@@ -99,7 +218,17 @@ hipError_t launch_sconv(const SConvArgs& a, hipStream_t s) {
 hipError_t launch_sconvtr(const SConvTrArgs& a, hipStream_t s) {
   const uint32_t len = a.t_in * a.stride + a.tl;
   if (a.t_in == 0 || a.c_out == 0 || a.c_out > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_sconvtr, dim3((len + 63) / 64, a.c_out), dim3(64), 0, s, a);
+  if (a.groups == 1) {
+    uint32_t oc_t, t_t;
+    conv_tile(len, oc_t, t_t);
+    const uint32_t xcap = t_t / a.stride + a.k / a.stride + 2;
+    const size_t lds = (static_cast<size_t>(kConvIcb) * xcap + static_cast<size_t>(kConvIcb) * oc_t * a.k) * sizeof(float);
+    if (lds > 64 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_sconvtr_tiled, dim3((len + t_t - 1) / t_t, (a.c_out + oc_t - 1) / oc_t),
+                       dim3(kConvTileThreads), lds, s, a, oc_t, t_t, kConvIcb);
+  } else {
+    hipLaunchKernelGGL(k_sconvtr, dim3((len + 63) / 64, a.c_out), dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 
