@@ -90,6 +90,24 @@ __global__ __launch_bounds__(64) void k_sconvtr(SConvTrArgs a) {
 // inner loop reads only LDS.  Per output the sum runs over input channels, then taps, as in the
 // one-thread-per-output kernels above.
 constexpr uint32_t kConvTileThreads = 256;
+constexpr int kConvStageBatch = 8;
+
+// Fills n LDS elements, kConvStageBatch per thread per batch: the batch's global loads are all
+// issued before any result is used (indices clamped into [0, n), so no branch guards a load), so
+// a thread waits about one memory round trip per batch instead of one per element.
+template <typename Load, typename Store>
+__device__ __forceinline__ void conv_stage(uint32_t n, Load load, Store store) {
+  for (uint32_t e0 = threadIdx.x; e0 < n; e0 += kConvStageBatch * kConvTileThreads) {
+    float v[kConvStageBatch];
+#pragma unroll
+    for (int u = 0; u < kConvStageBatch; ++u) v[u] = load(min(e0 + u * kConvTileThreads, n - 1));
+#pragma unroll
+    for (int u = 0; u < kConvStageBatch; ++u) {
+      const uint32_t e = e0 + u * kConvTileThreads;
+      if (e < n) store(e, v[u]);
+    }
+  }
+}
 
 __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, uint32_t oc_t,
                                                                   uint32_t t_t, uint32_t icb) {
@@ -107,18 +125,48 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, u
   for (uint32_t ic0 = 0; ic0 < a.c_in; ic0 += icb) {
     const uint32_t nb = min(icb, a.c_in - ic0);
     __syncthreads();  // the previous block is consumed
-    for (uint32_t e = tid; e < nb * xw; e += kConvTileThreads) {
-      const uint32_t i = e / xw, j = e % xw, col = col0 * a.stride + j;
-      float v = col < a.t_in + a.pad ? sconv_sample(a, ic0 + i, col) : 0.f;
-      if (a.pre_elu) v = elu_f(v);
-      X[e] = v;
+    // X[i][j]: padded-stream column col0 * stride + j of input channel ic0 + i.  The tile's
+    // first n_pre columns lie in the carried prefix (only tiles that start inside it have
+    // any); the rest come from this frame, zero past its end.  Each region is staged with one
+    // unconditional load per element.
+    const uint32_t c_lo = col0 * a.stride;
+    const uint32_t n_pre = c_lo < a.pad ? min(a.pad - c_lo, xw) : 0u, wx = xw - n_pre;
+    conv_stage(
+        nb * wx,
+        [&](uint32_t e) {
+          const uint32_t col = c_lo + n_pre + e % wx;
+          const float v = a.x[static_cast<size_t>(ic0 + e / wx) * a.t_in +
+                              min(col - a.pad, a.t_in - 1)];
+          return col < a.t_in + a.pad ? v : 0.f;
+        },
+        [&](uint32_t e, float v) {
+          X[(e / wx) * xw + n_pre + e % wx] = a.pre_elu ? elu_f(v) : v;
+        });
+    if (n_pre) {
+      // the prefix, or on the first frame zeros or copies of the frame's first column
+      const bool from_x = a.first && a.replicate_first;
+      conv_stage(
+          nb * n_pre,
+          [&](uint32_t e) {
+            const size_t row = static_cast<size_t>(ic0 + e / n_pre);
+            return from_x ? a.x[row * a.t_in] : a.prefix[row * a.pad + c_lo + e % n_pre];
+          },
+          [&](uint32_t e, float v) {
+            if (a.first && !a.replicate_first) v = 0.f;
+            X[(e / n_pre) * xw + e % n_pre] = a.pre_elu ? elu_f(v) : v;
+          });
     }
-    for (uint32_t e = tid; e < oc_t * nb * a.k; e += kConvTileThreads) {
-      const uint32_t o = e / (nb * a.k), r = e % (nb * a.k);
-      W[o * icb * a.k + r] = oc0 + o < a.c_out
-                                 ? a.w[(static_cast<size_t>(oc0 + o) * a.c_in + ic0) * a.k + r]
-                                 : 0.f;
-    }
+    // W[o][i][k] for output channel oc0 + o (zero past c_out)
+    conv_stage(
+        oc_t * nb * a.k,
+        [&](uint32_t e) {
+          const uint32_t o = e / (nb * a.k), r = e % (nb * a.k);
+          return a.w[(static_cast<size_t>(min(oc0 + o, a.c_out - 1)) * a.c_in + ic0) * a.k + r];
+        },
+        [&](uint32_t e, float v) {
+          const uint32_t o = e / (nb * a.k), r = e % (nb * a.k);
+          W[o * icb * a.k + r] = oc0 + o < a.c_out ? v : 0.f;
+        });
     __syncthreads();
     if (live) {
       const float* wr = W + ocl * icb * a.k;
@@ -154,18 +202,20 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconvtr_tiled(SConvTrArgs 
   for (uint32_t ic0 = 0; ic0 < a.c_in; ic0 += icb) {
     const uint32_t nb = min(icb, a.c_in - ic0);
     __syncthreads();
-    for (uint32_t e = tid; e < nb * xw; e += kConvTileThreads) {
-      const uint32_t c = e / xw, j = e % xw;
-      float v = a.x[static_cast<size_t>(ic0 + c) * a.t_in + lo + j];
-      if (a.pre_elu) v = elu_f(v);
-      X[c * xcap + j] = v;
-    }
-    for (uint32_t e = tid; e < nb * oc_t * a.k; e += kConvTileThreads) {
-      const uint32_t c = e / (oc_t * a.k), r = e % (oc_t * a.k), o = r / a.k, k = r % a.k;
-      W[(c * oc_t + o) * a.k + k] = oc0 + o < a.c_out
-                                        ? a.w[(static_cast<size_t>(ic0 + c) * a.c_out + oc0 + o) * a.k + k]
-                                        : 0.f;
-    }
+    conv_stage(
+        nb * xw,
+        [&](uint32_t e) { return a.x[static_cast<size_t>(ic0 + e / xw) * a.t_in + lo + e % xw]; },
+        [&](uint32_t e, float v) { X[(e / xw) * xcap + e % xw] = a.pre_elu ? elu_f(v) : v; });
+    conv_stage(
+        nb * oc_t * a.k,
+        [&](uint32_t e) {
+          const uint32_t c = e / (oc_t * a.k), r = e % (oc_t * a.k), o = r / a.k, k = r % a.k;
+          return a.w[(static_cast<size_t>(ic0 + c) * a.c_out + min(oc0 + o, a.c_out - 1)) * a.k + k];
+        },
+        [&](uint32_t e, float v) {
+          const uint32_t o = (e % (oc_t * a.k)) / a.k;
+          W[e] = oc0 + o < a.c_out ? v : 0.f;
+        });
     __syncthreads();
     if (live) {
       for (uint32_t k = i % a.stride; k < a.k && k <= i; k += a.stride) {
