@@ -53,6 +53,10 @@ def parse():
                     help="skip the split-RVQ measurement (64 frames, 8 codebooks of 2048 bins)")
     ap.add_argument("--no-seanet", action="store_true",
                     help="skip the streaming SEANet-decoder measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (codec stacks 1-3, the m=8 talker 5)")
+    ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
+                    help="budget of each other workload's oracle sample (0: none)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes three times (the "
                          "known-size kernel that calibrates HBM byte counters)")
@@ -134,6 +138,101 @@ def cpu_baseline(cfg, layers, final, xs, budget_s):
     return {"value": n / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
             "sample": f"positions 0..{n - 1} of a fresh stream of this workload "
                       f"({n} steps, {dt:.1f} s, NumPy float32, BLAS threads={threads})"}
+
+
+def oracle_rate(cfg, layers, final, xs, pos0, budget_s, setup=None):
+    """Oracle steps/s on the first positions of a run from `pos0` (at least one step)."""
+    import oracle
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    if setup is not None:
+        setup(orc)
+    t0 = time.perf_counter()
+    n = 0
+    while n < xs.shape[0]:
+        orc.step(xs[n], pos0 + n, first=(n == 0 and setup is None))
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"steps_per_s": round(n / dt, 2), "steps": n, "seconds": round(dt, 2)}
+
+
+def bench_configs(ids, dl4, df4, stream, cpu_s):
+    """Steps/s and algorithmic GB/s of the other workloads on the graph path: the codec stacks
+    over their whole runs from a fresh stream, the m=8 talker over its 256 positions after the
+    4096-position import; each next to the oracle on a bounded sample."""
+    import numpy as np
+    import torch
+    from streaming_ar_transformer_amd import sdec, workloads as wl
+    from streaming_ar_transformer_amd.device import to_device, upload_weights
+    out = {}
+    for cid in ids:
+        cfg = wl.CONFIGS[cid]
+        layers, final = wl.make_weights(cfg)
+        if cid == 5:
+            dl, df = dl4, df4  # the same talker: config 4's weights
+        else:
+            dl, df = upload_weights(layers, final)
+        xs_host = wl.make_inputs(cfg, cfg.steps)
+        xs = to_device(xs_host)
+        dec = sdec.Decoder(cfg, dl, df)
+        pos0 = cfg.start_pos
+        setup = None
+        if pos0:
+            pos_ring = np.full(cfg.ring, 0xFFFFFFFF, np.uint32)
+            pos_ring[:pos0] = np.arange(pos0, dtype=np.uint32)
+            pre = {}
+            for s in range(cfg.m):
+                pre.update(wl.make_prefill(cfg, streams=[s]))
+                K, V = pre[s]
+                for li in range(cfg.n_layers):
+                    kp, vp, pp = dec.kv_view(s, li)
+                    sdec.copy_to_device(kp, K[li])
+                    sdec.copy_to_device(vp, V[li])
+                sdec.copy_to_device(pp, pos_ring)
+
+            def setup(orc, pre=pre):
+                for s in range(cfg.m):
+                    orc.import_kv(s, pre[s][0], pre[s][1], np.arange(pos0))
+        # one warmup step records the graph; the state it leaves is restored below
+        first0 = not pos0
+        if pos0:
+            dec.set_next_position(pos0)
+        warm = torch.empty((cfg.m, cfg.d_model), device="cuda")
+        warm.copy_(xs[0])
+        dec.step(warm, pos0, first=first0, stream=stream)
+        torch.cuda.synchronize()
+        if pos0:
+            # the warmup pushed position pos0 into every stream's ring: clear that slot again
+            for s in range(cfg.m):
+                _, _, pp = dec.kv_view(s, 0)
+                sdec.copy_to_device(pp, pos_ring)
+            dec.set_next_position(pos0)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(cfg.steps):
+            dec.step(xs[i], pos0 + i, first=(i == 0 and first0), stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / cfg.steps
+        dec.close()
+        bts = float(np.mean([step_bytes(cfg, pos0 + i, cfg.ring, cfg.window)
+                             for i in range(cfg.steps)]))
+        gbs = bts / (ms * 1e-3) / 1e9
+        rec = {"steps": cfg.steps, "positions": f"{pos0}..{pos0 + cfg.steps - 1}", "m": cfg.m,
+               "steps_per_s": round(1000.0 / ms, 1), "tokens_per_s": round(cfg.m * 1000.0 / ms, 1),
+               "ms_per_step": round(ms, 5), "hbm_gbs": round(gbs, 1),
+               "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": int(bts),
+               "mode": "hipgraph"}
+        if cpu_s > 0:
+            rec["oracle"] = oracle_rate(cfg, layers, final, xs_host, pos0, cpu_s, setup)
+        out[cfg.name] = rec
+        print(f"{cfg.name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s"
+              + (f", oracle {rec['oracle']['steps_per_s']} steps/s" if cpu_s > 0 else ""),
+              file=sys.stderr, flush=True)
+        del xs
+    return out
 
 
 def main():
@@ -382,6 +481,11 @@ def main():
         print(f"{scfg.name}: {sms * 1e3:.1f} us/frame", file=sys.stderr, flush=True)
         sdec_.close()
 
+    configs = None
+    if not args.no_configs and args.config == 4:
+        configs = bench_configs((1, 2, 3, 5), dl, df, stream,
+                                0.0 if args.no_cpu_baseline else args.config_cpu_seconds)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, layers, final, xs_host, args.cpu_seconds)
@@ -399,7 +503,7 @@ def main():
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": int(bytes_avg),
         "roofline": roofline, "eager_kernels": kernels, "prefill": prefill, "variant": variant,
-        "rvq": rvq, "seanet": seanet,
+        "rvq": rvq, "seanet": seanet, "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
