@@ -327,11 +327,11 @@ __device__ __forceinline__ void compact_legal(const uint32_t* P, uint32_t R, uin
   }
 }
 
-template <int HD, int G, int NT>
+template <int HD, int G, int NT, int LIST = NT>
 struct AttnSmem {
   static constexpr int LPS = HD / 8;
   static constexpr int NG = (NT / kWave) * (kWave / LPS);
-  uint32_t list[NT];
+  uint32_t list[LIST];
   float qs[G][HD];
   float ks[HD], vs[HD];  // this step's key (normed, roped) and value, for the item that pushes
   float sm_m[NG][G], sm_l[NG][G];
@@ -348,9 +348,16 @@ struct AttnSmem {
 // together; then every key and value row of the item is requested at once, and the query and key
 // normalisation and rope run while those loads are in flight.  The slot this step pushes (always
 // the first of item 0) is scored from LDS, so no load waits for the push.
-template <int HD, int G, int NT, bool COH, int UNR = 4, int CG = 0>
+//
+// SPLIT (streams that each attend a long ring): instead of fixed-size chunks, the legal slots of a
+// (stream, kv head) are split evenly over its n_chunks items, up to LIST slots each, so all items
+// of a step run in one round however long the context; an item walks its share in passes of
+// NG * UNR slots with two passes' keys and values in flight, the next pass requested before the
+// current one is scored.
+template <int HD, int G, int NT, bool COH, int UNR = 4, int CG = 0, bool SPLIT = false,
+          int LIST = NT>
 __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk, uint32_t kvh,
-                                               uint32_t s, AttnSmem<HD, G, NT>& sm) {
+                                               uint32_t s, AttnSmem<HD, G, NT, LIST>& sm) {
   constexpr int LPS = HD / 8;
   constexpr int GPW = kWave / LPS;
   constexpr int NWV = NT / kWave;
@@ -382,8 +389,9 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   static_assert(NT >= 2 * HD, "one thread per raw key or value element");
   constexpr int QPT = (G * HD + NT - 1) / NT;
   const uint32_t nl = a.n_legal[s];
-  const uint32_t c0 = chunk * a.chunk;
-  const uint32_t slot_of = a.legal[static_cast<size_t>(s) * a.ring + min(c0 + tid, a.ring - 1)];
+  // fixed chunks: this item's slot entry is requested with the count (clamped index)
+  const uint32_t slot_of =
+      SPLIT ? 0u : a.legal[static_cast<size_t>(s) * a.ring + min(chunk * a.chunk + tid, a.ring - 1)];
   float qv[QPT];
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
@@ -395,11 +403,19 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   // keep the compiler from sinking these loads below the early exit, which waits for the count
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  const uint32_t n_items = (nl + a.chunk - 1) / a.chunk;
+  // slots per item: fixed, or the even split of this stream's legal slots over n_chunks items
+  const uint32_t per = SPLIT ? max((nl + a.n_chunks - 1) / a.n_chunks, 1u) : a.chunk;
+  const uint32_t n_items = (nl + per - 1) / per;
   if (chunk >= n_items) return;  // no legal slot falls in this item
-  const uint32_t total = min(a.chunk, nl - c0);
+  const uint32_t c0 = chunk * per;
+  const uint32_t total =
+      SPLIT ? min(min(per, nl - c0), static_cast<uint32_t>(LIST)) : min(per, nl - c0);
   const bool lead = a.push && a.st != nullptr && chunk == 0;  // list[0] is the slot pushed now
-  if (static_cast<uint32_t>(tid) < total) list[tid] = slot_of;
+  if constexpr (SPLIT) {
+    for (uint32_t i = tid; i < total; i += NT) list[i] = a.legal[static_cast<size_t>(s) * a.ring + c0 + i];
+  } else {
+    if (static_cast<uint32_t>(tid) < total) list[tid] = slot_of;
+  }
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
     const int t = tid + j * NT;
@@ -413,25 +429,30 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   const float* kb = a.k_ring + static_cast<size_t>(s) * a.ring_stream_stride + kvh * HD + 8 * sub;
   const float* vb = a.v_ring + static_cast<size_t>(s) * a.ring_stream_stride + kvh * HD + 8 * sub;
   float4 kk[UNR][2], vv[UNR][2];
-  auto load_pass = [&](uint32_t i0) {
+  float4 kk2[SPLIT ? UNR : 1][2], vv2[SPLIT ? UNR : 1][2];  // SPLIT: the pass after kk, vv
+  auto load_pass = [&](auto& K, auto& V, uint32_t i0) {
     uint32_t slots[UNR];  // every slot index of the pass read from LDS before any load waits
 #pragma unroll
     for (int u = 0; u < UNR; ++u) slots[u] = list[min(i0 + u * NG, total - 1)];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const uint32_t i = i0 + u * NG;
-      if (i < total && !(lead && i == 0)) {
+      // SPLIT requests every row unconditionally (indices clamped into the item, rows past its
+      // end weigh nothing), so the waits of consecutive passes stay ordered and narrow
+      if (SPLIT || (i < total && !(lead && i == 0))) {
         const size_t sl = slots[u];
         const float4* kp = reinterpret_cast<const float4*>(kb + sl * row);
         const float4* vp = reinterpret_cast<const float4*>(vb + sl * row);
-        kk[u][0] = kp[0]; kk[u][1] = kp[1];
-        vv[u][0] = vp[0]; vv[u][1] = vp[1];
+        K[u][0] = kp[0]; K[u][1] = kp[1];
+        V[u][0] = vp[0]; V[u][1] = vp[1];
       } else {
-        kk[u][0] = kk[u][1] = vv[u][0] = vv[u][1] = f4zero();
+        K[u][0] = K[u][1] = V[u][0] = V[u][1] = f4zero();
       }
     }
   };
-  load_pass(grp);
+  constexpr uint32_t PASS = NG * UNR;
+  load_pass(kk, vv, grp);
+  if constexpr (SPLIT) load_pass(kk2, vv2, grp + PASS);
 
   // 3. queries: qk-norm + rope, one wave per head; the pushing item's last wave also normalises and
   //    ropes this step's key and writes key and value into the ring slot pos mod R
@@ -479,19 +500,19 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
   }
-  for (uint32_t i0 = grp; i0 < total;) {  // a group past the item's end has nothing to score
+  auto score_pass = [&](auto& K, auto& V, uint32_t i0) {
     // all UNR scores of the pass first (independent chains), then one softmax update per head
     float sc[UNR][G];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const uint32_t i = i0 + u * NG;
-      float kf[8] = {kk[u][0].x, kk[u][0].y, kk[u][0].z, kk[u][0].w,
-                     kk[u][1].x, kk[u][1].y, kk[u][1].z, kk[u][1].w};
+      float kf[8] = {K[u][0].x, K[u][0].y, K[u][0].z, K[u][0].w,
+                     K[u][1].x, K[u][1].y, K[u][1].z, K[u][1].w};
       if (lead && i == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) kf[e] = sm.ks[8 * sub + e];
-        vv[u][0] = make_float4(sm.vs[8 * sub], sm.vs[8 * sub + 1], sm.vs[8 * sub + 2], sm.vs[8 * sub + 3]);
-        vv[u][1] = make_float4(sm.vs[8 * sub + 4], sm.vs[8 * sub + 5], sm.vs[8 * sub + 6], sm.vs[8 * sub + 7]);
+        V[u][0] = make_float4(sm.vs[8 * sub], sm.vs[8 * sub + 1], sm.vs[8 * sub + 2], sm.vs[8 * sub + 3]);
+        V[u][1] = make_float4(sm.vs[8 * sub + 4], sm.vs[8 * sub + 5], sm.vs[8 * sub + 6], sm.vs[8 * sub + 7]);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -516,8 +537,8 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
           const float p = expf(sc[u][g] - mnew);
-          const float vf[8] = {vv[u][0].x, vv[u][0].y, vv[u][0].z, vv[u][0].w,
-                               vv[u][1].x, vv[u][1].y, vv[u][1].z, vv[u][1].w};
+          const float vf[8] = {V[u][0].x, V[u][0].y, V[u][0].z, V[u][0].w,
+                               V[u][1].x, V[u][1].y, V[u][1].z, V[u][1].w};
           lrun[g] += p;
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
@@ -525,9 +546,24 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
         mrun[g] = mnew;
       }
     }
-    i0 += NG * UNR;
-    if (i0 >= total) break;
-    load_pass(i0);
+  };
+  if constexpr (SPLIT) {
+    for (uint32_t i0 = grp; i0 < total;) {
+      score_pass(kk, vv, i0);
+      load_pass(kk, vv, i0 + 2 * PASS);  // clamped: past the end it re-reads the last slot
+      i0 += PASS;
+      if (i0 >= total) break;
+      score_pass(kk2, vv2, i0);
+      load_pass(kk2, vv2, i0 + 2 * PASS);
+      i0 += PASS;
+    }
+  } else {
+    for (uint32_t i0 = grp; i0 < total;) {  // a group past the item's end has nothing to score
+      score_pass(kk, vv, i0);
+      i0 += PASS;
+      if (i0 >= total) break;
+      load_pass(kk, vv, i0);
+    }
   }
 
   // 5. merge the slot groups of this workgroup into the chunk's (max, sum, output)

@@ -458,6 +458,15 @@ __global__ __launch_bounds__(kWgThreads) void k_attention(AttnArgs a) {
   attention_item<HD, G, kWgThreads, false, UNR>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
+// Split form for streams with long rings: grid (item, kv head, stream), n_chunks items per
+// (stream, kv head) sharing its legal slots evenly, two passes of keys and values in flight.
+template <int HD, int G>
+__global__ __launch_bounds__(kWgThreads) void k_attention_split(AttnArgs a) {
+  __shared__ AttnSmem<HD, G, kWgThreads, kAttnSplitList> sm;
+  attention_item<HD, G, kWgThreads, false, 4, 0, true, kAttnSplitList>(a, blockIdx.x, blockIdx.y,
+                                                                       blockIdx.z, sm);
+}
+
 // ------------------------------------------------------------------------------------------------
 // Row-stream GEMV for one stream: each wave holds one weight row (KB float4 per lane) in flight and
 // walks rows t, t + W, t + 2W, ... (W waves in the grid), so at any moment the device streams a
@@ -1259,11 +1268,16 @@ hipError_t launch_attention_hd(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.n_chunks, a.n_kv_heads, a.m);
   const void* fn = nullptr;
   switch (a.n_q_heads / a.n_kv_heads) {
-    case 1: fn = reinterpret_cast<const void*>(&k_attention<HD, 1>); break;
-    case 2: fn = reinterpret_cast<const void*>(&k_attention<HD, 2>); break;
-    case 4: fn = reinterpret_cast<const void*>(&k_attention<HD, 4>); break;
+    case 1: fn = a.split ? reinterpret_cast<const void*>(&k_attention_split<HD, 1>)
+                         : reinterpret_cast<const void*>(&k_attention<HD, 1>); break;
+    case 2: fn = a.split ? reinterpret_cast<const void*>(&k_attention_split<HD, 2>)
+                         : reinterpret_cast<const void*>(&k_attention<HD, 2>); break;
+    case 4: fn = a.split ? reinterpret_cast<const void*>(&k_attention_split<HD, 4>)
+                         : reinterpret_cast<const void*>(&k_attention<HD, 4>); break;
     default: return hipErrorInvalidValue;
   }
+  if (a.split && (a.n_chunks == 0 || (a.ring + a.n_chunks - 1) / a.n_chunks > kAttnSplitList))
+    return hipErrorInvalidValue;
   AttnArgs args = a;
   void* params[] = {&args};
   return launch_timed(fn, grid, dim3(kWgThreads), params, 0, s);

@@ -75,6 +75,8 @@ struct sdec_handle {
   std::vector<GemvLaunch> plan_qkv, plan_o, plan_up, plan_down;
   // one stream: the attention launch leaves its chunk partials and the o projection combines them
   bool attn_fused = false;
+  // several streams: attention items split each stream's legal slots evenly (n_chunks per kv head)
+  bool attn_split = false;
 
   hipStream_t cap_stream = nullptr;
   hipGraphExec_t exec = nullptr;
@@ -261,6 +263,7 @@ int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk) {
     aa.m = c.m; aa.n_q_heads = hq; aa.n_kv_heads = hkv; aa.head_dim = hd; aa.ring = h->ring;
     aa.chunk = h->chunk; aa.n_chunks = h->n_chunks; aa.st = h->st;
     aa.partials_only = h->attn_fused ? 1 : 0;
+    aa.split = h->attn_split ? 1 : 0;
     LAUNCH(hk, s, SDEC_K_ATTENTION, launch_attention(aa, s));
     // o projection + (LayerScale) residual; with the fused combine its prologue finishes the
     // attention output from the chunk partials (and copies it to the tap)
@@ -535,6 +538,17 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
   const uint32_t qw = hq * hd, kw = hkv * hd;
   h->chunk = attention_chunk(hd);
   h->n_chunks = (ring_slots + h->chunk - 1) / h->chunk;
+  if (c.m > 1) {
+    // several streams, each attending its own ring: the split form, a fixed number of items per
+    // (stream, kv head) whatever the context length (tuning override SDEC_ATTN_ITEMS)
+    const char* ev = std::getenv("SDEC_ATTN_ITEMS");
+    uint32_t items = ev && *ev ? static_cast<uint32_t>(atoi(ev)) : 8u;
+    const uint32_t least = (ring_slots + kAttnSplitList - 1) / kAttnSplitList;
+    if (items < least) items = least;
+    if (items > ring_slots) items = ring_slots;
+    h->attn_split = true;
+    h->n_chunks = items;
+  }
   h->ring_layer_stride = static_cast<uint64_t>(ring_slots) * kw;
   h->ring_stream_stride = h->ring_layer_stride * c.n_layers;
   const bool taps = (c.flags & SDEC_FLAG_TAPS) != 0;

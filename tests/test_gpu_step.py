@@ -202,6 +202,38 @@ def test_talker_m8_from_prefill(sd):
     dec.close()
 
 
+SPLIT_T = wl.small_config("T", n_layers=2, d_model=512, n_q_heads=4, n_kv_heads=2,
+                          head_dim=128, d_ff=1024, ring=600, window=520, steps=700).replace(m=3, unbounded=False)
+
+
+@pytest.mark.parametrize("items", ["2", "8"])
+def test_streams_split_attention_long_windowed_ring(sd, items, monkeypatch):
+    # Several streams: each stream's legal slots are split evenly over a fixed number of items
+    # that walk them in double-buffered passes of 64 slots.  Two items per kv head put up to 260
+    # slots (five passes) in one item; the 520-slot window over a 600-slot ring wraps at 600.
+    monkeypatch.setenv("SDEC_ATTN_ITEMS", items)
+    cfg = SPLIT_T
+    layers, final = weights(cfg)
+    dec = make(sd, cfg)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    xs = wl.make_inputs(cfg, cfg.steps)
+    x = torch.empty((cfg.m, cfg.d_model), device="cuda")
+    check = set(range(0, cfg.steps, 37)) | {63, 64, 65, 519, 520, 521, 599, 600, 601, cfg.steps - 1}
+    for p in range(cfg.steps):
+        want = orc.step(xs[p], p, first=(p == 0))
+        if p in check:
+            x.copy_(torch.from_numpy(xs[p]))
+            dec.step(x, p, first=(p == 0))
+            cos, mx = assert_close_rows(x.cpu().numpy(), want, f"split items={items} pos {p}")
+        else:
+            x.copy_(torch.from_numpy(xs[p]))
+            dec.step(x, p, first=(p == 0))
+    log(f"split items={items}: last pos cos {cos:.9f} max|d| {mx:.3e}")
+    for s in range(cfg.m):
+        np.testing.assert_array_equal(read_pos_ring(sd, dec, s, cfg.ring), orc.P[s])
+    dec.close()
+
+
 # ---------------------------------------------------------------------------------------------
 # cross-checks on the GPU path itself
 # ---------------------------------------------------------------------------------------------
