@@ -1175,6 +1175,10 @@ template <int M>
 GemvKernel gemv_ksm(const GemvLaunch& l) {
   if (l.waves_per_wg == 4 && l.ks == 2 && l.rows_per_wave == 4) return gemv_ksm_kind<M, 4, 2, 4>(l);
   if (l.waves_per_wg == 8 && l.ks == 3 && l.rows_per_wave == 2) return gemv_ksm_kind<M, 8, 3, 2>(l);
+  if constexpr (M == 8) {  // taller tiles: every tile of the launch in flight in one round
+    if (l.waves_per_wg == 4 && l.ks == 2 && l.rows_per_wave == 8) return gemv_ksm_kind<M, 4, 2, 8>(l);
+    if (l.waves_per_wg == 8 && l.ks == 3 && l.rows_per_wave == 4) return gemv_ksm_kind<M, 8, 3, 4>(l);
+  }
   return {nullptr, 0};
 }
 
@@ -1342,6 +1346,15 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
     l.kb = 0;
     l.waves_per_wg = k == 2048 ? 4 : 8;
     l.rows_per_wave = k == 2048 ? 4 : 2;
+    if (M == 8) {
+      // taller tiles where measured faster at 8 streams: the q/k/v projection (8 rows per tile,
+      // 10.7 vs 12.8 us) and the down projection (4 rows, 12.6 vs 13.1 us); the o and gate/up
+      // projections keep theirs.  Tuning overrides: SDEC_KSM_RB2048, SDEC_KSM_RB6144.
+      const int dflt = k == 2048 ? (epilogue == EPI_STORE ? 8 : 4) : 4;
+      const int rb = env_int(k == 2048 ? "SDEC_KSM_RB2048" : "SDEC_KSM_RB6144", dflt);
+      if ((k == 2048 && (rb == 4 || rb == 8)) || (k == 6144 && (rb == 2 || rb == 4)))
+        l.rows_per_wave = rb;
+    }
     const int units_per_wg = epilogue == EPI_SWIGLU ? l.rows_per_wave / 2 : l.rows_per_wave;
     int occ_m = 1;
     const GemvKernel kern = gemv_pick(l, k, m);
