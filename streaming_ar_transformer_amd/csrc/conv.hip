@@ -109,10 +109,15 @@ __device__ __forceinline__ void conv_stage(uint32_t n, Load load, Store store) {
   }
 }
 
+// With gridDim.z > 1 the input channels are split: workgroup z sums channels [z * ics, (z+1) * ics)
+// without the bias into part[z], and k_sconv_sum adds the splits in order.
 __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, uint32_t oc_t,
-                                                                  uint32_t t_t, uint32_t icb) {
+                                                                  uint32_t t_t, uint32_t icb,
+                                                                  uint32_t ics) {
   extern __shared__ float lds[];
   const uint32_t t_out = a.t_in / a.stride;
+  const bool split = gridDim.z > 1;
+  const uint32_t ic_begin = blockIdx.z * ics, ic_end = min(a.c_in, ic_begin + ics);
   const uint32_t oc0 = blockIdx.y * oc_t, col0 = blockIdx.x * t_t;
   const uint32_t xw = t_t * a.stride + a.pad;  // padded-stream columns the tile reads
   float* X = lds;
@@ -121,9 +126,9 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, u
   const uint32_t ocl = tid / t_t, otl = tid % t_t;
   const uint32_t oc = oc0 + ocl, ot = col0 + otl;
   const bool live = oc < a.c_out && ot < t_out;
-  float acc = live ? a.b[oc] : 0.f;
-  for (uint32_t ic0 = 0; ic0 < a.c_in; ic0 += icb) {
-    const uint32_t nb = min(icb, a.c_in - ic0);
+  float acc = live && !split ? a.b[oc] : 0.f;
+  for (uint32_t ic0 = ic_begin; ic0 < ic_end; ic0 += icb) {
+    const uint32_t nb = min(icb, ic_end - ic0);
     __syncthreads();  // the previous block is consumed
     // X[i][j]: padded-stream column col0 * stride + j of input channel ic0 + i.  The tile's
     // first n_pre columns lie in the carried prefix (only tiles that start inside it have
@@ -177,15 +182,46 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, u
     }
   }
   if (live) {
+    if (split) {
+      a.part[(static_cast<size_t>(blockIdx.z) * a.c_out + oc) * t_out + ot] = acc;
+      return;
+    }
     float* y = a.y + static_cast<size_t>(oc) * t_out + ot;
     *y = a.accumulate ? *y + acc : acc;
   }
 }
 
+// The splits of a split-k conv: bias, then the partial sums in split order.
+__global__ __launch_bounds__(256) void k_sconv_sum(SConvArgs a, uint32_t splits) {
+  const uint32_t t_out = a.t_in / a.stride;
+  const uint32_t e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= a.c_out * t_out) return;
+  const uint32_t oc = e / t_out;
+  float acc = a.b[oc];
+  for (uint32_t z = 0; z < splits; ++z) acc += a.part[static_cast<size_t>(z) * a.c_out * t_out + e];
+  a.y[e] = a.accumulate ? a.y[e] + acc : acc;
+}
+
+// Column i of this frame's full transposed-conv output (bias included in acc): below t_in * S it
+// is emitted with the carried tail added; the rest becomes the next tail, bias subtracted.
+__device__ __forceinline__ void sconvtr_emit(const SConvTrArgs& a, uint32_t oc, uint32_t i, float acc) {
+  const uint32_t emit = a.t_in * a.stride;
+  const float old = (!a.first && i < a.tl) ? a.tail[static_cast<size_t>(oc) * a.tl + i] : 0.f;
+  if (i < emit) {
+    a.y[static_cast<size_t>(oc) * emit + i] = acc + old;
+  } else {
+    a.tail_out[static_cast<size_t>(oc) * a.tl + (i - emit)] = (acc - a.b[oc]) + old;
+  }
+}
+
+// Split input channels as in k_sconv_tiled; k_sconvtr_sum adds the splits and emits.
 __global__ __launch_bounds__(kConvTileThreads) void k_sconvtr_tiled(SConvTrArgs a, uint32_t oc_t,
-                                                                    uint32_t t_t, uint32_t icb) {
+                                                                    uint32_t t_t, uint32_t icb,
+                                                                    uint32_t ics) {
   extern __shared__ float lds[];
   const uint32_t emit = a.t_in * a.stride, len = emit + a.tl;
+  const bool split = gridDim.z > 1;
+  const uint32_t ic_begin = blockIdx.z * ics, ic_end = min(a.c_in, ic_begin + ics);
   const uint32_t i0 = blockIdx.x * t_t, oc0 = blockIdx.y * oc_t;
   // input columns that reach output columns [i0, i0 + t_t)
   const uint32_t lo = i0 + 1 > a.k ? (i0 + 1 - a.k + a.stride - 1) / a.stride : 0;
@@ -198,9 +234,9 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconvtr_tiled(SConvTrArgs 
   const uint32_t ocl = tid / t_t, il = tid % t_t;
   const uint32_t oc = oc0 + ocl, i = i0 + il;
   const bool live = oc < a.c_out && i < len;
-  float acc = live ? a.b[oc] : 0.f;
-  for (uint32_t ic0 = 0; ic0 < a.c_in; ic0 += icb) {
-    const uint32_t nb = min(icb, a.c_in - ic0);
+  float acc = live && !split ? a.b[oc] : 0.f;
+  for (uint32_t ic0 = ic_begin; ic0 < ic_end; ic0 += icb) {
+    const uint32_t nb = min(icb, ic_end - ic0);
     __syncthreads();
     conv_stage(
         nb * xw,
@@ -228,12 +264,21 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconvtr_tiled(SConvTrArgs 
     }
   }
   if (!live) return;
-  const float old = (!a.first && i < a.tl) ? a.tail[static_cast<size_t>(oc) * a.tl + i] : 0.f;
-  if (i < emit) {
-    a.y[static_cast<size_t>(oc) * emit + i] = acc + old;
-  } else {
-    a.tail_out[static_cast<size_t>(oc) * a.tl + (i - emit)] = (acc - a.b[oc]) + old;
+  if (split) {
+    a.part[(static_cast<size_t>(blockIdx.z) * a.c_out + oc) * len + i] = acc;
+    return;
   }
+  sconvtr_emit(a, oc, i, acc);
+}
+
+__global__ __launch_bounds__(256) void k_sconvtr_sum(SConvTrArgs a, uint32_t splits) {
+  const uint32_t len = a.t_in * a.stride + a.tl;
+  const uint32_t e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= a.c_out * len) return;
+  const uint32_t oc = e / len, i = e % len;
+  float acc = a.b[oc];
+  for (uint32_t z = 0; z < splits; ++z) acc += a.part[static_cast<size_t>(z) * a.c_out * len + e];
+  sconvtr_emit(a, oc, i, acc);
 }
 
 // Output tile: t_t columns (a power of two, 16..64, covering short frames) x 256/t_t channels.
@@ -242,6 +287,23 @@ void conv_tile(uint32_t cols, uint32_t& oc_t, uint32_t& t_t) {
   oc_t = kConvTileThreads / t_t;
 }
 constexpr uint32_t kConvIcb = 32;
+
+// Input-channel splits for a tiled launch of `grid` workgroups: enough to give the device about
+// two workgroups per CU, whole blocks of kConvIcb channels per split, and within the scratch.
+uint32_t conv_splits(uint32_t grid, uint32_t c_in, uint64_t outs, uint64_t cap, uint32_t* ics) {
+  const uint32_t blocks = (c_in + kConvIcb - 1) / kConvIcb;
+  uint32_t s = (512 + grid - 1) / grid;
+  if (s > blocks) s = blocks;
+  if (s > kConvMaxSplits) s = kConvMaxSplits;
+  while (s > 1 && static_cast<uint64_t>(s) * outs > cap) --s;
+  if (s <= 1) {
+    *ics = c_in;
+    return 1;
+  }
+  const uint32_t bps = (blocks + s - 1) / s;  // blocks per split
+  *ics = bps * kConvIcb;
+  return (c_in + *ics - 1) / *ics;
+}
 
 }  // namespace
 
@@ -254,8 +316,18 @@ hipError_t launch_sconv(const SConvArgs& a, hipStream_t s) {
     const uint32_t xw = t_t * a.stride + a.pad;
     const size_t lds = (static_cast<size_t>(kConvIcb) * xw + static_cast<size_t>(oc_t) * kConvIcb * a.k) * sizeof(float);
     if (lds > 64 * 1024) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_sconv_tiled, dim3((t_out + t_t - 1) / t_t, (a.c_out + oc_t - 1) / oc_t),
-                       dim3(kConvTileThreads), lds, s, a, oc_t, t_t, kConvIcb);
+    const dim3 g((t_out + t_t - 1) / t_t, (a.c_out + oc_t - 1) / oc_t);
+    uint32_t ics = a.c_in;
+    const uint32_t splits = a.part ? conv_splits(g.x * g.y, a.c_in,
+                                                 static_cast<uint64_t>(a.c_out) * t_out, a.part_cap, &ics)
+                                   : 1u;
+    hipLaunchKernelGGL(k_sconv_tiled, dim3(g.x, g.y, splits), dim3(kConvTileThreads), lds, s, a,
+                       oc_t, t_t, kConvIcb, ics);
+    if (splits > 1) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_sconv_sum, dim3((a.c_out * t_out + 255) / 256), dim3(256), 0, s, a, splits);
+    }
   } else {
     hipLaunchKernelGGL(k_sconv, dim3((t_out + 63) / 64, a.c_out), dim3(64), 0, s, a);
   }
@@ -274,8 +346,18 @@ hipError_t launch_sconvtr(const SConvTrArgs& a, hipStream_t s) {
     const uint32_t xcap = t_t / a.stride + a.k / a.stride + 2;
     const size_t lds = (static_cast<size_t>(kConvIcb) * xcap + static_cast<size_t>(kConvIcb) * oc_t * a.k) * sizeof(float);
     if (lds > 64 * 1024) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_sconvtr_tiled, dim3((len + t_t - 1) / t_t, (a.c_out + oc_t - 1) / oc_t),
-                       dim3(kConvTileThreads), lds, s, a, oc_t, t_t, kConvIcb);
+    const dim3 g((len + t_t - 1) / t_t, (a.c_out + oc_t - 1) / oc_t);
+    uint32_t ics = a.c_in;
+    const uint32_t splits = a.part ? conv_splits(g.x * g.y, a.c_in,
+                                                 static_cast<uint64_t>(a.c_out) * len, a.part_cap, &ics)
+                                   : 1u;
+    hipLaunchKernelGGL(k_sconvtr_tiled, dim3(g.x, g.y, splits), dim3(kConvTileThreads), lds, s, a,
+                       oc_t, t_t, kConvIcb, ics);
+    if (splits > 1) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_sconvtr_sum, dim3((a.c_out * len + 255) / 256), dim3(256), 0, s, a, splits);
+    }
   } else {
     hipLaunchKernelGGL(k_sconvtr, dim3((len + 63) / 64, a.c_out), dim3(64), 0, s, a);
   }

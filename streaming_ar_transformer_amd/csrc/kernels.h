@@ -204,6 +204,8 @@ struct SConvArgs {
   float* y;                // [c_out][t_in / stride]
   uint32_t c_in, c_out, k, stride, groups, t_in, pad;
   int pre_elu, replicate_first, first, accumulate;
+  float* part;             // split-k partial sums [splits][c_out][t_in / stride] (groups == 1)
+  uint64_t part_cap;       // floats part holds (0: no split)
 };
 hipError_t launch_sconv(const SConvArgs& a, hipStream_t s);
 struct SConvTrArgs {
@@ -215,7 +217,11 @@ struct SConvTrArgs {
   float* y;                // [c_out][t_in * stride]
   uint32_t c_in, c_out, k, stride, groups, t_in, tl;
   int pre_elu, first;
+  float* part;             // split-k partial sums [splits][c_out][t_in * stride + tl] (groups == 1)
+  uint64_t part_cap;       // floats part holds (0: no split)
 };
+// Most input-channel splits a streaming conv launch uses (its partial-sum scratch is sized for it).
+constexpr uint32_t kConvMaxSplits = 16;
 hipError_t launch_sconvtr(const SConvTrArgs& a, hipStream_t s);
 
 // Persistent step kernel (step.hip): one cooperative launch per step for a single stream.

@@ -1113,6 +1113,8 @@ struct sdec_conv {
   const float* w = nullptr;
   const float* b = nullptr;
   float* state[2] = {nullptr, nullptr};  // prefix [in_ch][k - s] or tail [out_ch][k - s]
+  float* part = nullptr;                 // split-k partial sums (groups == 1)
+  uint64_t part_cap = 0;
   int cur = 0;
   bool started = false;
 };
@@ -1138,6 +1140,18 @@ int sdec_conv_create(const sdec_conv_config* cfg, const float* w, const float* b
   Alloc A;
   h->state[0] = A.get<float>(n);
   h->state[1] = A.get<float>(n);
+  if (c.groups == 1) {
+    // partial sums of up to kConvMaxSplits input-channel splits of the largest frame
+    const uint64_t cols = c.transposed
+                              ? static_cast<uint64_t>(c.max_t_in) * c.stride + (c.kernel - c.stride)
+                              : c.max_t_in / c.stride;
+    uint64_t splits = (c.in_ch + 31) / 32;
+    if (splits > kConvMaxSplits) splits = kConvMaxSplits;
+    if (splits > 1) {
+      h->part_cap = splits * c.out_ch * cols;
+      h->part = A.get<float>(h->part_cap);
+    }
+  }
   if (A.code != SDEC_OK) {
     for (void* p : A.ptrs) (void)hipFree(p);
     delete h;
@@ -1163,6 +1177,7 @@ int sdec_conv_step(sdec_conv* h, const float* x, uint32_t t_in, float* y, uint32
     a.y = y; a.c_in = c.in_ch; a.c_out = c.out_ch; a.k = c.kernel; a.stride = c.stride;
     a.groups = c.groups; a.t_in = t_in; a.tl = carry; a.pre_elu = c.pre_elu ? 1 : 0;
     a.first = first ? 1 : 0;
+    a.part = h->part; a.part_cap = h->part_cap;
     HIP_TRY(launch_sconvtr(a, s));
   } else {
     if (t_in % c.stride) return fail(SDEC_E_ARG, "t_in=%u is not a multiple of stride %u", t_in, c.stride);
@@ -1172,6 +1187,7 @@ int sdec_conv_step(sdec_conv* h, const float* x, uint32_t t_in, float* y, uint32
     a.groups = c.groups; a.t_in = t_in; a.pad = carry; a.pre_elu = c.pre_elu ? 1 : 0;
     a.replicate_first = c.replicate_first ? 1 : 0; a.first = first ? 1 : 0;
     a.accumulate = c.accumulate ? 1 : 0;
+    a.part = h->part; a.part_cap = h->part_cap;
     HIP_TRY(launch_sconv(a, s));
   }
   h->cur ^= 1;
@@ -1184,6 +1200,7 @@ void sdec_conv_destroy(sdec_conv* h) {
   (void)hipDeviceSynchronize();
   for (float* p : h->state)
     if (p) (void)hipFree(p);
+  if (h->part) (void)hipFree(h->part);
   delete h;
 }
 
