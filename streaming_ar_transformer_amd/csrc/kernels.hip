@@ -1369,10 +1369,14 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
     if (kern.fn != nullptr) return l;
     l.ks = 0;  // no such kernel: the register GEMV below
   }
-  if (M == 1 && l.kb == 8 && epilogue == EPI_SWIGLU && env_int("SDEC_GEMV_STREAM", 1) != 0 &&
+  if (M == 1 && l.kb == 8 &&
+      (epilogue == EPI_SWIGLU ||
+       (epilogue == EPI_STORE && prologue != PRO_NONE && env_int("SDEC_GEMV_STREAM_QKV", 1) != 0)) &&
+      env_int("SDEC_GEMV_STREAM", 1) != 0 &&
       n_rows % (4u * static_cast<uint32_t>(cus)) == 0 && n_rows / (4u * static_cast<uint32_t>(cus)) <= 64) {
     // one row per wave in flight, one workgroup per CU: the gate rows and then the up rows stream
-    // as a dense band (16.8 vs 17.2 us for 2 x 6144 x 2048)
+    // as a dense band (16.8 vs 17.2 us for 2 x 6144 x 2048); the normed q/k/v projection streams
+    // its 4096 rows the same way (6.9 vs 7.0 us; tuning override SDEC_GEMV_STREAM_QKV=0)
     l.stream = 1;
     l.rows_per_wave = 1;
     l.waves_per_wg = kWgThreads / kWave;
