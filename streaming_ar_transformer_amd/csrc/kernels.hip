@@ -920,9 +920,24 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_ks(GemvArgs a) {
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kWgThreads) void k_begin(BeginArgs a) {
   __shared__ uint32_t scan[kWgThreads];
-  const uint32_t s = blockIdx.x;  // one workgroup per stream
+  const uint32_t s = blockIdx.x;  // one workgroup per stream, then one for the rope and the state
   const int tid = threadIdx.x;
   const uint32_t slot = a.pos % a.ring;
+  if (s == a.m) {  // workgroup-uniform: the float64 trig runs beside the streams' compaction
+    const uint32_t half = a.head_dim >> 1;
+    if (static_cast<uint32_t>(tid) < half) {
+      const double inv_freq = pow(a.theta, -2.0 * static_cast<double>(tid) /
+                                               static_cast<double>(a.head_dim));
+      const double ang = static_cast<double>(a.pos) * inv_freq;
+      a.cs[tid] = static_cast<float>(cos(ang));
+      a.cs[half + tid] = static_cast<float>(sin(ang));
+    }
+    if (tid == 0) {
+      a.st->pos = a.pos;
+      a.st->slot = slot;
+    }
+    return;
+  }
   const float4* src = reinterpret_cast<const float4*>(a.x_in + static_cast<size_t>(s) * a.d);
   float4* dst = reinterpret_cast<float4*>(a.xres + static_cast<size_t>(s) * a.d);
   for (uint32_t i = tid; i < (a.d >> 2); i += kWgThreads) dst[i] = src[i];
@@ -935,19 +950,6 @@ __global__ __launch_bounds__(kWgThreads) void k_begin(BeginArgs a) {
   __syncthreads();
   compact_legal<kWgThreads, false>(P, a.ring, a.pos, a.window, static_cast<int>(slot),
                                    a.legal + static_cast<size_t>(s) * a.ring, a.n_legal + s, scan);
-  if (s != 0) return;
-  const uint32_t half = a.head_dim >> 1;
-  if (static_cast<uint32_t>(tid) < half) {
-    const double inv_freq = pow(a.theta, -2.0 * static_cast<double>(tid) /
-                                             static_cast<double>(a.head_dim));
-    const double ang = static_cast<double>(a.pos) * inv_freq;
-    a.cs[tid] = static_cast<float>(cos(ang));
-    a.cs[half + tid] = static_cast<float>(sin(ang));
-  }
-  if (tid == 0) {
-    a.st->pos = a.pos;
-    a.st->slot = slot;
-  }
 }
 
 // Multi-position begin ([talker] TalkerGpu::prefill → forward_rows): the m rows are positions
@@ -1108,6 +1110,13 @@ GemvKernel gemv_rx(int kb) {
   switch (kb) {
     case 2: return {reinterpret_cast<const void*>(&k_gemv_rx<M, R, PRO, EPI, 2>), 0};
     case 8: return {reinterpret_cast<const void*>(&k_gemv_rx<M, R, PRO, EPI, 8>), 0};
+    case 4:  // k = 1024 (the FlowLM backbone)
+      if constexpr (M == 1) return {reinterpret_cast<const void*>(&k_gemv_rx<M, R, PRO, EPI, 4>), 0};
+      break;
+    case 16:  // k = 4096 (the FlowLM FFN down projection)
+      if constexpr (M == 1 && R == 1)
+        return {reinterpret_cast<const void*>(&k_gemv_rx<M, R, PRO, EPI, 16>), 0};
+      break;
     case 24:
       if constexpr (M == 1 && R == 1)
         return {reinterpret_cast<const void*>(&k_gemv_rx<M, R, PRO, EPI, 24>), 0};
@@ -1150,6 +1159,7 @@ template <int R>
 GemvKernel gemv_rx_attn(int kb) {
   if (kb == 2) return {reinterpret_cast<const void*>(&k_gemv_rx<1, R, PRO_ATTN, EPI_RESIDUAL, 2>), 0};
   if (kb == 8) return {reinterpret_cast<const void*>(&k_gemv_rx<1, R, PRO_ATTN, EPI_RESIDUAL, 8>), 0};
+  if (kb == 4) return {reinterpret_cast<const void*>(&k_gemv_rx<1, R, PRO_ATTN, EPI_RESIDUAL, 4>), 0};
   return {nullptr, 0};
 }
 
@@ -1316,6 +1326,8 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
   l.ks = 0;
   l.stream = 0;
   if (M <= 2 && (kb == 2 || kb == 8)) l.kb = static_cast<int>(kb);
+  if (M == 1 && (kb == 4 || (kb == 16 && epilogue != EPI_SWIGLU)) && env_int("SDEC_GEMV_RX_1K", 1) != 0)
+    l.kb = static_cast<int>(kb);
   if (M == 1 && kb == 24 && epilogue != EPI_SWIGLU) l.kb = 24;
   int dev = 0, cus = 256, occ = 1;
   if (hipGetDevice(&dev) == hipSuccess)
@@ -1389,7 +1401,7 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
       l.rows_per_wave = 2;
     } else if (l.kb == 2) {
       l.rows_per_wave = M == 1 ? 4 : 2;
-    } else if (l.kb == 8 && M == 1) {
+    } else if ((l.kb == 8 || l.kb == 4) && M == 1) {
       // the widest tile that still gives every SIMD of the device a tile of its own
       const uint32_t waves = 4u * static_cast<uint32_t>(cus);
       l.rows_per_wave = n_rows / 4 >= waves ? 4 : n_rows / 2 >= waves ? 2 : 1;
@@ -1447,7 +1459,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_begin(const BeginArgs& a, hipStream_t s) {
   BeginArgs args = a;
   void* params[] = {&args};
-  return launch_timed(reinterpret_cast<const void*>(&k_begin), dim3(a.m), dim3(kWgThreads), params, 0, s);
+  return launch_timed(reinterpret_cast<const void*>(&k_begin), dim3(a.m + 1), dim3(kWgThreads), params, 0, s);
 }
 
 hipError_t launch_begin_rows(const BeginArgs& a, hipStream_t s) {

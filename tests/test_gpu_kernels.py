@@ -31,7 +31,8 @@ def dev(a):
 # ---------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("n,k,m", [(1000, 6144, 1), (4096, 2048, 1), (777, 2048, 3),
-                                   (2048, 6144, 8), (1536, 512, 1), (33, 1000, 5)])
+                                   (2048, 6144, 8), (1536, 512, 1), (33, 1000, 5),
+                                   (1001, 1024, 1), (1023, 4096, 1)])
 def test_gemv_small_integers_bit_exact(sd, n, k, m):
     # |w|, |x| <= 4 with k <= 6144 keeps every partial sum an exact integer below 2^24.
     log(f"gemv exact n={n} k={k} m={m}")
@@ -45,7 +46,8 @@ def test_gemv_small_integers_bit_exact(sd, n, k, m):
 
 
 @pytest.mark.parametrize("n,k,m", [(4096, 2048, 1), (2048, 6144, 1), (12288, 2048, 1),
-                                   (2048, 2048, 8), (2048, 6144, 8), (1, 4, 1), (5, 260, 2)])
+                                   (2048, 2048, 8), (2048, 6144, 8), (1, 4, 1), (5, 260, 2),
+                                   (3072, 1024, 1), (1024, 4096, 1), (1, 1024, 1)])
 def test_gemv_random_within_error_bound(sd, n, k, m):
     log(f"gemv random n={n} k={k} m={m}")
     rng = np.random.default_rng(k + n + m)
