@@ -53,6 +53,8 @@ def parse():
                     help="skip the split-RVQ measurement (64 frames, 8 codebooks of 2048 bins)")
     ap.add_argument("--no-seanet", action="store_true",
                     help="skip the streaming SEANet-decoder measurement")
+    ap.add_argument("--fixed-positions", type=int, default=1,
+                    help="also time the step at fixed positions 0, R/2 and R-1 (0: skip)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (codec stacks 1-3, the m=8 talker 5)")
     ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
@@ -320,6 +322,43 @@ def main():
         dec.close()
         return
 
+    # the step at fixed positions: a seeded N(0, 1) K/V import of positions 0..p-1, then repeated
+    # steps at p (each re-stamps slot p with p, so every repetition attends the same p + 1 slots)
+    fixed = None
+    if args.fixed_positions and cfg.m == 1 and not args.persistent:
+        fixed = {}
+        xs.copy_(torch.from_numpy(xs_host))
+        fpos = [p for p in (0, ring // 2, ring - 1) if p < ring]
+        pre = wl.make_prefill(cfg, n_pos=max(fpos), streams=[0])[0] if max(fpos) else None
+        for p in fpos:
+            dec.reset()
+            pos_ring = np.full(ring, 0xFFFFFFFF, np.uint32)
+            if p:
+                pos_ring[:p] = np.arange(p, dtype=np.uint32)
+                for li in range(cfg.n_layers):
+                    kp, vp, pp = dec.kv_view(0, li)
+                    sdec.copy_to_device(kp, pre[0][li, :p])
+                    sdec.copy_to_device(vp, pre[1][li, :p])
+                sdec.copy_to_device(pp, pos_ring)
+            else:
+                _, _, pp = dec.kv_view(0, 0)
+                sdec.copy_to_device(pp, pos_ring)
+            reps = min(64, xs.shape[0] - 4)
+            for i in range(reps + 4):  # each step takes (and overwrites) its own input row
+                if i == 4:
+                    torch.cuda.synchronize()
+                    start.record(stream)
+                dec.set_next_position(p)
+                dec.step(xs[i], p, stream=stream)
+            end.record(stream)
+            torch.cuda.synchronize()
+            fms = start.elapsed_time(end) / reps
+            fb = step_bytes(cfg, p, ring, window)
+            fixed[str(p)] = {"us_per_step": round(fms * 1e3, 1),
+                             "hbm_gbs": round(fb / (fms * 1e-3) / 1e9, 1)}
+        print("fixed positions: " + ", ".join(f"p={k}: {v['us_per_step']} us" for k, v in fixed.items()),
+              file=sys.stderr, flush=True)
+
     # per-kernel launch times from profiled eager steps (each launch stamps a HIP event pair around
     # its own execution)
     xs.copy_(torch.from_numpy(xs_host))
@@ -502,7 +541,8 @@ def main():
                    "mode": mode},
         "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "bytes_per_step": int(bytes_avg),
-        "roofline": roofline, "eager_kernels": kernels, "prefill": prefill, "variant": variant,
+        "roofline": roofline, "fixed_positions": fixed, "eager_kernels": kernels,
+        "prefill": prefill, "variant": variant,
         "rvq": rvq, "seanet": seanet, "configs": configs,
         "cpu_baseline": cpu,
     }
