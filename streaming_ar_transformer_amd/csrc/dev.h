@@ -350,10 +350,10 @@ struct AttnSmem {
 // the first of item 0) is scored from LDS, so no load waits for the push.
 //
 // SPLIT (streams that each attend a long ring): instead of fixed-size chunks, the legal slots of a
-// (stream, kv head) are split evenly over its n_chunks items, up to LIST slots each, so all items
-// of a step run in one round however long the context; an item walks its share in passes of
-// NG * UNR slots with two passes' keys and values in flight, the next pass requested before the
-// current one is scored.
+// (stream, kv head) are dealt round-robin to its n_chunks items, up to LIST slots each, so all
+// items of a step run in one round however long the context; an item walks its share in passes
+// of NG * UNR slots with two passes' keys and values in flight, the next pass requested before
+// the current one is scored.
 template <int HD, int G, int NT, bool COH, int UNR = 4, int CG = 0, bool SPLIT = false,
           int LIST = NT>
 __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk, uint32_t kvh,
@@ -389,9 +389,17 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   static_assert(NT >= 2 * HD, "one thread per raw key or value element");
   constexpr int QPT = (G * HD + NT - 1) / NT;
   const uint32_t nl = a.n_legal[s];
-  // fixed chunks: this item's slot entry is requested with the count (clamped index)
-  const uint32_t slot_of =
-      SPLIT ? 0u : a.legal[static_cast<size_t>(s) * a.ring + min(chunk * a.chunk + tid, a.ring - 1)];
+  // this item's slot entries are requested with the count (clamped indices).  Fixed chunks: entry
+  // chunk * chunk_size + tid.  SPLIT: the item takes every n_chunks-th legal slot from `chunk`
+  // (entries chunk, chunk + n, chunk + 2n, ...), whose indices do not depend on the count.
+  constexpr int LPT = SPLIT ? (LIST + NT - 1) / NT : 1;
+  uint32_t slot_of[LPT];
+  const uint32_t* lg = a.legal + static_cast<size_t>(s) * a.ring;
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const uint32_t e = SPLIT ? chunk + (tid + j * NT) * a.n_chunks : chunk * a.chunk + tid;
+    slot_of[j] = lg[min(e, a.ring - 1)];
+  }
   float qv[QPT];
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
@@ -403,19 +411,15 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   // keep the compiler from sinking these loads below the early exit, which waits for the count
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  // slots per item: fixed, or the even split of this stream's legal slots over n_chunks items
-  const uint32_t per = SPLIT ? max((nl + a.n_chunks - 1) / a.n_chunks, 1u) : a.chunk;
-  const uint32_t n_items = (nl + per - 1) / per;
+  // items holding at least one legal slot, and this item's slot count
+  const uint32_t n_items = SPLIT ? min(nl, a.n_chunks) : (nl + a.chunk - 1) / a.chunk;
   if (chunk >= n_items) return;  // no legal slot falls in this item
-  const uint32_t c0 = chunk * per;
-  const uint32_t total =
-      SPLIT ? min(min(per, nl - c0), static_cast<uint32_t>(LIST)) : min(per, nl - c0);
+  const uint32_t total = SPLIT ? min((nl - 1 - chunk) / a.n_chunks + 1, static_cast<uint32_t>(LIST))
+                               : min(a.chunk, nl - chunk * a.chunk);
   const bool lead = a.push && a.st != nullptr && chunk == 0;  // list[0] is the slot pushed now
-  if constexpr (SPLIT) {
-    for (uint32_t i = tid; i < total; i += NT) list[i] = a.legal[static_cast<size_t>(s) * a.ring + c0 + i];
-  } else {
-    if (static_cast<uint32_t>(tid) < total) list[tid] = slot_of;
-  }
+#pragma unroll
+  for (int j = 0; j < LPT; ++j)
+    if (static_cast<uint32_t>(tid + j * NT) < total) list[tid + j * NT] = slot_of[j];
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
     const int t = tid + j * NT;

@@ -100,7 +100,7 @@ struct AttnArgs {
   const DevState* st;    // slot of this step's push; null: no push
   int partials_only;     // nonzero: with more than one item, every item leaves its chunk
                          // partial (plain stores) and the consumer of `out` combines them
-  int split;             // nonzero: each stream's legal slots are split evenly over n_chunks
+  int split;             // nonzero: each stream's legal slots are dealt round-robin to n_chunks
                          // items (chunk unused), at most kAttnSplitList per item
 };
 // Most legal slots one item of a split attention launch takes (its slot list lives in LDS).
