@@ -363,3 +363,34 @@ def test_resume_from_exported_rings(sd):
         b.step(x2, p)
         np.testing.assert_array_equal(x1.cpu().numpy(), x2.cpu().numpy())
     assert read_pos_ring(sd, b, 0, cfg.ring).tolist().count(INVALID_POS) == 0
+
+
+def test_repeated_step_at_one_position_matches_single_steps(sd):
+    # bench.py times fixed positions by stepping p again and again after set_next_position(p):
+    # each repetition re-stamps slot p with p and rewrites its K/V rows, so every repetition must
+    # equal a single step at p over the same imported history (the oracle's import + one step).
+    cfg = SMALL_T
+    layers, final = weights(cfg)
+    p = 23
+    pre = wl.make_prefill(cfg, n_pos=p, streams=[0])[0]
+    dec = make(sd, cfg)
+    pos_ring = np.full(cfg.ring, INVALID_POS, np.uint32)
+    pos_ring[:p] = np.arange(p, dtype=np.uint32)
+    for li in range(cfg.n_layers):
+        kp, vp, pp = dec.kv_view(0, li)
+        sd.copy_to_device(kp, pre[0][li])
+        sd.copy_to_device(vp, pre[1][li])
+    sd.copy_to_device(pp, pos_ring)
+    xs = wl.make_inputs(cfg, 4)
+    x = torch.empty((cfg.m, cfg.d_model), device="cuda")
+    for i in range(4):
+        orc = oracle.OracleDecoder(cfg, layers, final)
+        orc.import_kv(0, pre[0], pre[1], np.arange(p))
+        want = orc.step(xs[i], p)
+        dec.set_next_position(p)
+        x.copy_(torch.from_numpy(xs[i]))
+        dec.step(x, p)
+        cos, mx = assert_close_rows(x.cpu().numpy(), want, f"repeat {i} at pos {p}")
+        np.testing.assert_array_equal(read_pos_ring(sd, dec, 0, cfg.ring), orc.P[0])
+    log(f"repeated steps at pos {p}: cos {cos:.9f} max|d| {mx:.3e}")
+    dec.close()
