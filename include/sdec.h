@@ -285,11 +285,19 @@ typedef struct sdec_conv_config {
   uint32_t max_t_in;        /* largest frame, in input columns */
 } sdec_conv_config;
 typedef struct sdec_conv sdec_conv;
+/* The handle owns two state buffers (the carried prefix or tail, ping-pong) and, for groups == 1
+ * with more than 32 input channels, a partial-sum buffer for up to 16 input-channel splits of a
+ * max_t_in frame.  Errors: SDEC_E_ARG (null pointers, channels outside [1, 65535], kernel <
+ * stride, groups other than 1 or channel-wise, max_t_in == 0, replicate_first / accumulate on a
+ * transposed conv), SDEC_E_NOMEM. */
 int sdec_conv_create(const sdec_conv_config* cfg, const float* w, const float* b, sdec_conv** out);
-/* One frame.  first != 0 starts a fresh stream (the carried state is ignored).  Asynchronous. */
+/* One frame.  first != 0 starts a fresh stream (the carried state is ignored).  Asynchronous.
+ * Errors (checked before anything is enqueued): SDEC_E_ARG for a null x / y, t_in outside
+ * [1, max_t_in] or (conv) not a multiple of stride; SDEC_E_POS for a first frame without first;
+ * SDEC_E_HIP for a failed launch.  Steps of one handle must not overlap (they share its state). */
 int sdec_conv_step(sdec_conv* c, const float* x, uint32_t t_in, float* y, uint32_t first,
                    void* stream);
-/* Release the state buffers (synchronizes the device first).  NULL is accepted. */
+/* Release the handle's buffers (synchronizes the device first).  NULL is accepted. */
 void sdec_conv_destroy(sdec_conv* c);
 
 #ifdef __cplusplus
