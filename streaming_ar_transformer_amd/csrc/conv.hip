@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include "dev.h"
 #include "kernels.h"
 
 namespace sdec {
@@ -92,6 +93,49 @@ __global__ __launch_bounds__(64) void k_sconvtr(SConvTrArgs a) {
 constexpr uint32_t kConvTileThreads = 256;
 constexpr int kConvStageBatch = 8;
 
+// Quotient and remainder by a divisor fixed for the launch, for dividends below 2^24: the float
+// estimate e * (1/d) is within one of the quotient (both operands exact in float32, the product
+// off by under 2 ulp of a value below 2^24), and one remainder test corrects it.  A few
+// instructions instead of the ~30 of an integer division, which dominated the staging loops.
+struct FastDiv {
+  uint32_t d;
+  float inv;
+  __device__ explicit FastDiv(uint32_t dv) : d(dv), inv(1.0f / static_cast<float>(dv)) {}
+  __device__ __forceinline__ uint32_t div(uint32_t e, uint32_t& rem) const {
+    uint32_t q = static_cast<uint32_t>(static_cast<float>(e) * inv);
+    int32_t r = static_cast<int32_t>(e) - static_cast<int32_t>(q * d);
+    if (r < 0) {
+      --q;
+      r += static_cast<int32_t>(d);
+    } else if (r >= static_cast<int32_t>(d)) {
+      ++q;
+      r -= static_cast<int32_t>(d);
+    }
+    rem = static_cast<uint32_t>(r);
+    return q;
+  }
+};
+
+// Split-k hand-off: every split of an output tile leaves its partial sum with a device-coherent
+// store and counts itself in the tile's counter; the last one to arrive (nothing waits) reads
+// the others' partials back with device-coherent loads and finishes the tile.  Returns whether
+// this workgroup is that last one; it also resets the counter for the next launch.
+__device__ __forceinline__ bool conv_split_arrive(uint32_t* counter, uint32_t splits, bool live,
+                                                  float* slot, float acc) {
+  __shared__ uint32_t last;
+  if (live) dev::st_dev(slot, acc);
+  dev::wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == splits - 1 ? 1u : 0u;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return last != 0;
+}
+
 // Fills n LDS elements, kConvStageBatch per thread per batch: the batch's global loads are all
 // issued before any result is used (indices clamped into [0, n), so no branch guards a load), so
 // a thread waits about one memory round trip per batch instead of one per element.
@@ -111,6 +155,10 @@ __device__ __forceinline__ void conv_stage(uint32_t n, Load load, Store store) {
 
 // With gridDim.z > 1 the input channels are split: workgroup z sums channels [z * ics, (z+1) * ics)
 // without the bias into part[z], and k_sconv_sum adds the splits in order.
+// KT: the kernel size when it is one of the unrolled ones (1, 3, 7), else 0 (a.k at run time).
+// Unrolled, the LDS reads of several input channels are issued before their products are summed,
+// instead of one LDS round trip per product.
+template <int KT>
 __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, uint32_t oc_t,
                                                                   uint32_t t_t, uint32_t icb,
                                                                   uint32_t ics) {
@@ -136,16 +184,20 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, u
     // unconditional load per element.
     const uint32_t c_lo = col0 * a.stride;
     const uint32_t n_pre = c_lo < a.pad ? min(a.pad - c_lo, xw) : 0u, wx = xw - n_pre;
+    const FastDiv dwx(wx);
     conv_stage(
         nb * wx,
         [&](uint32_t e) {
-          const uint32_t col = c_lo + n_pre + e % wx;
-          const float v = a.x[static_cast<size_t>(ic0 + e / wx) * a.t_in +
-                              min(col - a.pad, a.t_in - 1)];
+          uint32_t j;
+          const uint32_t i = dwx.div(e, j);
+          const uint32_t col = c_lo + n_pre + j;
+          const float v = a.x[static_cast<size_t>(ic0 + i) * a.t_in + min(col - a.pad, a.t_in - 1)];
           return col < a.t_in + a.pad ? v : 0.f;
         },
         [&](uint32_t e, float v) {
-          X[(e / wx) * xw + n_pre + e % wx] = a.pre_elu ? elu_f(v) : v;
+          uint32_t j;
+          const uint32_t i = dwx.div(e, j);
+          X[i * xw + n_pre + j] = a.pre_elu ? elu_f(v) : v;
         });
     if (n_pre) {
       // the prefix, or on the first frame zeros or copies of the frame's first column
@@ -162,30 +214,52 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, u
           });
     }
     // W[o][i][k] for output channel oc0 + o (zero past c_out)
+    const FastDiv dnk(nb * a.k);
     conv_stage(
         oc_t * nb * a.k,
         [&](uint32_t e) {
-          const uint32_t o = e / (nb * a.k), r = e % (nb * a.k);
+          uint32_t r;
+          const uint32_t o = dnk.div(e, r);
           return a.w[(static_cast<size_t>(min(oc0 + o, a.c_out - 1)) * a.c_in + ic0) * a.k + r];
         },
         [&](uint32_t e, float v) {
-          const uint32_t o = e / (nb * a.k), r = e % (nb * a.k);
+          uint32_t r;
+          const uint32_t o = dnk.div(e, r);
           W[o * icb * a.k + r] = oc0 + o < a.c_out ? v : 0.f;
         });
     __syncthreads();
     if (live) {
       const float* wr = W + ocl * icb * a.k;
-      for (uint32_t i = 0; i < nb; ++i) {
-        const float* xr = X + i * xw + otl * a.stride;
-        for (uint32_t k = 0; k < a.k; ++k) acc = fmaf(wr[i * a.k + k], xr[k], acc);
+      if constexpr (KT > 0) {
+#pragma unroll 4
+        for (uint32_t i = 0; i < nb; ++i) {
+          const float* xr = X + i * xw + otl * a.stride;
+#pragma unroll
+          for (int k = 0; k < KT; ++k) acc = fmaf(wr[i * KT + k], xr[k], acc);
+        }
+      } else {
+        for (uint32_t i = 0; i < nb; ++i) {
+          const float* xr = X + i * xw + otl * a.stride;
+          for (uint32_t k = 0; k < a.k; ++k) acc = fmaf(wr[i * a.k + k], xr[k], acc);
+        }
       }
     }
   }
-  if (live) {
-    if (split) {
-      a.part[(static_cast<size_t>(blockIdx.z) * a.c_out + oc) * t_out + ot] = acc;
+  if (split) {
+    const size_t plane = static_cast<size_t>(a.c_out) * t_out, e = static_cast<size_t>(oc) * t_out + ot;
+    if (a.counters == nullptr) {  // k_sconv_sum finishes the tiles
+      if (live) a.part[blockIdx.z * plane + e] = acc;
       return;
     }
+    float* mine = a.part + blockIdx.z * plane + e;
+    if (!conv_split_arrive(a.counters + blockIdx.y * gridDim.x + blockIdx.x, gridDim.z, live, mine,
+                           acc))
+      return;
+    if (!live) return;
+    acc = a.b[oc];  // the bias, then the splits in order
+    for (uint32_t z = 0; z < gridDim.z; ++z) acc += dev::ld_dev(a.part + z * plane + e);
+  }
+  if (live) {
     float* y = a.y + static_cast<size_t>(oc) * t_out + ot;
     *y = a.accumulate ? *y + acc : acc;
   }
@@ -235,21 +309,33 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconvtr_tiled(SConvTrArgs 
   const uint32_t oc = oc0 + ocl, i = i0 + il;
   const bool live = oc < a.c_out && i < len;
   float acc = live && !split ? a.b[oc] : 0.f;
+  const FastDiv dxw(xw > 0 ? xw : 1u), dok(oc_t * a.k), dk(a.k);
   for (uint32_t ic0 = ic_begin; ic0 < ic_end; ic0 += icb) {
     const uint32_t nb = min(icb, ic_end - ic0);
     __syncthreads();
     conv_stage(
         nb * xw,
-        [&](uint32_t e) { return a.x[static_cast<size_t>(ic0 + e / xw) * a.t_in + lo + e % xw]; },
-        [&](uint32_t e, float v) { X[(e / xw) * xcap + e % xw] = a.pre_elu ? elu_f(v) : v; });
+        [&](uint32_t e) {
+          uint32_t j;
+          const uint32_t c = dxw.div(e, j);
+          return a.x[static_cast<size_t>(ic0 + c) * a.t_in + lo + j];
+        },
+        [&](uint32_t e, float v) {
+          uint32_t j;
+          const uint32_t c = dxw.div(e, j);
+          X[c * xcap + j] = a.pre_elu ? elu_f(v) : v;
+        });
     conv_stage(
         nb * oc_t * a.k,
         [&](uint32_t e) {
-          const uint32_t c = e / (oc_t * a.k), r = e % (oc_t * a.k), o = r / a.k, k = r % a.k;
+          uint32_t r, k;
+          const uint32_t c = dok.div(e, r), o = dk.div(r, k);
           return a.w[(static_cast<size_t>(ic0 + c) * a.c_out + min(oc0 + o, a.c_out - 1)) * a.k + k];
         },
         [&](uint32_t e, float v) {
-          const uint32_t o = (e % (oc_t * a.k)) / a.k;
+          uint32_t r, k;
+          dok.div(e, r);
+          const uint32_t o = dk.div(r, k);
           W[e] = oc0 + o < a.c_out ? v : 0.f;
         });
     __syncthreads();
@@ -259,15 +345,26 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconvtr_tiled(SConvTrArgs 
         if (ti >= a.t_in) continue;
         const float* xr = X + (ti - lo);
         const float* wr = W + ocl * a.k + k;
+#pragma unroll 8
         for (uint32_t c = 0; c < nb; ++c) acc = fmaf(wr[c * oc_t * a.k], xr[c * xcap], acc);
       }
     }
   }
-  if (!live) return;
   if (split) {
-    a.part[(static_cast<size_t>(blockIdx.z) * a.c_out + oc) * len + i] = acc;
-    return;
+    const size_t plane = static_cast<size_t>(a.c_out) * len, e = static_cast<size_t>(oc) * len + i;
+    if (a.counters == nullptr) {  // k_sconvtr_sum finishes the tiles
+      if (live) a.part[blockIdx.z * plane + e] = acc;
+      return;
+    }
+    float* mine = a.part + blockIdx.z * plane + e;
+    if (!conv_split_arrive(a.counters + blockIdx.y * gridDim.x + blockIdx.x, gridDim.z, live, mine,
+                           acc))
+      return;
+    if (!live) return;
+    acc = a.b[oc];  // the bias, then the splits in order
+    for (uint32_t z = 0; z < gridDim.z; ++z) acc += dev::ld_dev(a.part + z * plane + e);
   }
+  if (!live) return;
   sconvtr_emit(a, oc, i, acc);
 }
 
@@ -322,13 +419,18 @@ hipError_t launch_sconv(const SConvArgs& a, hipStream_t s) {
     const uint32_t splits = a.part ? conv_splits(g.x * g.y, a.c_in,
                                                  static_cast<uint64_t>(a.c_out) * t_out, a.part_cap, &ics)
                                    : 1u;
-    hipLaunchKernelGGL(k_sconv_tiled, dim3(g.x, g.y, splits), dim3(kConvTileThreads), lds, s, a,
-                       oc_t, t_t, kConvIcb, ics);
-    if (splits > 1) {
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+    const void* fn = a.k == 1   ? reinterpret_cast<const void*>(&k_sconv_tiled<1>)
+                     : a.k == 3 ? reinterpret_cast<const void*>(&k_sconv_tiled<3>)
+                     : a.k == 7 ? reinterpret_cast<const void*>(&k_sconv_tiled<7>)
+                                : reinterpret_cast<const void*>(&k_sconv_tiled<0>);
+    SConvArgs args = a;
+    if (splits <= 1 || static_cast<uint64_t>(g.x) * g.y > a.counter_cap) args.counters = nullptr;
+    uint32_t p_oc = oc_t, p_t = t_t, p_icb = kConvIcb, p_ics = ics;
+    void* params[] = {&args, &p_oc, &p_t, &p_icb, &p_ics};
+    hipError_t le = hipLaunchKernel(fn, dim3(g.x, g.y, splits), dim3(kConvTileThreads), params, lds, s);
+    if (le != hipSuccess) return le;
+    if (splits > 1 && args.counters == nullptr)
       hipLaunchKernelGGL(k_sconv_sum, dim3((a.c_out * t_out + 255) / 256), dim3(256), 0, s, a, splits);
-    }
   } else {
     hipLaunchKernelGGL(k_sconv, dim3((t_out + 63) / 64, a.c_out), dim3(64), 0, s, a);
   }
@@ -352,9 +454,11 @@ hipError_t launch_sconvtr(const SConvTrArgs& a, hipStream_t s) {
     const uint32_t splits = a.part ? conv_splits(g.x * g.y, a.c_in,
                                                  static_cast<uint64_t>(a.c_out) * len, a.part_cap, &ics)
                                    : 1u;
-    hipLaunchKernelGGL(k_sconvtr_tiled, dim3(g.x, g.y, splits), dim3(kConvTileThreads), lds, s, a,
+    SConvTrArgs args = a;
+    if (splits <= 1 || static_cast<uint64_t>(g.x) * g.y > a.counter_cap) args.counters = nullptr;
+    hipLaunchKernelGGL(k_sconvtr_tiled, dim3(g.x, g.y, splits), dim3(kConvTileThreads), lds, s, args,
                        oc_t, t_t, kConvIcb, ics);
-    if (splits > 1) {
+    if (splits > 1 && args.counters == nullptr) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(k_sconvtr_sum, dim3((a.c_out * len + 255) / 256), dim3(256), 0, s, a, splits);

@@ -206,6 +206,8 @@ struct SConvArgs {
   int pre_elu, replicate_first, first, accumulate;
   float* part;             // split-k partial sums [splits][c_out][t_in / stride] (groups == 1)
   uint64_t part_cap;       // floats part holds (0: no split)
+  uint32_t* counters;      // per output tile: splits finished (zero between launches)
+  uint32_t counter_cap;    // tiles the counters cover (0: a separate launch sums the splits)
 };
 hipError_t launch_sconv(const SConvArgs& a, hipStream_t s);
 struct SConvTrArgs {
@@ -219,6 +221,8 @@ struct SConvTrArgs {
   int pre_elu, first;
   float* part;             // split-k partial sums [splits][c_out][t_in * stride + tl] (groups == 1)
   uint64_t part_cap;       // floats part holds (0: no split)
+  uint32_t* counters;      // per output tile: splits finished (zero between launches)
+  uint32_t counter_cap;    // tiles the counters cover (0: a separate launch sums the splits)
 };
 // Most input-channel splits a streaming conv launch uses (its partial-sum scratch is sized for it).
 constexpr uint32_t kConvMaxSplits = 16;

@@ -1115,6 +1115,8 @@ struct sdec_conv {
   float* state[2] = {nullptr, nullptr};  // prefix [in_ch][k - s] or tail [out_ch][k - s]
   float* part = nullptr;                 // split-k partial sums (groups == 1)
   uint64_t part_cap = 0;
+  uint32_t* counters = nullptr;          // per output tile: splits finished
+  uint32_t counter_cap = 0;
   int cur = 0;
   bool started = false;
 };
@@ -1150,6 +1152,11 @@ int sdec_conv_create(const sdec_conv_config* cfg, const float* w, const float* b
     if (splits > 1) {
       h->part_cap = splits * c.out_ch * cols;
       h->part = A.get<float>(h->part_cap);
+      // output tiles are at least 16 columns x 4 channels
+      h->counter_cap = static_cast<uint32_t>(((cols + 15) / 16) * ((c.out_ch + 3) / 4));
+      h->counters = A.get<uint32_t>(h->counter_cap);
+      if (h->counters && hipMemset(h->counters, 0, sizeof(uint32_t) * h->counter_cap) != hipSuccess)
+        A.code = fail(SDEC_E_HIP, "clearing the conv tile counters failed");
     }
   }
   if (A.code != SDEC_OK) {
@@ -1178,6 +1185,7 @@ int sdec_conv_step(sdec_conv* h, const float* x, uint32_t t_in, float* y, uint32
     a.groups = c.groups; a.t_in = t_in; a.tl = carry; a.pre_elu = c.pre_elu ? 1 : 0;
     a.first = first ? 1 : 0;
     a.part = h->part; a.part_cap = h->part_cap;
+    a.counters = h->counters; a.counter_cap = h->counter_cap;
     HIP_TRY(launch_sconvtr(a, s));
   } else {
     if (t_in % c.stride) return fail(SDEC_E_ARG, "t_in=%u is not a multiple of stride %u", t_in, c.stride);
@@ -1188,6 +1196,7 @@ int sdec_conv_step(sdec_conv* h, const float* x, uint32_t t_in, float* y, uint32
     a.replicate_first = c.replicate_first ? 1 : 0; a.first = first ? 1 : 0;
     a.accumulate = c.accumulate ? 1 : 0;
     a.part = h->part; a.part_cap = h->part_cap;
+    a.counters = h->counters; a.counter_cap = h->counter_cap;
     HIP_TRY(launch_sconv(a, s));
   }
   h->cur ^= 1;
@@ -1201,6 +1210,7 @@ void sdec_conv_destroy(sdec_conv* h) {
   for (float* p : h->state)
     if (p) (void)hipFree(p);
   if (h->part) (void)hipFree(h->part);
+  if (h->counters) (void)hipFree(h->counters);
   delete h;
 }
 
