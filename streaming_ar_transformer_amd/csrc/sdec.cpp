@@ -392,6 +392,19 @@ int enqueue_prefill(sdec_handle* h, float* x, uint32_t pos, uint32_t t, uint32_t
     aa.out = h->attn_out; aa.part = h->part; aa.counters = h->counters;
     aa.m = t; aa.n_q_heads = hq; aa.n_kv_heads = hkv; aa.head_dim = hd; aa.ring = h->ring;
     aa.chunk = h->chunk; aa.n_chunks = h->n_chunks; aa.st = nullptr; aa.partials_only = 0;
+    {
+      // a block's rows attend with 256-slot chunks: half the items of the step's 128 and no merge
+      // below 256 legal slots (blocks of 8 on the talker: 1.84 vs 2.10 ms from position 0, 2.16 vs
+      // 2.54 ms from 1792).  At most one slot per thread in the item's list, and never more items
+      // than the partial buffers hold (they are sized for the step's chunks).  Tuning override:
+      // SDEC_PREFILL_CHUNK.
+      const char* ev = std::getenv("SDEC_PREFILL_CHUNK");
+      const uint32_t pc = ev && *ev ? static_cast<uint32_t>(atoi(ev)) : 256u;
+      if (pc >= h->chunk && pc <= 256 && pc % 64 == 0) {
+        aa.chunk = pc;
+        aa.n_chunks = (h->ring + pc - 1) / pc;
+      }
+    }
     LAUNCH(hk, s, SDEC_K_ATTENTION, launch_attention(aa, s));
     GemvArgs o{};
     o.w[0] = o.w[1] = o.w[2] = w.wo;

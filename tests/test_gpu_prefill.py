@@ -85,6 +85,36 @@ def test_talker_prefill_blocks_then_decode(sd):
     run_blocks(sd, cfg, [8, 3, 8, 1, 5], decode_after=4)
 
 
+def test_talker_prefill_over_long_imported_history(sd):
+    # Blocks whose rows attend 600+ legal slots: several attention chunks per row, merged.
+    cfg = wl.CONFIGS[4]
+    layers, final = weights(cfg)
+    start = 600
+    pre = wl.make_prefill(cfg, n_pos=start, streams=[0])[0]
+    dec = make(sd, cfg, max_prefill=8)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    orc.import_kv(0, pre[0], pre[1], np.arange(start))
+    for li in range(cfg.n_layers):
+        kp, vp, pp = dec.kv_view(0, li)
+        sd.copy_to_device(kp, pre[0][li])
+        sd.copy_to_device(vp, pre[1][li])
+    sd.copy_to_device(pp, orc.P[0])
+    dec.set_next_position(start)
+    xs = wl.make_inputs(cfg, 13)
+    p = start
+    for t in (8, 5):
+        xb = torch.from_numpy(np.ascontiguousarray(xs[p - start:p - start + t, 0])).cuda()
+        print(f"prefill {cfg.name} pos {p} t {t}", flush=True)
+        dec.prefill(xb, p)
+        got = xb.cpu().numpy()
+        want = orc.prefill(xs[p - start:p - start + t, 0], p)
+        cos, mx = assert_close_rows(got, want, f"{cfg.name} prefill block at {p}")
+        np.testing.assert_array_equal(read_pos_ring(sd, dec, cfg.ring), orc.P[0])
+        p += t
+    dec.close()
+    log(f"{cfg.name} prefill over {start} imported positions: cos {cos:.9f} max|d| {mx:.3e}")
+
+
 def test_codec_prefill_across_ring_wraps(sd):
     # ring = window + 7: any block of up to 8 rows is legal after the ring wraps (257, 514)
     cfg = wl.CONFIGS[3]
