@@ -620,16 +620,18 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   if (single || a.partials_only) return;
 
   // 6. the last chunk of this (stream, kv head) to finish merges all chunks.  The partials went
-  // out with device-coherent stores; they are complete before this workgroup's count is added.
-  wait_stores();
+  // out with device-coherent stores, released at agent scope by every thread before the count
+  // (an agent-scope acquire-release RMW) is added; the merging workgroup acquires before it reads.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&a.counters[s * hkv + kvh], 1u, __ATOMIC_RELAXED,
+    const uint32_t prev = __hip_atomic_fetch_add(&a.counters[s * hkv + kvh], 1u, __ATOMIC_ACQ_REL,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     is_last = prev == n_items - 1 ? 1u : 0u;
   }
   __syncthreads();
   if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   float* stage = &sm_acc[0][0][0];  // [CB][G][HD]
   float Mr[(G * HD + NT - 1) / NT], Lr[(G * HD + NT - 1) / NT];
   float Or[(G * HD + NT - 1) / NT];

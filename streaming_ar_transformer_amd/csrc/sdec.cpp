@@ -522,6 +522,66 @@ int setup_persistent(sdec_handle* h) {
   return SDEC_OK;
 }
 
+// One-shot ring attention (sdec_ring_attention and its variant without allocation): argument
+// checks, the scratch each call needs, and the launches.
+int check_ring_attention(const float* q, const float* k_ring, const float* v_ring,
+                         const uint32_t* pos_ring, const float* out, uint32_t m,
+                         uint32_t n_q_heads, uint32_t n_kv_heads, uint32_t head_dim,
+                         uint32_t ring_slots, uint32_t window) {
+  if (!q || !k_ring || !v_ring || !pos_ring || !out) return fail(SDEC_E_ARG, "null pointer");
+  if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring))
+    return fail(SDEC_E_ARG, "q and the rings must be 16-byte aligned");
+  if (head_dim != 64 && head_dim != 128) return fail(SDEC_E_ARG, "head_dim must be 64 or 128");
+  if (!n_kv_heads || !n_q_heads || n_q_heads % n_kv_heads) return fail(SDEC_E_ARG, "bad heads");
+  const uint32_t group = n_q_heads / n_kv_heads;
+  if (group != 1 && group != 2 && group != 4) return fail(SDEC_E_ARG, "GQA group must be 1, 2 or 4");
+  if (m < 1 || m > static_cast<uint32_t>(kMaxM) || ring_slots < 1 || window < 1)
+    return fail(SDEC_E_ARG, "bad m, ring_slots or window");
+  return SDEC_OK;
+}
+
+struct OneShotSizes {
+  uint32_t chunk, n_chunks;
+  size_t part;      // floats: chunk partials [m][Hq][n_chunks][hd + 2]
+  size_t counters;  // words: [m][Hkv]
+  size_t legal;     // words: legal-slot lists [m][R], then the counts [m]
+};
+
+OneShotSizes one_shot_sizes(uint32_t m, uint32_t n_q_heads, uint32_t n_kv_heads,
+                            uint32_t head_dim, uint32_t ring_slots) {
+  OneShotSizes z;
+  z.chunk = attention_chunk(head_dim);
+  z.n_chunks = (ring_slots + z.chunk - 1) / z.chunk;
+  z.part = static_cast<size_t>(m) * n_q_heads * z.n_chunks * (head_dim + 2);
+  z.counters = static_cast<size_t>(m) * n_kv_heads;
+  z.legal = static_cast<size_t>(m) * ring_slots + m;
+  return z;
+}
+
+// Needs counters [m][Hkv] at zero; leaves them at zero.
+int enqueue_ring_attention(const float* q, const float* k_ring, const float* v_ring,
+                           const uint32_t* pos_ring, float* out, uint32_t m, uint32_t n_q_heads,
+                           uint32_t n_kv_heads, uint32_t head_dim, uint32_t ring_slots,
+                           uint32_t window, uint32_t pos, float* part, uint32_t* counters,
+                           uint32_t* legal, hipStream_t s) {
+  const OneShotSizes z = one_shot_sizes(m, n_q_heads, n_kv_heads, head_dim, ring_slots);
+  uint32_t* n_legal = legal + static_cast<size_t>(m) * ring_slots;
+  HIP_TRY(launch_compact_legal(pos_ring, m, ring_slots, pos, window, legal, n_legal, s));
+  AttnArgs a{};
+  a.qkv = q; a.qkv_stride = n_q_heads * head_dim;
+  a.q_norm = a.k_norm = nullptr; a.cs = nullptr; a.push = 0;
+  a.k_ring = const_cast<float*>(k_ring); a.v_ring = const_cast<float*>(v_ring);
+  a.ring_stream_stride = static_cast<uint64_t>(ring_slots) * n_kv_heads * head_dim;
+  a.legal = legal; a.n_legal = n_legal; a.out = out; a.part = part;
+  a.counters = counters; a.m = m; a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads;
+  a.head_dim = head_dim; a.ring = ring_slots; a.chunk = z.chunk;
+  a.n_chunks = z.n_chunks; a.st = nullptr;
+  // a head with no legal slot gets zeros: the attention kernel skips items past the legal count
+  HIP_TRY(launch_fill_f32(out, 0.f, static_cast<uint64_t>(m) * n_q_heads * head_dim, s));
+  HIP_TRY(launch_attention(a, s));
+  return SDEC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -595,7 +655,10 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
     return A.code;
   }
 
-  if (c.m == 1 && hq <= kAttnMaxHeads && static_cast<size_t>(hq) * h->n_chunks <= kAttnMaxPartials) {
+  // the o prologue forms chunk weights for at most kAttnMaxChunks chunks per head; longer rings
+  // merge their chunks in the attention launch instead
+  if (c.m == 1 && hq <= kAttnMaxHeads && h->n_chunks <= kAttnMaxChunks &&
+      static_cast<size_t>(hq) * h->n_chunks <= kAttnMaxPartials) {
     const GemvLaunch fused = plan_gemv(PRO_ATTN, EPI_RESIDUAL, c.d_model, qw, c.m);
     const char* fe = std::getenv("SDEC_ATTN_COMBINE_IN_O");  // tuning override: "0" = combine in attention
     h->attn_fused = gemv_supported(fused, qw, c.m) && !(fe != nullptr && fe[0] == '0');
@@ -853,15 +916,9 @@ int sdec_ring_attention(const float* q, const float* k_ring, const float* v_ring
                         const uint32_t* pos_ring, float* out, uint32_t m, uint32_t n_q_heads,
                         uint32_t n_kv_heads, uint32_t head_dim, uint32_t ring_slots,
                         uint32_t window, uint32_t pos, void* stream) {
-  if (!q || !k_ring || !v_ring || !pos_ring || !out) return fail(SDEC_E_ARG, "null pointer");
-  if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring))
-    return fail(SDEC_E_ARG, "q and the rings must be 16-byte aligned");
-  if (head_dim != 64 && head_dim != 128) return fail(SDEC_E_ARG, "head_dim must be 64 or 128");
-  if (!n_kv_heads || !n_q_heads || n_q_heads % n_kv_heads) return fail(SDEC_E_ARG, "bad heads");
-  const uint32_t group = n_q_heads / n_kv_heads;
-  if (group != 1 && group != 2 && group != 4) return fail(SDEC_E_ARG, "GQA group must be 1, 2 or 4");
-  if (m < 1 || m > static_cast<uint32_t>(kMaxM) || ring_slots < 1 || window < 1)
-    return fail(SDEC_E_ARG, "bad m, ring_slots or window");
+  int r = check_ring_attention(q, k_ring, v_ring, pos_ring, out, m, n_q_heads, n_kv_heads,
+                               head_dim, ring_slots, window);
+  if (r != SDEC_OK) return r;
   // The chunk partials, counters and legal-slot lists live in buffers kept for the life of the
   // process and grown on demand; the counters are returned to zero by each launch.
   static float* part = nullptr;
@@ -870,53 +927,36 @@ int sdec_ring_attention(const float* q, const float* k_ring, const float* v_ring
   static size_t cnt_cap = 0;
   static uint32_t* legal = nullptr;
   static size_t legal_cap = 0;
-  const uint32_t chunk = attention_chunk(head_dim);
-  const uint32_t n_chunks = (ring_slots + chunk - 1) / chunk;
-  const size_t need = static_cast<size_t>(m) * n_q_heads * n_chunks * (head_dim + 2);
+  const OneShotSizes z = one_shot_sizes(m, n_q_heads, n_kv_heads, head_dim, ring_slots);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (need > part_cap) {
+  if (z.part > part_cap) {
     HIP_TRY(hipDeviceSynchronize());
     if (part) HIP_TRY(hipFree(part));
     part = nullptr;
     part_cap = 0;
-    HIP_TRY(hipMalloc(&part, need * sizeof(float)));
-    part_cap = need;
+    HIP_TRY(hipMalloc(&part, z.part * sizeof(float)));
+    part_cap = z.part;
   }
-  const size_t ncnt = static_cast<size_t>(m) * n_kv_heads;
-  if (ncnt > cnt_cap) {
+  if (z.counters > cnt_cap) {
     HIP_TRY(hipDeviceSynchronize());
     if (counters) HIP_TRY(hipFree(counters));
     counters = nullptr;
     cnt_cap = 0;
-    const size_t alloc = ncnt > 64 ? ncnt : 64;
+    const size_t alloc = z.counters > 64 ? z.counters : 64;
     HIP_TRY(hipMalloc(&counters, alloc * sizeof(uint32_t)));
     cnt_cap = alloc;
     HIP_TRY(launch_fill_u32(counters, 0u, cnt_cap, s));
   }
-  const size_t nleg = static_cast<size_t>(m) * ring_slots + m;
-  if (nleg > legal_cap) {
+  if (z.legal > legal_cap) {
     HIP_TRY(hipDeviceSynchronize());
     if (legal) HIP_TRY(hipFree(legal));
     legal = nullptr;
     legal_cap = 0;
-    HIP_TRY(hipMalloc(&legal, nleg * sizeof(uint32_t)));
-    legal_cap = nleg;
+    HIP_TRY(hipMalloc(&legal, z.legal * sizeof(uint32_t)));
+    legal_cap = z.legal;
   }
-  uint32_t* n_legal = legal + static_cast<size_t>(m) * ring_slots;
-  HIP_TRY(launch_compact_legal(pos_ring, m, ring_slots, pos, window, legal, n_legal, s));
-  AttnArgs a{};
-  a.qkv = q; a.qkv_stride = n_q_heads * head_dim;
-  a.q_norm = a.k_norm = nullptr; a.cs = nullptr; a.push = 0;
-  a.k_ring = const_cast<float*>(k_ring); a.v_ring = const_cast<float*>(v_ring);
-  a.ring_stream_stride = static_cast<uint64_t>(ring_slots) * n_kv_heads * head_dim;
-  a.legal = legal; a.n_legal = n_legal; a.out = out; a.part = part;
-  a.counters = counters; a.m = m; a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads;
-  a.head_dim = head_dim; a.ring = ring_slots; a.chunk = chunk;
-  a.n_chunks = n_chunks; a.st = nullptr;
-  // a head with no legal slot gets zeros: the attention kernel skips items past the legal count
-  HIP_TRY(launch_fill_f32(out, 0.f, static_cast<uint64_t>(m) * n_q_heads * head_dim, s));
-  HIP_TRY(launch_attention(a, s));
-  return SDEC_OK;
+  return enqueue_ring_attention(q, k_ring, v_ring, pos_ring, out, m, n_q_heads, n_kv_heads,
+                                head_dim, ring_slots, window, pos, part, counters, legal, s);
 }
 
 }  // extern "C"

@@ -116,7 +116,7 @@ def test_codec2_full_run(sd, persistent):
 @pytest.mark.parametrize("persistent", PATHS, ids=PATH_IDS)
 def test_codec8_full_run(sd, persistent):
     cfg = wl.CONFIGS[3]
-    run_parity(sd, cfg, cfg.steps, ring_check=False, persistent=persistent)
+    run_parity(sd, cfg, cfg.steps, ring_check=True, persistent=persistent)
 
 
 @pytest.mark.parametrize("persistent", PATHS, ids=PATH_IDS)
@@ -183,6 +183,105 @@ def test_talker_last_positions_from_prefill(sd, persistent):
     assert e.value.code == sd.E_CAPACITY
     check_path(sd, dec, persistent)
     dec.close()
+
+
+@pytest.mark.parametrize("p", [130, 300, 600, 1030, 1500])
+def test_talker_mid_positions_from_prefill(sd, p):
+    # Over a seeded import of positions 0..p-1 the step at p attends p+1 slots: 2, 3, 5, 9 and 12
+    # chunks of 128, whose partials the o projection's prologue combines in batches of 4, 8 and 16
+    # (the last two partly filled).
+    cfg = wl.CONFIGS[4]
+    layers, final = weights(cfg)
+    dec = make(sd, cfg)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    _import_prefill(sd, dec, orc, cfg, p, [0])
+    xs = wl.make_inputs(cfg, p + 2)
+    x = torch.empty((1, cfg.d_model), device="cuda")
+    for q in (p, p + 1):
+        log(f"talker step at {q} over a {p}-position import")
+        x.copy_(torch.from_numpy(xs[q]))
+        dec.step(x, q)
+        want = orc.step(xs[q], q)
+        cos, mx = assert_close_rows(x.cpu().numpy(), want, f"talker pos {q}")
+        np.testing.assert_array_equal(read_pos_ring(sd, dec, 0, cfg.ring), orc.P[0])
+    log(f"talker pos {p}..{p + 1}: cos {cos:.9f} max|d| {mx:.3e}")
+    dec.close()
+
+
+def test_talker_one_stream_long_ring_combines_batches(sd):
+    # The talker at one stream over config 5's 4352-slot ring: at positions 4350-4351 the o
+    # prologue combines 34 chunk partials (two full batches of 16, then 2); 4352 is refused.
+    cfg = wl.CONFIGS[5].replace(m=1)
+    layers, final = weights(cfg)
+    dec = make(sd, cfg)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    _import_prefill(sd, dec, orc, cfg, 4350, [0])
+    xs = wl.make_inputs(cfg, 2)
+    x = torch.empty((1, cfg.d_model), device="cuda")
+    for i, q in enumerate((4350, 4351)):
+        log(f"one-stream talker step at {q}")
+        x.copy_(torch.from_numpy(xs[i]))
+        dec.step(x, q)
+        want = orc.step(xs[i], q)
+        cos, mx = assert_close_rows(x.cpu().numpy(), want, f"talker R4352 pos {q}")
+    np.testing.assert_array_equal(read_pos_ring(sd, dec, 0, cfg.ring), orc.P[0])
+    with pytest.raises(sd.SdecError) as e:
+        dec.step(x, 4352)
+    assert e.value.code == sd.E_CAPACITY
+    log(f"one-stream talker R4352: cos {cos:.9f} max|d| {mx:.3e}")
+    dec.close()
+
+
+LONG_C = wl.small_config("C", n_layers=2, ring=8320, window=8320, steps=8202)
+
+
+def test_codec_one_stream_more_than_64_chunks(sd):
+    # An 8-head, head_dim-64 stack at one stream with an 8320-slot ring: past position 8191 more
+    # than 64 chunks of 128 slots are legal, more than the o prologue's combine takes, so the
+    # chunks merge in the attention launch; the outputs still match the oracle.
+    cfg = LONG_C
+    layers, final = weights(cfg)
+    dec = make(sd, cfg)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    _import_prefill(sd, dec, orc, cfg, 8200, [0])
+    xs = wl.make_inputs(cfg, 2)
+    x = torch.empty((1, cfg.d_model), device="cuda")
+    for i, q in enumerate((8200, 8201)):
+        log(f"codec R8320 step at {q}")
+        x.copy_(torch.from_numpy(xs[i]))
+        dec.step(x, q)
+        want = orc.step(xs[i], q)
+        cos, mx = assert_close_rows(x.cpu().numpy(), want, f"codec R8320 pos {q}")
+        assert_close_rows(x.cpu().numpy() - xs[i], want - xs[i], f"codec R8320 pos {q} y-x")
+    np.testing.assert_array_equal(read_pos_ring(sd, dec, 0, cfg.ring), orc.P[0])
+    log(f"codec R8320: cos {cos:.9f} max|d| {mx:.3e}")
+    dec.close()
+
+
+def test_talker_m8_last_positions_and_capacity(sd):
+    # All 8 streams at positions 4350-4351 over a seeded 4350-position import (the last two steps
+    # of the m=8 run); position 4352 is past the 4352-slot ring and is refused.
+    cfg = wl.CONFIGS[5]
+    layers, final = weights(cfg)
+    dec = make(sd, cfg)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    _import_prefill(sd, dec, orc, cfg, 4350, list(range(cfg.m)))
+    xs = wl.make_inputs(cfg, 256)
+    x = torch.empty((cfg.m, cfg.d_model), device="cuda")
+    for q in (4350, 4351):
+        log(f"m8 step at {q}")
+        x.copy_(torch.from_numpy(xs[q - cfg.start_pos]))
+        dec.step(x, q)
+        want = orc.step(xs[q - cfg.start_pos], q)
+        cos, mx = assert_close_rows(x.cpu().numpy(), want, f"m8 pos {q}")
+        for s in range(cfg.m):
+            np.testing.assert_array_equal(read_pos_ring(sd, dec, s, cfg.ring), orc.P[s])
+    with pytest.raises(sd.SdecError) as e:
+        dec.step(x, 4352)
+    assert e.value.code == sd.E_CAPACITY
+    log(f"m8 pos 4350..4351: cos {cos:.9f} max|d| {mx:.3e}")
+    dec.close()
+    del orc
 
 
 def test_talker_m8_from_prefill(sd):

@@ -620,3 +620,90 @@ def test_conv_transpose1d_is_the_library_convolution(stride, k, groups, pre_elu)
                                    stride=stride, groups=groups)[0].numpy()
     np.testing.assert_allclose(y, ref, rtol=1e-6, atol=1e-6)
     assert oracle.streamed_conv_transpose1d(x, w, b, stride, pre_elu, groups).shape == (cout, T * stride)
+
+
+def _overlap_add_frames(x, w, b, stride, frame_cols):
+    # Frame-by-frame transposed convolution written from the definition with scalar float64
+    # loops: input column t adds w[i, o, k] * x[i, t] to output column t*stride + k; a column is
+    # emitted once no later input column can reach it (column j < (t_end) * stride after a frame
+    # ending at input column t_end), the rest stays pending.  Single group, no ELU.
+    c_in, T = x.shape
+    _, c_out, K = w.shape
+    acc = {}  # output column -> per-channel float64 sums (bias added when emitted)
+    out = []
+    t0 = 0
+    while t0 < T:
+        t1 = min(T, t0 + frame_cols)
+        for t in range(t0, t1):
+            for k in range(K):
+                col = acc.setdefault(t * stride + k, [0.0] * c_out)
+                for o in range(c_out):
+                    col[o] += sum(float(w[i, o, k]) * float(x[i, t]) for i in range(c_in))
+        for j in range(t0 * stride, t1 * stride):
+            col = acc.pop(j, [0.0] * c_out)
+            out.append([float(b[o]) + col[o] for o in range(c_out)])
+        t0 = t1
+    return np.array(out, np.float64).T  # [c_out, T * stride]
+
+
+@pytest.mark.parametrize("stride,k,frame_cols", [(2, 4, 1), (3, 7, 2), (4, 4, 3), (2, 5, 5)])
+def test_streamed_conv_transpose1d_is_frame_by_frame_overlap_add(stride, k, frame_cols):
+    # The streamed result is what frame-by-frame overlap-add emits: its first T*stride columns,
+    # not its last ones, and not shifted by the K - stride pending columns.
+    rng = np.random.default_rng(70 + k)
+    cin, cout, T = 3, 2, 6
+    x = rng.standard_normal((cin, T)).astype(F32)
+    w = rng.standard_normal((cin, cout, k)).astype(F32)
+    b = rng.standard_normal(cout).astype(F32)
+    y = oracle.streamed_conv_transpose1d(x, w, b, stride)
+    ref = _overlap_add_frames(x, w, b, stride, frame_cols)
+    assert y.shape == ref.shape == (cout, T * stride)
+    np.testing.assert_allclose(y, ref, rtol=1e-6, atol=1e-6)
+    # a prefix of the input emits a prefix of the output
+    y3 = oracle.streamed_conv_transpose1d(x[:, :3], w, b, stride)
+    np.testing.assert_allclose(y3, y[:, :3 * stride], rtol=1e-6, atol=1e-6)
+
+
+def test_streamed_conv_transpose1d_is_a_prefix_of_the_library_convolution():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(77)
+    cin, cout, T, stride, k = 4, 3, 7, 5, 10
+    x = rng.standard_normal((cin, T)).astype(F32)
+    w = rng.standard_normal((cin, cout, k)).astype(F32)
+    b = rng.standard_normal(cout).astype(F32)
+    ref = torch.nn.functional.conv_transpose1d(
+        torch.from_numpy(x)[None].double(), torch.from_numpy(w).double(),
+        torch.from_numpy(b).double(), stride=stride)[0].numpy()
+    y = oracle.streamed_conv_transpose1d(x, w, b, stride)
+    np.testing.assert_allclose(y, ref[:, :T * stride], rtol=1e-6, atol=1e-6)
+
+
+def test_rvq_first_and_rest_projections_are_not_interchangeable():
+    # Distinct, non-identity projections on a latent twice the quantiser width: in_first = [2I | 0]
+    # sees the first half doubled, in_rest = [0 | P] a permutation of the second half; out_first =
+    # [2I ; 0] writes the first group's code vector doubled into the first half, out_rest = [0 ; Q]
+    # the rest group's sum permuted into the second half.  Codes are planted in both halves, so
+    # swapping a first projection with its rest one changes the codes or the decoded latent.
+    vq, bins, nq = 16, 32, 4
+    _, cb_first, cb_rest = _rvq_identity(nq=nq, vq=vq, bins=bins)
+    rng = np.random.default_rng(34)
+    perm = rng.permutation(vq)
+    qperm = rng.permutation(vq)
+    z = np.zeros((vq, vq), F32)
+    in_first = np.concatenate([2 * np.eye(vq, dtype=F32), z], axis=1)
+    P = np.eye(vq, dtype=F32)[perm]  # (P w)[i] = w[perm[i]]
+    in_rest = np.concatenate([z, P], axis=1)
+    out_first = np.concatenate([2 * np.eye(vq, dtype=F32), z], axis=0)
+    Q = np.eye(vq, dtype=F32)[qperm]
+    out_rest = np.concatenate([z, Q], axis=0)
+    q = oracle.OracleRVQ(in_first, in_rest, out_first, out_rest, cb_first, cb_rest)
+    c0, planted = 11, [5, 17, 30]
+    s = ((cb_rest[0, 5] + cb_rest[1, 17]).astype(F32) + cb_rest[2, 30]).astype(F32)
+    x = np.zeros(2 * vq, F32)
+    x[:vq] = cb_first[0, c0] / F32(2)
+    x[vq + perm] = s  # so that (P x_rest)[i] = s[i]
+    codes = q.encode(x)
+    assert list(codes) == [c0] + planted
+    y = q.decode(codes)
+    want = np.concatenate([2 * cb_first[0, c0], s[qperm]]).astype(F32)
+    np.testing.assert_array_equal(y, want)
