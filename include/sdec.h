@@ -46,7 +46,6 @@ enum { SDEC_FFN_SWIGLU = 0, SDEC_FFN_GELU_ERF = 1 };
 /* sdec_config.flags */
 #define SDEC_FLAG_EAGER 1u /* launch kernels one by one per step instead of replaying a graph */
 #define SDEC_FLAG_TAPS 2u  /* keep per-layer branch outputs readable through sdec_tap_view */
-#define SDEC_FLAG_PERSISTENT 4u /* run each step as one persistent cooperative launch */
 
 /* Geometry and options of one decoder stack ([talker] Dims; [mimi] TrShape). */
 typedef struct sdec_config {
@@ -143,12 +142,10 @@ int sdec_reset(sdec_handle* h, void* stream);
  * NULL is accepted. */
 void sdec_destroy(sdec_handle* h);
 
-/* Which step path the handle runs: 0 = per-kernel launches replayed from a hipGraph, 1 = per-kernel
- * eager launches, 2 = one persistent cooperative launch per step (with SDEC_FLAG_PERSISTENT, for a
- * single stream of a geometry the persistent kernel is built for; otherwise the graph path).  *device_error (optional) receives the persistent kernel's sticky error word after a
- * device synchronize: nonzero if a device-wide barrier wait ever timed out, in which case the
- * outputs of that step are not valid. */
-int sdec_status(sdec_handle* h, uint32_t* path, uint32_t* device_error);
+/* Which step path the handle runs: 0 = the per-layer launches recorded once as a hipGraph and
+ * replayed per step ([talker] StepPlan: the plan is built once and replayed per token), 1 = the
+ * same launches enqueued one by one (SDEC_FLAG_EAGER).  path may be NULL. */
+int sdec_status(sdec_handle* h, uint32_t* path);
 
 /* Message of the last failed call on this thread ("" if none).  Valid until the next call. */
 const char* sdec_last_error(void);
@@ -186,15 +183,6 @@ enum {
 };
 int sdec_step_profile(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stream,
                       double* ms, uint32_t* calls);
-
-/* Phase trace of one persistent step (the handle must run the persistent path): runs the step
- * like sdec_step, waits for it, and writes 2 * (1 + 5 * n_layers) + 2 stamps of the device's
- * constant-rate clock (sdec_status path 2 only) into host array ts: ts[2i] when workgroup 0
- * reached device-wide barrier i and ts[2i + 1] when that barrier released it, then the kernel's
- * start and workgroup 0's start of the end phase.  Barriers: 0 after the begin phase, then per
- * layer after QKV, attention, O, FFN up and down.  *clock_hz receives the clock's rate. */
-int sdec_step_trace(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stream,
-                    uint64_t* ts, uint32_t n_ts, double* clock_hz);
 
 /* One-shot GEMV, the step's weight-streaming kernel on its own ([talker] MATVEC_SRC):
  * y[r][i] = sum_j x[r][j] * w[i][j] for r < m (1..8), i < n, with w row-major [n][k]

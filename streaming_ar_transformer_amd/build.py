@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsdec.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
-SOURCES = [os.path.join(PKG, "csrc", n) for n in ("kernels.hip", "step.hip", "rvq.hip", "conv.hip", "sdec.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", n) for n in ("kernels.hip", "rvq.hip", "conv.hip", "sdec.cpp")]
 ARCH = os.environ.get("SDEC_OFFLOAD_ARCH", "gfx950")
 
 

@@ -1,5 +1,4 @@
-// Device helpers shared by the per-kernel step path (kernels.hip) and the persistent step kernel
-// (step.hip).  Page names in citations: [talker] inferencelayer 0.2.8 src/qwen3tts_gpu.rs,
+// Device helpers of the step kernels (kernels.hip).  Page names in citations: [talker] inferencelayer 0.2.8 src/qwen3tts_gpu.rs,
 // [mimi] 0.2.1 src/mimi_gpu.rs.
 #pragma once
 

@@ -228,54 +228,6 @@ struct SConvTrArgs {
 constexpr uint32_t kConvMaxSplits = 16;
 hipError_t launch_sconvtr(const SConvTrArgs& a, hipStream_t s);
 
-// Persistent step kernel (step.hip): one cooperative launch per step for a single stream.
-struct StepLayer {
-  const float *attn_norm_w, *attn_norm_b, *wq, *wk, *wv, *wo, *q_norm, *k_norm, *ls1;
-  const float *ffn_norm_w, *ffn_norm_b, *w_gate, *w_up, *w_down, *ls2;
-  float* k_ring;          // this layer's rings [R][Hkv][hd]
-  float* v_ring;
-  const float* x_in;      // residual stream entering the layer
-  float* qkv;             // [nqkv]        per-layer hand-off buffers, each written once per launch
-  float* attn_out;        // [Hq*hd]
-  float* x_attn;          // [d]  residual after the attention block
-  float* act;             // [d_ff]
-  float* x_ffn;           // [d]  residual after the FFN block
-  float* part;            // [Hq][n_chunks][hd+2]
-  uint32_t* counters;     // [Hkv]
-};
-struct StepArgs {
-  const StepLayer* layers;  // device array [n_layers]
-  uint32_t n_layers, d, hq, hkv, hd, d_ff, nqkv;
-  int norm;                 // PRO_RMS or PRO_LN
-  float eps, qk_eps;
-  int rope_style;
-  double theta;
-  int ffn;                  // EPI_SWIGLU or EPI_GELU
-  int layer_scale, final_norm;
-  uint32_t window, ring, chunk, n_chunks;
-  uint32_t* legal;          // [R]
-  uint32_t* n_legal;        // [1]
-  const float* fin_w;
-  const float* fin_b;
-  float* x0;                // [d] the step's input row
-  uint32_t* pos_ring;       // [R]
-  float* cs;                // [hd]
-  DevState* st;
-  uint64_t* bar;            // monotonic barrier arrival counter
-  uint32_t* err;            // nonzero after a barrier wait timed out
-  // per step
-  const float* x_in;
-  float* x_out;
-  uint32_t pos, first;
-  uint64_t bar_base;        // counter value when this launch starts
-  uint64_t* trace;          // null, or [2 * (barriers + 1)] device-clock stamps (see step.hip)
-};
-uint32_t step_barriers(uint32_t n_layers);
-// hipSuccess and the grid if the persistent kernel serves this geometry on this device.
-hipError_t plan_step(uint32_t head_dim, uint32_t group, uint32_t d_model, uint32_t d_ff,
-                     uint32_t q_width, int norm, int ffn, uint32_t* grid);
-hipError_t launch_step(const StepArgs& a, uint32_t grid, uint32_t group, hipStream_t s);
-
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, uint64_t n, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float value, uint64_t n, hipStream_t s);
 

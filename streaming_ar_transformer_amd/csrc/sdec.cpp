@@ -82,17 +82,6 @@ struct sdec_handle {
   hipGraphExec_t exec = nullptr;
   bool graph_ready = false;
 
-  // persistent single-launch step
-  bool persistent = false;
-  uint32_t step_grid = 0;
-  uint32_t step_group = 0;
-  StepArgs step{};            // static fields; per-step fields are filled per launch
-  StepLayer* step_layers = nullptr;  // device array
-  float* step_bufs = nullptr;        // per-layer hand-off buffers + the input row
-  uint64_t* bar = nullptr;
-  uint32_t* err = nullptr;
-  uint64_t bar_base = 0;
-
   bool has_next = false;
   uint32_t next_pos = 0;
 };
@@ -120,8 +109,7 @@ struct Alloc {
 
 void free_handle_memory(sdec_handle* h) {
   void* ps[] = {h->k_rings, h->v_rings, h->pos_rings, h->legal, h->n_legal, h->xres, h->qkv, h->attn_out,
-                h->act, h->part, h->counters, h->cs, h->st, h->tap_attn_proj, h->tap_ffn_proj,
-                h->step_layers, h->step_bufs, h->bar, h->err};
+                h->act, h->part, h->counters, h->cs, h->st, h->tap_attn_proj, h->tap_ffn_proj};
   for (void* p : ps)
     if (p) (void)hipFree(p);
 }
@@ -445,80 +433,6 @@ int clear_state(sdec_handle* h, hipStream_t s) {
   HIP_TRY(launch_fill_f32(h->v_rings, 0.f, nkv, s));
   HIP_TRY(launch_fill_u32(h->pos_rings, kInvalidPos, static_cast<uint64_t>(c.m) * h->ring, s));
   HIP_TRY(launch_fill_u32(h->counters, 0u, static_cast<uint64_t>(h->rows) * c.n_kv_heads, s));
-  if (h->persistent) {
-    for (uint32_t l = 0; l < c.n_layers; ++l) {
-      // the counters sit inside the per-layer hand-off block; see setup_persistent
-      StepLayer L;
-      HIP_TRY(hipMemcpy(&L, h->step_layers + l, sizeof L, hipMemcpyDeviceToHost));
-      HIP_TRY(launch_fill_u32(L.counters, 0u, c.n_kv_heads, s));
-    }
-    HIP_TRY(launch_fill_u32(h->err, 0u, 1, s));
-    // restart the barrier count with the host's base (a timed-out launch leaves it inconsistent)
-    HIP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(h->bar), 0u, 2, s));
-    h->bar_base = 0;
-  }
-  return SDEC_OK;
-}
-
-// Per-layer hand-off buffers of the persistent kernel, each 256-byte aligned so no two share a
-// cache line, and the device array of per-layer pointers.
-int setup_persistent(sdec_handle* h) {
-  const sdec_config& c = h->cfg;
-  const uint32_t hd = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads;
-  const uint32_t qw = hq * hd, nqkv = qw + 2 * hkv * hd;
-  auto pad = [](size_t n) { return (n + 63) / 64 * 64; };  // floats, to 256 bytes
-  const size_t n_part = static_cast<size_t>(hq) * h->n_chunks * (hd + 2);
-  const size_t per_layer = pad(nqkv) + pad(qw) + pad(c.d_model) + pad(c.d_ff) + pad(c.d_model) +
-                           pad(n_part) + pad(hkv);
-  const size_t total = pad(c.d_model) + per_layer * c.n_layers;
-  hipError_t e = hipMalloc(&h->step_bufs, total * sizeof(float));
-  if (e != hipSuccess) return fail(SDEC_E_NOMEM, "hipMalloc(step buffers): %s", hipGetErrorString(e));
-  HIP_TRY(hipMemset(h->step_bufs, 0, total * sizeof(float)));
-  e = hipMalloc(&h->step_layers, sizeof(StepLayer) * c.n_layers);
-  if (e != hipSuccess) return fail(SDEC_E_NOMEM, "hipMalloc(step layers): %s", hipGetErrorString(e));
-  e = hipMalloc(&h->bar, 64);
-  if (e != hipSuccess) return fail(SDEC_E_NOMEM, "hipMalloc(barrier): %s", hipGetErrorString(e));
-  e = hipMalloc(&h->err, 64);
-  if (e != hipSuccess) return fail(SDEC_E_NOMEM, "hipMalloc(error word): %s", hipGetErrorString(e));
-  HIP_TRY(hipMemset(h->bar, 0, 64));
-  HIP_TRY(hipMemset(h->err, 0, 64));
-  float* x0 = h->step_bufs;
-  float* cur = h->step_bufs + pad(c.d_model);
-  std::vector<StepLayer> L(c.n_layers);
-  const float* x_in = x0;
-  for (uint32_t l = 0; l < c.n_layers; ++l) {
-    const sdec_layer_weights& w = h->layers[l];
-    StepLayer& s = L[l];
-    s.attn_norm_w = w.attn_norm_w; s.attn_norm_b = w.attn_norm_b;
-    s.wq = w.wq; s.wk = w.wk; s.wv = w.wv; s.wo = w.wo;
-    s.q_norm = c.qk_norm ? w.q_norm : nullptr; s.k_norm = c.qk_norm ? w.k_norm : nullptr;
-    s.ls1 = w.ls1; s.ffn_norm_w = w.ffn_norm_w; s.ffn_norm_b = w.ffn_norm_b;
-    s.w_gate = w.w_gate; s.w_up = w.w_up; s.w_down = w.w_down; s.ls2 = w.ls2;
-    s.k_ring = ring_at(h, h->k_rings, 0, l);
-    s.v_ring = ring_at(h, h->v_rings, 0, l);
-    s.x_in = x_in;
-    s.qkv = cur; cur += pad(nqkv);
-    s.attn_out = cur; cur += pad(qw);
-    s.x_attn = cur; cur += pad(c.d_model);
-    s.act = cur; cur += pad(c.d_ff);
-    s.x_ffn = cur; cur += pad(c.d_model);
-    s.part = cur; cur += pad(n_part);
-    s.counters = reinterpret_cast<uint32_t*>(cur); cur += pad(hkv);
-    x_in = s.x_ffn;
-  }
-  HIP_TRY(hipMemcpy(h->step_layers, L.data(), sizeof(StepLayer) * c.n_layers,
-                    hipMemcpyHostToDevice));
-  StepArgs& a = h->step;
-  a.layers = h->step_layers; a.n_layers = c.n_layers; a.d = c.d_model; a.hq = hq; a.hkv = hkv;
-  a.hd = hd; a.d_ff = c.d_ff; a.nqkv = nqkv;
-  a.norm = c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN; a.eps = c.norm_eps; a.qk_eps = c.qk_norm_eps;
-  a.rope_style = c.rope == SDEC_ROPE_HALF ? 0 : 1; a.theta = c.rope_theta;
-  a.ffn = c.ffn == SDEC_FFN_SWIGLU ? EPI_SWIGLU : EPI_GELU;
-  a.layer_scale = c.layer_scale ? 1 : 0; a.final_norm = c.final_norm ? 1 : 0;
-  a.window = c.window; a.ring = h->ring; a.chunk = h->chunk; a.n_chunks = h->n_chunks;
-  a.fin_w = h->fin.norm_w; a.fin_b = h->fin.norm_b;
-  a.x0 = x0; a.pos_ring = h->pos_rings; a.legal = h->legal; a.n_legal = h->n_legal;
-  a.cs = h->cs; a.st = h->st; a.bar = h->bar; a.err = h->err;
   return SDEC_OK;
 }
 
@@ -680,14 +594,6 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
     delete h;
     return code;
   };
-  if (c.m == 1 && (c.flags & SDEC_FLAG_PERSISTENT) && !(c.flags & (SDEC_FLAG_EAGER | SDEC_FLAG_TAPS)) &&
-      plan_step(hd, hq / hkv, c.d_model, c.d_ff, qw, c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN,
-                c.ffn == SDEC_FFN_SWIGLU ? EPI_SWIGLU : EPI_GELU, &h->step_grid) == hipSuccess) {
-    h->persistent = true;
-    h->step_group = hq / hkv;
-    r = setup_persistent(h);
-    if (r != SDEC_OK) return bail(r);
-  }
   hipError_t e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
   if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "hipStreamCreate: %s", hipGetErrorString(e)));
   r = clear_state(h, h->cap_stream);
@@ -695,7 +601,7 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
   e = hipStreamSynchronize(h->cap_stream);
   if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "init: %s", hipGetErrorString(e)));
 
-  if (!(c.flags & SDEC_FLAG_EAGER) && !h->persistent) {
+  if (!(c.flags & SDEC_FLAG_EAGER)) {
     e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "begin capture: %s", hipGetErrorString(e)));
     r = enqueue_layers(h, h->cap_stream, nullptr);
@@ -719,15 +625,6 @@ int sdec_step(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stre
   int r = check_step(h, x, pos, first);
   if (r != SDEC_OK) return r;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (h->persistent) {
-    StepArgs a = h->step;
-    a.x_in = x; a.x_out = x; a.pos = pos; a.first = first ? 1u : 0u; a.bar_base = h->bar_base;
-    HIP_TRY(launch_step(a, h->step_grid, h->step_group, s));
-    h->bar_base += static_cast<uint64_t>(step_barriers(h->cfg.n_layers)) * h->step_grid;
-    h->has_next = true;
-    h->next_pos = pos + 1;
-    return SDEC_OK;
-  }
   r = enqueue_begin(h, x, pos, first, s, nullptr);
   if (r != SDEC_OK) return r;
   if (h->graph_ready) {
@@ -815,45 +712,9 @@ int sdec_reset(sdec_handle* h, void* stream) {
   return SDEC_OK;
 }
 
-int sdec_step_trace(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stream,
-                    uint64_t* ts, uint32_t n_ts, double* clock_hz) {
-  int r = check_step(h, x, pos, first);
-  if (r != SDEC_OK) return r;
-  if (!h->persistent) return fail(SDEC_E_ARG, "the handle does not run the persistent step");
-  const uint32_t n = 2 * (step_barriers(h->cfg.n_layers) + 1);
-  if (!ts || n_ts < n) return fail(SDEC_E_ARG, "trace needs %u stamps", n);
-  uint64_t* dtrace = nullptr;
-  HIP_TRY(hipMalloc(&dtrace, n * sizeof(uint64_t)));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  StepArgs a = h->step;
-  a.x_in = x; a.x_out = x; a.pos = pos; a.first = first ? 1u : 0u; a.bar_base = h->bar_base;
-  a.trace = dtrace;
-  hipError_t e = launch_step(a, h->step_grid, h->step_group, s);
-  if (e == hipSuccess) {
-    h->bar_base += static_cast<uint64_t>(step_barriers(h->cfg.n_layers)) * h->step_grid;
-    h->has_next = true;
-    h->next_pos = pos + 1;
-    e = hipStreamSynchronize(s);
-  }
-  if (e == hipSuccess) e = hipMemcpy(ts, dtrace, n * sizeof(uint64_t), hipMemcpyDeviceToHost);
-  int rate_khz = 0;
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, h->device);
-  (void)hipFree(dtrace);
-  if (e != hipSuccess) return fail(SDEC_E_HIP, "step trace: %s", hipGetErrorString(e));
-  if (clock_hz) *clock_hz = 1e3 * rate_khz;
-  return SDEC_OK;
-}
-
-int sdec_status(sdec_handle* h, uint32_t* path, uint32_t* device_error) {
+int sdec_status(sdec_handle* h, uint32_t* path) {
   if (!h) return fail(SDEC_E_ARG, "null handle");
-  if (path) *path = h->persistent ? 2u : (h->graph_ready ? 0u : 1u);
-  if (device_error) {
-    *device_error = 0;
-    if (h->persistent) {
-      HIP_TRY(hipDeviceSynchronize());
-      HIP_TRY(hipMemcpy(device_error, h->err, sizeof(uint32_t), hipMemcpyDeviceToHost));
-    }
-  }
+  if (path) *path = h->graph_ready ? 0u : 1u;
   return SDEC_OK;
 }
 

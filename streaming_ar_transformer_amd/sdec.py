@@ -16,14 +16,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsdec.so")
 
 OK, E_ARG, E_POS, E_CAPACITY, E_HIP, E_NOMEM = 0, -1, -2, -3, -4, -5
-FLAG_EAGER, FLAG_TAPS, FLAG_PERSISTENT = 1, 2, 4
-PATH_GRAPH, PATH_EAGER, PATH_PERSISTENT = 0, 1, 2
+FLAG_EAGER, FLAG_TAPS = 1, 2
+PATH_GRAPH, PATH_EAGER = 0, 1
 K_NAMES = ["begin", "qkv", "attention", "o_proj", "ffn_up", "ffn_down", "end"]
 
 # Every symbol include/sdec.h declares.
 EXPORTS = ["sdec_create", "sdec_step", "sdec_reset", "sdec_destroy", "sdec_last_error",
            "sdec_kv_view", "sdec_set_next_position", "sdec_tap_view", "sdec_step_profile",
-           "sdec_gemv", "sdec_ring_attention", "sdec_status", "sdec_step_trace", "sdec_prefill",
+           "sdec_gemv", "sdec_ring_attention", "sdec_status", "sdec_prefill",
            "sdec_rvq_create", "sdec_rvq_encode", "sdec_rvq_quantise", "sdec_rvq_decode",
            "sdec_rvq_destroy", "sdec_conv_create", "sdec_conv_step", "sdec_conv_destroy"]
 
@@ -104,9 +104,7 @@ def lib():
             "sdec_step_profile": (i32, [vp, vp, u32, u32, vp, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(u32)]),
             "sdec_gemv": (i32, [vp, vp, vp, u32, u32, u32, vp]),
-            "sdec_status": (i32, [vp, ctypes.POINTER(u32), ctypes.POINTER(u32)]),
-            "sdec_step_trace": (i32, [vp, vp, u32, u32, vp, ctypes.POINTER(ctypes.c_uint64), u32,
-                                      ctypes.POINTER(ctypes.c_double)]),
+            "sdec_status": (i32, [vp, ctypes.POINTER(u32)]),
             "sdec_ring_attention": (i32, [vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, u32, u32,
                                           vp]),
             "sdec_rvq_create": (i32, [ctypes.POINTER(RVQConfig), ctypes.POINTER(RVQWeights),
@@ -149,7 +147,7 @@ def _ptr(t):
 
 
 def make_config(cfg, window=None, unbounded=None, eager=False, taps=False,
-                persistent=False, max_prefill=0) -> Config:
+                max_prefill=0) -> Config:
     """Fill the C struct from a ``workloads.StepConfig``-like object."""
     c = Config()
     c.n_layers, c.d_model = cfg.n_layers, cfg.d_model
@@ -161,8 +159,7 @@ def make_config(cfg, window=None, unbounded=None, eager=False, taps=False,
     c.ffn, c.layer_scale, c.final_norm = cfg.ffn, int(cfg.layer_scale), int(cfg.final_norm)
     c.window = cfg.window if window is None else window
     c.unbounded = int(cfg.is_unbounded if unbounded is None else unbounded)
-    c.flags = (FLAG_EAGER if eager else 0) | (FLAG_TAPS if taps else 0) | \
-        (FLAG_PERSISTENT if persistent else 0)
+    c.flags = (FLAG_EAGER if eager else 0) | (FLAG_TAPS if taps else 0)
     c.max_prefill = max_prefill
     return c
 
@@ -174,11 +171,11 @@ class Decoder:
     they are borrowed (this object keeps references so they outlive the handle)."""
 
     def __init__(self, cfg, layers, final=None, ring=None, window=None, unbounded=None,
-                 eager=False, taps=False, persistent=False, max_prefill=0):
+                 eager=False, taps=False, max_prefill=0):
         self.cfg = cfg
         self.ring = cfg.ring if ring is None else ring
         self.c = make_config(cfg, window=window, unbounded=unbounded, eager=eager, taps=taps,
-                             persistent=persistent, max_prefill=max_prefill)
+                             max_prefill=max_prefill)
         self._keep = (layers, final)
         arr = (LayerWeights * cfg.n_layers)()
         for i, lw in enumerate(layers):
@@ -214,26 +211,12 @@ class Decoder:
             out[k][1] += calls[i]
         return out
 
-    def status(self):
-        """(path, device_error): the step path in use and the persistent kernel's error word."""
-        path, err = ctypes.c_uint32(), ctypes.c_uint32()
-        _check(lib().sdec_status(self.h, ctypes.byref(path), ctypes.byref(err)))
-        return path.value, err.value
-
     @property
     def path(self) -> int:
+        """The step path in use: PATH_GRAPH or PATH_EAGER."""
         path = ctypes.c_uint32()
-        _check(lib().sdec_status(self.h, ctypes.byref(path), None))
+        _check(lib().sdec_status(self.h, ctypes.byref(path)))
         return path.value
-
-    def step_trace(self, x, pos: int, first: bool = False, stream=None):
-        """One persistent step with per-barrier device-clock stamps; returns (stamps, clock_hz)."""
-        n = 2 * (1 + 5 * self.cfg.n_layers + 1)
-        ts = (ctypes.c_uint64 * n)()
-        hz = ctypes.c_double()
-        _check(lib().sdec_step_trace(self.h, _ptr(x), int(pos), int(bool(first)),
-                                     _stream(stream), ts, n, ctypes.byref(hz)))
-        return list(ts), hz.value
 
     def reset(self, stream=None):
         _check(lib().sdec_reset(self.h, _stream(stream)))

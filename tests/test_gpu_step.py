@@ -32,20 +32,6 @@ def make(sd, cfg, **kw):
     return sd.Decoder(cfg, dl, df, **kw)
 
 
-def check_path(sd, dec, persistent):
-    path, err = dec.status()
-    assert err == 0, "a device-wide barrier wait timed out"
-    if persistent:
-        assert path == sd.PATH_PERSISTENT
-    else:
-        assert path != sd.PATH_PERSISTENT
-    return path
-
-
-PATHS = [True, False]
-PATH_IDS = ["persistent", "graph"]
-
-
 def read_pos_ring(sd, dec, stream, ring):
     _, _, p = dec.kv_view(stream, 0)
     return sd.copy_from_device(p, ring * 4, np.uint32, (ring,))
@@ -58,18 +44,16 @@ def read_kv(sd, dec, cfg, stream, layer, ring):
     return sd.copy_from_device(k, n, np.float32, shape), sd.copy_from_device(v, n, np.float32, shape)
 
 
-def run_parity(sd, cfg, steps, check_every=1, taps=False, ring_check=True, persistent=False):
+def run_parity(sd, cfg, steps, check_every=1, taps=False, ring_check=True):
     layers, final = weights(cfg)
     xs = wl.make_inputs(cfg, steps)
-    dec = make(sd, cfg, taps=taps, persistent=persistent)
+    dec = make(sd, cfg, taps=taps)
     orc = oracle.OracleDecoder(cfg, layers, final)
     x = torch.empty((cfg.m, cfg.d_model), device="cuda")
     worst = (1.0, 0.0)
     for p in range(steps):
         x.copy_(torch.from_numpy(xs[p]))
         dec.step(x, p, first=(p == 0))
-        if p == 0:
-            assert dec.status()[1] == 0, "a device-wide barrier wait timed out"
         t = {} if taps else None
         want = orc.step(xs[p], p, first=(p == 0), taps=t)
         if p % check_every and p != steps - 1:
@@ -90,7 +74,7 @@ def run_parity(sd, cfg, steps, check_every=1, taps=False, ring_check=True, persi
             for s in range(cfg.m):
                 np.testing.assert_array_equal(read_pos_ring(sd, dec, s, cfg.ring), orc.P[s],
                                               err_msg=f"pos ring, pos {p}")
-    path = check_path(sd, dec, persistent and not taps and cfg.m == 1)
+    path = dec.path
     dec.close()
     log(f"{cfg.name} path {path}: {steps} steps, worst cos {worst[0]:.9f} max|d| {worst[1]:.3e}")
     return dec, orc
@@ -101,31 +85,27 @@ def test_codec1_full_run_with_taps_and_ring_state(sd):
     run_parity(sd, cfg, cfg.steps, taps=True)
 
 
-@pytest.mark.parametrize("persistent", PATHS, ids=PATH_IDS)
-def test_codec1_full_run(sd, persistent):
+def test_codec1_full_run(sd):
     cfg = wl.CONFIGS[1]
-    run_parity(sd, cfg, cfg.steps, persistent=persistent)
+    run_parity(sd, cfg, cfg.steps)
 
 
-@pytest.mark.parametrize("persistent", PATHS, ids=PATH_IDS)
-def test_codec2_full_run(sd, persistent):
+def test_codec2_full_run(sd):
     cfg = wl.CONFIGS[2]
-    run_parity(sd, cfg, cfg.steps, ring_check=True, persistent=persistent)
+    run_parity(sd, cfg, cfg.steps, ring_check=True)
 
 
-@pytest.mark.parametrize("persistent", PATHS, ids=PATH_IDS)
-def test_codec8_full_run(sd, persistent):
+def test_codec8_full_run(sd):
     cfg = wl.CONFIGS[3]
-    run_parity(sd, cfg, cfg.steps, ring_check=True, persistent=persistent)
+    run_parity(sd, cfg, cfg.steps, ring_check=True)
 
 
-@pytest.mark.parametrize("persistent", PATHS, ids=PATH_IDS)
-def test_codec_kv_ring_contents_past_wrap(sd, persistent):
+def test_codec_kv_ring_contents_past_wrap(sd):
     # K (roped) and V ring rows equal the oracle's, slot by slot, around each wrap.
     cfg = wl.CONFIGS[2]
     layers, final = weights(cfg)
     xs = wl.make_inputs(cfg, 520)
-    dec = make(sd, cfg, persistent=persistent)
+    dec = make(sd, cfg)
     orc = oracle.OracleDecoder(cfg, layers, final)
     x = torch.empty((1, cfg.d_model), device="cuda")
     for p in range(520):
@@ -138,14 +118,12 @@ def test_codec_kv_ring_contents_past_wrap(sd, persistent):
                 assert np.max(np.abs(k - orc.K[0, li])) <= 1e-3
                 assert np.max(np.abs(v - orc.V[0, li])) <= 1e-3
             np.testing.assert_array_equal(read_pos_ring(sd, dec, 0, cfg.ring), orc.P[0])
-    check_path(sd, dec, persistent)
     dec.close()
 
 
-@pytest.mark.parametrize("persistent", PATHS, ids=PATH_IDS)
-def test_talker_first_positions(sd, persistent):
+def test_talker_first_positions(sd):
     cfg = wl.CONFIGS[4]
-    run_parity(sd, cfg, 24, ring_check=True, persistent=persistent)
+    run_parity(sd, cfg, 24, ring_check=True)
 
 
 def _import_prefill(sd, dec, orc, cfg, n_pos, streams):
@@ -162,12 +140,11 @@ def _import_prefill(sd, dec, orc, cfg, n_pos, streams):
     dec.set_next_position(n_pos)
 
 
-@pytest.mark.parametrize("persistent", PATHS, ids=PATH_IDS)
-def test_talker_last_positions_from_prefill(sd, persistent):
+def test_talker_last_positions_from_prefill(sd):
     # Positions 2040..2047 of the 2048-slot talker, over a seeded prefill of 0..2039.
     cfg = wl.CONFIGS[4]
     layers, final = weights(cfg)
-    dec = make(sd, cfg, persistent=persistent)
+    dec = make(sd, cfg)
     orc = oracle.OracleDecoder(cfg, layers, final)
     _import_prefill(sd, dec, orc, cfg, 2040, [0])
     xs = wl.make_inputs(cfg, cfg.steps)
@@ -181,7 +158,6 @@ def test_talker_last_positions_from_prefill(sd, persistent):
     with pytest.raises(sd.SdecError) as e:  # the unbounded cache refuses position 2048
         dec.step(x, 2048)
     assert e.value.code == sd.E_CAPACITY
-    check_path(sd, dec, persistent)
     dec.close()
 
 
@@ -356,43 +332,18 @@ def collect(dec, cfg, xs, positions, firsts=()):
 def test_graph_replay_equals_eager_and_is_deterministic(sd, cfg):
     xs = wl.make_inputs(cfg, 30)
     pos = list(range(30))
-    g1 = collect(make(sd, cfg, persistent=False), cfg, xs, pos)
-    g2 = collect(make(sd, cfg, persistent=False), cfg, xs, pos)
+    g1 = collect(make(sd, cfg), cfg, xs, pos)
+    g2 = collect(make(sd, cfg), cfg, xs, pos)
     e1 = collect(make(sd, cfg, eager=True), cfg, xs, pos)
     for a, b, c in zip(g1, g2, e1):
         np.testing.assert_array_equal(a, b)
         np.testing.assert_array_equal(a, c)
 
 
-@pytest.mark.parametrize("cfg", [wl.CONFIGS[4].replace(n_layers=4), wl.CONFIGS[1]],
-                         ids=["talker", "codec"])
-def test_persistent_matches_graph_and_is_deterministic(sd, cfg):
-    xs = wl.make_inputs(cfg, 40)
-    pos = list(range(40))
-    p1 = make(sd, cfg, persistent=True)
-    p2 = make(sd, cfg, persistent=True)
-    assert p1.path == sd.PATH_PERSISTENT
-    a = collect(p1, cfg, xs, pos)
-    b = collect(p2, cfg, xs, pos)
-    g = collect(make(sd, cfg), cfg, xs, pos)
-    for u, v, w in zip(a, b, g):
-        np.testing.assert_array_equal(u, v)
-        cos, mx = cos_maxabs(u, w)
-        assert cos >= 0.99999 and mx <= 1e-4
-    check_path(sd, p1, True)
-    check_path(sd, p2, True)
-
-
-PERSISTENT_CFGS = [(wl.CONFIGS[4].replace(n_layers=3, ring=40, window=40), True),
-                   (wl.CONFIGS[1].replace(ring=21, window=20), True),
-                   (SMALL_T, False), (SMALL_C, False)]
-
-
-@pytest.mark.parametrize("cfg,persistent", PERSISTENT_CFGS,
-                         ids=["T-persistent", "C-persistent", "T-graph", "C-graph"])
-def test_reset_replays_bitwise_and_first_restarts(sd, cfg, persistent):
+@pytest.mark.parametrize("cfg", [SMALL_T, SMALL_C], ids=["T", "C"])
+def test_reset_replays_bitwise_and_first_restarts(sd, cfg):
     xs = wl.make_inputs(cfg, 30)
-    dec = make(sd, cfg, persistent=persistent)
+    dec = make(sd, cfg)
     a = collect(dec, cfg, xs, list(range(30)))
     dec.reset()
     b = collect(dec, cfg, xs, list(range(30)))
@@ -401,10 +352,9 @@ def test_reset_replays_bitwise_and_first_restarts(sd, cfg, persistent):
     # first=1 in the middle of a stream equals a fresh handle started there
     start = 20 if cfg.family == "T" else 100  # the talker-family ring refuses pos >= ring
     c = collect(dec, cfg, xs, list(range(start, start + 15)))
-    fresh = collect(make(sd, cfg, persistent=persistent), cfg, xs, list(range(start, start + 15)))
+    fresh = collect(make(sd, cfg), cfg, xs, list(range(start, start + 15)))
     for u, v in zip(c, fresh):
         np.testing.assert_array_equal(u, v)
-    check_path(sd, dec, persistent)
 
 
 def test_streams_equal_separate_handles(sd):
