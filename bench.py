@@ -117,14 +117,35 @@ def kernel_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def host_info():
+    """The host the oracle runs on: CPU model, BLAS library and its thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
+    try:
+        import numpy  # noqa: F401  (loads the BLAS threadpoolctl reports)
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            i = infos[0]
+            blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')})"
+            threads = max(j.get("num_threads", 1) for j in infos)
+    except Exception:
+        pass
+    return model, blas, threads
+
+
 def cpu_baseline(cfg, layers, final, xs, budget_s):
     import numpy as np  # noqa: F401
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    model, blas, threads = host_info()
     orc = oracle.OracleDecoder(cfg, layers, final)
     t0 = time.perf_counter()
     n = 0
@@ -135,6 +156,7 @@ def cpu_baseline(cfg, layers, final, xs, budget_s):
             break
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "blas": blas,
             "sample": f"positions 0..{n - 1} of a fresh stream of this workload "
                       f"({n} steps, {dt:.1f} s, NumPy float32, BLAS threads={threads})"}
 

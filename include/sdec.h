@@ -139,7 +139,9 @@ int sdec_prefill(sdec_handle* h, float* x, uint32_t pos, uint32_t t, uint32_t fi
 int sdec_reset(sdec_handle* h, void* stream);
 
 /* Release every buffer the library owns and the graph.  Synchronizes the device first.
- * NULL is accepted. */
+ * NULL is accepted.  (The pages' GPU objects own the device buffers their constructor allocates
+ * -- [talker] TalkerGpu::load, [mimi] MimiGpu::new -- and release them when dropped; this is that
+ * release, made explicit for a C caller.) */
 void sdec_destroy(sdec_handle* h);
 
 /* Which step path the handle runs: 0 = the per-layer launches recorded once as a hipGraph and
@@ -147,7 +149,11 @@ void sdec_destroy(sdec_handle* h);
  * same launches enqueued one by one (SDEC_FLAG_EAGER).  path may be NULL. */
 int sdec_status(sdec_handle* h, uint32_t* path);
 
-/* Message of the last failed call on this thread ("" if none).  Valid until the next call. */
+/* Message of the last failed call on this thread ("" if none).  Valid until the next call.
+ * The pages return errors as a Result carrying the text of the failed check ([talker]
+ * TalkerGpu::step's ensure! on the embedding length, the position and the cache capacity;
+ * [pocket] PocketBackboneGpu::step); here the code is the return value and the text is kept
+ * here. */
 const char* sdec_last_error(void);
 
 /* Device pointers of stream `stream_idx`'s rings for `layer`: *k and *v are [ring_slots]
@@ -162,7 +168,9 @@ int sdec_kv_view(sdec_handle* h, uint32_t stream_idx, uint32_t layer, float** k,
  * sdec_kv_view ([pocket] load_voice sets the clock to the imported length). */
 int sdec_set_next_position(sdec_handle* h, uint32_t next_pos);
 
-/* With SDEC_FLAG_TAPS: device pointer of a per-layer branch output of the latest step,
+/* Stage taps ([pocket] PocketCodecGpu::debug_read and [mimi] MimiGpu::debug_read read a named
+ * intermediate buffer back for stage-level parity).
+ * With SDEC_FLAG_TAPS: device pointer of a per-layer branch output of the latest step,
  * [m][width] float32.  which = 0: attention output before the o projection (width
  * n_q_heads*head_dim); 1: o projection output before LayerScale and the residual add;
  * 2: FFN down projection output before LayerScale and the residual add (width d_model). */
