@@ -208,6 +208,23 @@ int sdec_ring_attention(const float* q, const float* k_ring, const float* v_ring
                         uint32_t n_kv_heads, uint32_t head_dim, uint32_t ring_slots,
                         uint32_t window, uint32_t pos, void* stream);
 
+/* sdec_ring_attention for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments, kernels and result, with
+ * no allocation at all.  Its scratch (legal-slot lists, per-chunk softmax partials, merge
+ * counters) is a fixed 4 MiB array in device memory that each device the library runs on holds
+ * until the process ends; a call whose scratch would exceed it (about m * n_q_heads *
+ * ceil(ring_slots / 128) * (head_dim + 2) floats of partials plus m * (ring_slots + 1) words
+ * of lists) returns SDEC_E_ARG without enqueuing anything.  Every call on a device shares that
+ * device's array and keeps the last call's contents (the merge counters are cleared at the start
+ * of each call by a fill kernel), so calls that overlap on one device -- on different streams
+ * or threads -- race and must be serialised by the caller.  The first call on a device looks up
+ * the array's address there (hipGetSymbolAddress, with that device current). */
+int sdec_ring_attention_static(const float* q, const float* k_ring, const float* v_ring,
+                               const uint32_t* pos_ring, float* out, uint32_t m,
+                               uint32_t n_q_heads, uint32_t n_kv_heads, uint32_t head_dim,
+                               uint32_t ring_slots, uint32_t window, uint32_t pos,
+                               void* stream);
+
 /* Split residual vector quantiser ([mimi] inferencelayer 0.2.1, src/mimi_gpu.rs: the NEAREST,
  * SUB_EMB and EMB_SUM kernels and MimiGpu's encode / decode plans).  A latent frame [dim] is
  * projected twice (in_first, in_rest: [vq][dim]); code 0 is the nearest bin of codebook

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -496,6 +497,35 @@ int enqueue_ring_attention(const float* q, const float* k_ring, const float* v_r
   return SDEC_OK;
 }
 
+// Scratch of the one-shot attention variant that allocates nothing: a fixed array in device
+// memory (each device the library runs on holds its own copy until the process ends).  Host code
+// never uses the array's name as an address: the device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and kept here.
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+constexpr int kStaticMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kStaticMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kStaticMaxDevices)
+    return fail(SDEC_E_ARG, "device %d: the static scratch serves devices 0..%d", dev,
+                kStaticMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (p == nullptr) return fail(SDEC_E_HIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SDEC_OK;
+}
+
+size_t align256(size_t bytes) { return (bytes + 255) / 256 * 256; }
+
 }  // namespace
 
 extern "C" {
@@ -816,6 +846,37 @@ int sdec_ring_attention(const float* q, const float* k_ring, const float* v_ring
     HIP_TRY(hipMalloc(&legal, z.legal * sizeof(uint32_t)));
     legal_cap = z.legal;
   }
+  return enqueue_ring_attention(q, k_ring, v_ring, pos_ring, out, m, n_q_heads, n_kv_heads,
+                                head_dim, ring_slots, window, pos, part, counters, legal, s);
+}
+
+int sdec_ring_attention_static(const float* q, const float* k_ring, const float* v_ring,
+                               const uint32_t* pos_ring, float* out, uint32_t m,
+                               uint32_t n_q_heads, uint32_t n_kv_heads, uint32_t head_dim,
+                               uint32_t ring_slots, uint32_t window, uint32_t pos,
+                               void* stream) {
+  int r = check_ring_attention(q, k_ring, v_ring, pos_ring, out, m, n_q_heads, n_kv_heads,
+                               head_dim, ring_slots, window);
+  if (r != SDEC_OK) return r;
+  const OneShotSizes z = one_shot_sizes(m, n_q_heads, n_kv_heads, head_dim, ring_slots);
+  const size_t off_legal = align256(z.counters * sizeof(uint32_t));
+  const size_t off_part = off_legal + align256(z.legal * sizeof(uint32_t));
+  const size_t need = off_part + z.part * sizeof(float);
+  if (need > kStaticScratchBytes)
+    return fail(SDEC_E_ARG,
+                "m=%u, %u query heads of %u over %u slots need %zu bytes of scratch, more than "
+                "the %zu-byte static scratch", m, n_q_heads, head_dim, ring_slots, need,
+                kStaticScratchBytes);
+  void* base = nullptr;
+  r = static_scratch(&base);
+  if (r != SDEC_OK) return r;
+  unsigned char* b = static_cast<unsigned char*>(base);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(b);
+  uint32_t* legal = reinterpret_cast<uint32_t*>(b + off_legal);
+  float* part = reinterpret_cast<float*>(b + off_part);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the array keeps whatever the last call on this device left: the counters start at zero
+  HIP_TRY(launch_fill_u32(counters, 0u, z.counters, s));
   return enqueue_ring_attention(q, k_ring, v_ring, pos_ring, out, m, n_q_heads, n_kv_heads,
                                 head_dim, ring_slots, window, pos, part, counters, legal, s);
 }

@@ -23,8 +23,8 @@ K_NAMES = ["begin", "qkv", "attention", "o_proj", "ffn_up", "ffn_down", "end"]
 # Every symbol include/sdec.h declares.
 EXPORTS = ["sdec_create", "sdec_step", "sdec_reset", "sdec_destroy", "sdec_last_error",
            "sdec_kv_view", "sdec_set_next_position", "sdec_tap_view", "sdec_step_profile",
-           "sdec_gemv", "sdec_ring_attention", "sdec_status", "sdec_prefill",
-           "sdec_rvq_create", "sdec_rvq_encode", "sdec_rvq_quantise", "sdec_rvq_decode",
+           "sdec_gemv", "sdec_ring_attention", "sdec_ring_attention_static", "sdec_status",
+           "sdec_prefill", "sdec_rvq_create", "sdec_rvq_encode", "sdec_rvq_quantise", "sdec_rvq_decode",
            "sdec_rvq_destroy", "sdec_conv_create", "sdec_conv_step", "sdec_conv_destroy"]
 
 
@@ -107,6 +107,8 @@ def lib():
             "sdec_status": (i32, [vp, ctypes.POINTER(u32)]),
             "sdec_ring_attention": (i32, [vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, u32, u32,
                                           vp]),
+            "sdec_ring_attention_static": (i32, [vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, u32,
+                                                 u32, vp]),
             "sdec_rvq_create": (i32, [ctypes.POINTER(RVQConfig), ctypes.POINTER(RVQWeights),
                                       ctypes.POINTER(vp)]),
             "sdec_rvq_encode": (i32, [vp, vp, u32, vp, vp]),
@@ -261,6 +263,17 @@ def ring_attention(q, k_ring, v_ring, pos_ring, out, n_q_heads, n_kv_heads, head
     _check(lib().sdec_ring_attention(_ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(pos_ring),
                                      _ptr(out), m, n_q_heads, n_kv_heads, head_dim, ring, window,
                                      int(pos), _stream(stream)))
+    return out
+
+
+def ring_attention_static(q, k_ring, v_ring, pos_ring, out, n_q_heads, n_kv_heads, head_dim,
+                          ring, window, pos, stream=None):
+    """``ring_attention`` through the entry point that allocates nothing (its scratch is a fixed
+    array in device memory, shared by every call on the device)."""
+    m = q.shape[0]
+    _check(lib().sdec_ring_attention_static(_ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(pos_ring),
+                                            _ptr(out), m, n_q_heads, n_kv_heads, head_dim, ring,
+                                            window, int(pos), _stream(stream)))
     return out
 
 

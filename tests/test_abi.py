@@ -173,3 +173,15 @@ def test_one_shot_entry_points_reject_bad_arguments():
     assert L.sdec_step(None, 16, 0, 1, None) == sdec.E_ARG
     assert L.sdec_reset(None, None) == sdec.E_ARG
     L.sdec_destroy(None)
+
+
+def test_static_scratch_attention_checks_on_the_host():
+    # The entry point that allocates nothing refuses, before any HIP call, arguments the
+    # allocating one refuses and any geometry whose scratch exceeds its fixed array.
+    L = sdec.lib()
+    assert L.sdec_ring_attention_static(16, 32, 48, 64, 80, 1, 4, 4, 96, 8, 8, 0, None) == sdec.E_ARG
+    assert L.sdec_ring_attention_static(None, 32, 48, 64, 80, 1, 4, 4, 64, 8, 8, 0, None) == sdec.E_ARG
+    # 8 streams x 16 heads of 128 over 100000 slots: about 52 MB of chunk partials
+    rc = L.sdec_ring_attention_static(256, 512, 768, 1024, 1280, 8, 16, 8, 128, 100000, 100000, 5,
+                                      None)
+    assert rc == sdec.E_ARG and "static scratch" in L.sdec_last_error().decode()
