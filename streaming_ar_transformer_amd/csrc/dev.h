@@ -619,18 +619,20 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   if (single || a.partials_only) return;
 
   // 6. the last chunk of this (stream, kv head) to finish merges all chunks.  The partials went
-  // out with device-coherent stores, released at agent scope by every thread before the count
-  // (an agent-scope acquire-release RMW) is added; the merging workgroup acquires before it reads.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // out with agent-scope stores (written through to the device's point of coherence); every wave
+  // waits for their acknowledgement before the barrier, the count is an agent-scope RMW at that
+  // point, and the merging workgroup reads with agent-scope loads issued after its RMW returned.
+  // (Release and acquire fences instead compile to an L2 writeback per wave and an L2 invalidate:
+  // measured on the eight-stream talker step, 3.05 -> 5.61 ms.)
+  wait_stores();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&a.counters[s * hkv + kvh], 1u, __ATOMIC_ACQ_REL,
+    const uint32_t prev = __hip_atomic_fetch_add(&a.counters[s * hkv + kvh], 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     is_last = prev == n_items - 1 ? 1u : 0u;
   }
   __syncthreads();
   if (!is_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   float* stage = &sm_acc[0][0][0];  // [CB][G][HD]
   float Mr[(G * HD + NT - 1) / NT], Lr[(G * HD + NT - 1) / NT];
   float Or[(G * HD + NT - 1) / NT];

@@ -19,11 +19,32 @@ struct DevState {
 
 // PRO_ATTN: the input row is this step's attention output, combined in the prologue from the
 // per-chunk softmax partials the ring-attention launch left (one stream only).
-enum GemvPrologue : int { PRO_NONE = 0, PRO_RMS = 1, PRO_LN = 2, PRO_ATTN = 3 };
+// PRO_ATTN_SHORT: the input row is this step's attention output, computed inside the launch from
+// the raw q/k/v and the ring by waves of its own (one stream, at most kShortSlots legal slots).
+enum GemvPrologue : int { PRO_NONE = 0, PRO_RMS = 1, PRO_LN = 2, PRO_ATTN = 3, PRO_ATTN_SHORT = 4 };
+constexpr uint32_t kShortSlots = 21;         // legal slots (the pushed one included) of PRO_ATTN_SHORT
 constexpr uint32_t kAttnMaxChunks = 64;      // chunks a PRO_ATTN prologue combines
 constexpr uint32_t kAttnMaxPartials = 1024;  // heads x chunks a PRO_ATTN prologue combines
 constexpr uint32_t kAttnMaxHeads = 16;       // query heads a PRO_ATTN prologue combines
 enum GemvEpilogue : int { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2, EPI_GELU = 3 };
+
+// PRO_ATTN_SHORT: what the attention needs ([talker] QK_NORM_SRC, ROPE_SRC, APPEND_SRC and
+// GQA_ATTN_SRC; [mimi] rope_push_src and attn_src).  The legal-slot list holds the pushed slot
+// first; at most kShortSlots entries are read.
+struct ShortAttnArgs {
+  const float* qkv;          // this step's raw q (Hq*hd), then k (Hkv*hd), then v (Hkv*hd)
+  const float* q_norm;       // [hd] or null (no qk-norm)
+  const float* k_norm;
+  float eps;
+  int rope_style;            // 0 rotate_half, 1 interleaved
+  const float* cs;           // [hd/2] cos then [hd/2] sin of this position
+  float* k_ring;             // this layer's rings [R][Hkv][hd]
+  float* v_ring;
+  const uint32_t* legal;     // [R]: the slots this step attends, the pushed slot first
+  const uint32_t* n_legal;
+  const DevState* st;        // slot of this step's push
+  uint32_t n_q_heads, n_kv_heads, ring;
+};
 
 // y = x . W^T over up to three row segments (q, k, v share one launch).  With EPI_SWIGLU the
 // launch covers `n_rows` FFN indices, reading rows of w[0] (gate) and w[1] (up).
@@ -52,7 +73,8 @@ struct GemvArgs {
   const float* part;
   const uint32_t* n_legal;
   uint32_t chunk, n_chunks, head_dim;
-  float* x_tap;          // PRO_ATTN: optional copy of the combined input row
+  float* x_tap;          // PRO_ATTN, PRO_ATTN_SHORT: optional copy of the combined input row
+  ShortAttnArgs sa;      // PRO_ATTN_SHORT
 };
 
 struct GemvLaunch {
@@ -64,11 +86,16 @@ struct GemvLaunch {
   int stream;         // 1: row-stream kernel (one row per wave in flight), k == 256*kb
   int waves_per_wg;
   uint32_t grid;      // workgroups; each wave owns a contiguous, balanced range of row tiles
+  int attn_hd, attn_g, attn_hpw;  // PRO_ATTN_SHORT: head_dim, GQA group, kv heads per wave
 };
 
 hipError_t launch_gemv(const GemvArgs& a, const GemvLaunch& l, hipStream_t s);
 // A launch shape for this GEMV on this device (grid sized to the row tiles).
 GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, uint32_t m);
+// The short-context attention + o projection launch (PRO_ATTN_SHORT, one stream, n_kv_heads a
+// multiple of 4); gemv_supported tells whether a kernel exists for it.
+GemvLaunch plan_attn_short_o(uint32_t n_rows, uint32_t k, uint32_t head_dim, uint32_t n_q_heads,
+                             uint32_t n_kv_heads);
 // Whether a kernel exists for this launch shape.
 bool gemv_supported(const GemvLaunch& l, uint32_t k, uint32_t m);
 // Per-kernel timing: while a pair is set (null to clear), the step-kernel launches of this thread

@@ -12,6 +12,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include <hip/hip_ext.h>
 
 #include "dev.h"
@@ -374,6 +376,347 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
       if ((t += ts) >= t_end) break;
       load_tile(t, w0, p0);
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Short-context attention + o projection for one stream (at most kShortSlots legal slots): the
+// attention of every head is computed inside the o-projection launch, so no attention launch sits
+// between the q/k/v projection and this one.  A workgroup has 4 GEMV waves and NAW attention
+// waves.  Attention wave a takes kv heads a*HPW .. a*HPW + HPW - 1 and their G query heads each
+// ([talker] QK_NORM_SRC, ROPE_SRC, GQA_ATTN_SRC; [mimi] rope_push_src, attn_src): lane (group,
+// sub) holds elements 8 sub .. 8 sub + 7 of a head row, so the raw q/k/v rows, the slot list and
+// the ring rows arrive in two round trips and every cross-lane step is a DPP or permlane move:
+// the qk-RMSNorm sums and the scores over the hd/8 lanes of a slot group, the rope partner
+// (rotate_half: the lane hd/16 away), and the merge of the slot groups' online softmax states.
+// The pushed slot is scored from registers by group 0.  The GEMV waves (k_gemv_rx's tile loop, R
+// rows per wave) request their weights once the attention waves' ring rows have arrived, so those
+// requests are not queued behind the weight stream; every workgroup computes the whole
+// attention row (its ring rows come from L2), and workgroup 0 pushes this step's key and value.
+// ------------------------------------------------------------------------------------------------
+
+template <int OFF>
+__device__ __forceinline__ float lane_xor(float x, int lane) {
+  if constexpr (OFF == 32) return partner32(x, lane);
+  else if constexpr (OFF == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((lane & 16) ? p[0] : p[1]);
+  } else if constexpr (OFF == 8) {
+    return dpp_mov<0x128>(x);  // row_ror:8 -- lane i of a 16-lane row reads lane i ^ 8
+  } else {
+    return __shfl_xor(x, OFF);
+  }
+}
+
+template <int HD, int G, int HPW>
+__device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, float* out) {
+  constexpr int LPS = HD / 8;            // lanes per slot row, 8 floats each
+  constexpr int GPW = kWave / LPS;       // slot groups per wave
+  constexpr int SPG = (static_cast<int>(kShortSlots) - 1 + GPW - 1) / GPW;  // older slots per group
+  constexpr int HALF = HD / 2;
+  const ShortAttnArgs& sa = a.sa;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int grp = lane / LPS, sub = lane % LPS;
+  const uint32_t hq = sa.n_q_heads, hkv = sa.n_kv_heads;
+  const uint32_t g0 = static_cast<uint32_t>(aw) * HPW;
+  // round trip 1: the slot count, this group's list entries (entry 0 is the pushed slot; group grp
+  // takes entries 1 + grp + GPW j), this lane's 8 elements of the raw q, k, v rows, the norm gains
+  // and the rope cos/sin of those elements
+  const uint32_t nl = *sa.n_legal;
+  const uint32_t push_slot = sa.st->slot;
+  uint32_t slot[SPG];
+#pragma unroll
+  for (int j = 0; j < SPG; ++j)  // entries past the count hold anything: clamp the slot too
+    slot[j] = min(sa.legal[min(1u + grp + GPW * j, sa.ring - 1)], sa.ring - 1);
+  auto ld8 = [&](const float* p, float (&d)[8]) {
+    const float4 u = reinterpret_cast<const float4*>(p)[0], v = reinterpret_cast<const float4*>(p)[1];
+    d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w; d[4] = v.x; d[5] = v.y; d[6] = v.z; d[7] = v.w;
+  };
+  float q8[HPW][G][8], k8[HPW][8], v8[HPW][8], gq[8], gk[8], cv[8], sv[8];
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+#pragma unroll
+    for (int q = 0; q < G; ++q) ld8(sa.qkv + static_cast<size_t>((g0 + h) * G + q) * HD + 8 * sub, q8[h][q]);
+    ld8(sa.qkv + static_cast<size_t>(hq + g0 + h) * HD + 8 * sub, k8[h]);
+    ld8(sa.qkv + static_cast<size_t>(hq + hkv + g0 + h) * HD + 8 * sub, v8[h]);
+  }
+  if (sa.q_norm) { ld8(sa.q_norm + 8 * sub, gq); ld8(sa.k_norm + 8 * sub, gk); }
+  if (sa.rope_style == 0) {  // element d takes frequency d mod hd/2: 8 consecutive ones
+    ld8(sa.cs + (8 * sub) % HALF, cv);
+    ld8(sa.cs + HALF + (8 * sub) % HALF, sv);
+  } else {                   // element d takes frequency d / 2: 4 consecutive ones, twice each
+    const float4 c4 = reinterpret_cast<const float4*>(sa.cs + 4 * sub)[0];
+    const float4 s4 = reinterpret_cast<const float4*>(sa.cs + HALF + 4 * sub)[0];
+    cv[0] = cv[1] = c4.x; cv[2] = cv[3] = c4.y; cv[4] = cv[5] = c4.z; cv[6] = cv[7] = c4.w;
+    sv[0] = sv[1] = s4.x; sv[2] = sv[3] = s4.y; sv[4] = sv[5] = s4.z; sv[6] = sv[7] = s4.w;
+  }
+  // round trip 2 starts as soon as the list is in: every older slot's key and value rows
+  float4 K[HPW][SPG][2], V[HPW][SPG][2];
+  const size_t row = static_cast<size_t>(hkv) * HD;
+#pragma unroll
+  for (int h = 0; h < HPW; ++h)
+#pragma unroll
+    for (int j = 0; j < SPG; ++j) {
+      const float4* kp = reinterpret_cast<const float4*>(sa.k_ring + slot[j] * row + (g0 + h) * HD + 8 * sub);
+      const float4* vp = reinterpret_cast<const float4*>(sa.v_ring + slot[j] * row + (g0 + h) * HD + 8 * sub);
+      K[h][j][0] = kp[0]; K[h][j][1] = kp[1];
+      V[h][j][0] = vp[0]; V[h][j][1] = vp[1];
+    }
+  // (1) the ring rows are in: only now do the GEMV waves start their weight stream, so these
+  // requests were not queued behind it; the math below overlaps the stream
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // qk-RMSNorm over the hd/8 lanes of a group (the G queries and the key of a kv head at once,
+  // so their reduction chains interleave), then rope
+  auto rope = [&](float (&x)[8]) {
+    float r[8];
+    if (sa.rope_style == 0) {  // rotate_half: element d pairs with d +- hd/2, hd/16 lanes away
+      const bool lo = 8 * sub < HALF;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = lane_xor<HALF / 8>(x[e], lane);
+        r[e] = lo ? x[e] * cv[e] - pr * sv[e] : x[e] * cv[e] + pr * sv[e];
+      }
+    } else {  // interleaved: pairs (2i, 2i + 1) inside the lane
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float xa = x[2 * i], xb = x[2 * i + 1];
+        r[2 * i] = xa * cv[2 * i] - xb * sv[2 * i];
+        r[2 * i + 1] = xa * sv[2 * i] + xb * cv[2 * i];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = r[e];
+  };
+  // scores in log2 units: exponentials are single exp2 instructions
+  const float scale = 1.4426950408889634f / sqrtf(static_cast<float>(HD));
+  constexpr int NS = 1 + SPG;  // the pushed slot, then this group's older slots
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+    const uint32_t g = g0 + h;
+    if (sa.q_norm) {
+      float ss[G + 1];
+#pragma unroll
+      for (int q = 0; q <= G; ++q) {
+        const float* x = q < G ? q8[h][q] : k8[h];
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t = fmaf(x[e], x[e], t);
+        ss[q] = t;
+      }
+#pragma unroll
+      for (int q = 0; q <= G; ++q) ss[q] = group_sum<LPS>(ss[q]);
+#pragma unroll
+      for (int q = 0; q <= G; ++q) {
+        const float inv = rsqrtf(ss[q] / static_cast<float>(HD) + sa.eps);
+        float* x = q < G ? q8[h][q] : k8[h];
+        const float* gn = q < G ? gq : gk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (x[e] * inv) * gn[e];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q) rope(q8[h][q]);
+    rope(k8[h]);
+    if (blockIdx.x == 0 && grp == 0) {  // workgroup 0 pushes this step's key and value
+      const size_t roff = (static_cast<size_t>(push_slot) * hkv + g) * HD + 8 * sub;
+      float4* kd = reinterpret_cast<float4*>(sa.k_ring + roff);
+      float4* vd = reinterpret_cast<float4*>(sa.v_ring + roff);
+      kd[0] = make_float4(k8[h][0], k8[h][1], k8[h][2], k8[h][3]);
+      kd[1] = make_float4(k8[h][4], k8[h][5], k8[h][6], k8[h][7]);
+      vd[0] = make_float4(v8[h][0], v8[h][1], v8[h][2], v8[h][3]);
+      vd[1] = make_float4(v8[h][4], v8[h][5], v8[h][6], v8[h][7]);
+    }
+    // every score of the group first (independent dot products and reductions), then the
+    // group's max, the exponentials and the sums: slot 0 is the pushed one (group 0 only)
+    float sc[NS][G];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      float kf[8];
+      if (j == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kf[e] = k8[h][e];
+      } else {
+        const float4 k0 = K[h][j - 1][0], k1 = K[h][j - 1][1];
+        kf[0] = k0.x; kf[1] = k0.y; kf[2] = k0.z; kf[3] = k0.w;
+        kf[4] = k1.x; kf[5] = k1.y; kf[6] = k1.z; kf[7] = k1.w;
+      }
+#pragma unroll
+      for (int q = 0; q < G; ++q) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(q8[h][q][e], kf[e], d);
+        sc[j][q] = d;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int q = 0; q < G; ++q) sc[j][q] = group_sum<LPS>(sc[j][q]);
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const uint32_t ent = j == 0 ? 0u : 1u + grp + GPW * (j - 1);
+        const bool live = j == 0 ? grp == 0 : (ent < nl && ent < kShortSlots);
+        sc[j][q] = live ? sc[j][q] * scale : -INFINITY;
+        mx = fmaxf(mx, sc[j][q]);
+      }
+      m[q] = mx;
+      l[q] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const float p = __builtin_amdgcn_exp2f(sc[j][q] - mx);  // 0 for a masked slot
+          l[q] += p;
+          if (j == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(p, v8[h][e], acc[q][e]);
+          } else {
+            const float4 v0 = V[h][j - 1][0], v1 = V[h][j - 1][1];
+            acc[q][0] = fmaf(p, v0.x, acc[q][0]); acc[q][1] = fmaf(p, v0.y, acc[q][1]);
+            acc[q][2] = fmaf(p, v0.z, acc[q][2]); acc[q][3] = fmaf(p, v0.w, acc[q][3]);
+            acc[q][4] = fmaf(p, v1.x, acc[q][4]); acc[q][5] = fmaf(p, v1.y, acc[q][5]);
+            acc[q][6] = fmaf(p, v1.z, acc[q][6]); acc[q][7] = fmaf(p, v1.w, acc[q][7]);
+          }
+        }
+      }
+    }
+    // merge the slot groups: first every group's (max, sum) with its partners LPS, 2 LPS, ... lanes
+    // apart, so each group knows the overall max and can rescale its sums; then reduce-scatter the
+    // G x 8 rescaled output sums, halving the values per step, so each element ends in one group
+    float M[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) M[q] = m[q];
+#pragma unroll
+    for (int off = LPS; off < kWave; off <<= 1)
+#pragma unroll
+      for (int q = 0; q < G; ++q) {
+        float mo;
+        if (off == 8) mo = lane_xor<8>(M[q], lane);
+        else if (off == 16) mo = lane_xor<16>(M[q], lane);
+        else mo = lane_xor<32>(M[q], lane);
+        M[q] = fmaxf(M[q], mo);
+      }
+    float vals[G * 8 + G];  // rescaled output sums, then the rescaled denominators
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      const float c = m[q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[q] - M[q]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vals[q * 8 + e] = acc[q][e] * c;
+      vals[G * 8 + q] = l[q] * c;
+    }
+    // the denominators are summed in full (every group needs them); the outputs reduce-scatter
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      float t = vals[G * 8 + q];
+      if constexpr (LPS <= 8) t += lane_xor<8>(t, lane);
+      if constexpr (LPS <= 16) t += lane_xor<16>(t, lane);
+      t += lane_xor<32>(t, lane);
+      vals[G * 8 + q] = t;
+    }
+    constexpr int NV = G * 8;
+    static_assert(NV == 8 || NV == 16, "reduce-scatter of 8 or 16 values");
+    float* r = vals;
+    // step over 32 lanes: the lower half keeps values [0, NV/2), the upper half [NV/2, NV)
+    {
+#pragma unroll
+      for (int i = 0; i < NV / 2; ++i) r[i] = halves_sum(r[i], r[i + NV / 2]);
+    }
+    int nv = NV / 2;
+    // step over 16 lanes (when groups are 16 lanes or narrower)
+    if constexpr (LPS <= 16) {
+#pragma unroll
+      for (int i = 0; i < NV / 4; ++i) r[i] = rows16_sum(r[i], r[i + NV / 4]);
+      nv = NV / 4;
+    }
+    if constexpr (LPS <= 8) {  // and over 8 lanes: rows of 16 hold two groups of 8
+#pragma unroll
+      for (int i = 0; i < NV / 8; ++i) {
+        const bool upper = (lane & 8) != 0;
+        const float send = upper ? r[i] : r[i + NV / 8];
+        const float keep = upper ? r[i + NV / 8] : r[i];
+        r[i] = keep + lane_xor<8>(send, lane);
+      }
+      nv = NV / 8;
+    }
+    // group k (of GPW) now holds values [k nv, (k + 1) nv) of the G x 8 sums: the value index of
+    // r[i] follows the halving order -- upper half of 32 lanes took the upper half of the values,
+    // odd rows of 16 the upper half of the rest, upper 8 lanes the upper half after that
+    {
+      const int hi32 = (lane & 32) ? 1 : 0, hi16 = (lane & 16) ? 1 : 0, hi8 = (lane & 8) ? 1 : 0;
+      int base = hi32 * (NV / 2);
+      if constexpr (LPS <= 16) base += hi16 * (NV / 4);
+      if constexpr (LPS <= 8) base += hi8 * (NV / 8);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (i < nv) {
+          const int v = base + i;            // value index: query v / 8, element v % 8
+          const int q = v / 8, e = v % 8;
+          const float den = vals[G * 8 + q];
+          out[static_cast<size_t>(g * G + q) * HD + 8 * sub + e] = r[i] / den;
+        }
+      }
+    }
+  }
+}
+
+// Rows per GEMV tile of k_attn_short_o for an input row of 256 KB floats (every SIMD of a
+// 256-CU device gets a tile at the workloads' widths).
+constexpr int short_o_rows(int kb) { return kb == 2 ? 4 : kb == 4 ? 1 : 2; }
+
+template <int HD, int G, int HPW, int NAW, int KB>
+__global__ __launch_bounds__(kWgThreads + NAW * kWave) void k_attn_short_o(GemvArgs a) {
+  constexpr int M = 1, EPI = EPI_RESIDUAL, R = short_o_rows(KB);
+  constexpr int NGW = kWgThreads / kWave;  // GEMV waves; the attention waves follow them
+  static_assert(R * M <= kWave, "tile too large for one wave");
+  __shared__ float4 xsh[KB * kWave];       // this step's attention output row
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (wave >= NGW) {
+    short_attention_wave<HD, G, HPW>(a, wave - NGW, reinterpret_cast<float*>(xsh));
+    __syncthreads();  // (2) the attention row is in LDS
+    return;
+  }
+  const uint32_t n_tiles = (a.n_rows + R - 1) / R;
+  const uint32_t ts = gridDim.x * NGW;
+  uint32_t t = blockIdx.x * NGW + wave;
+  float4 w0[KB][R];
+  ResPre p0;
+  auto load_tile = [&](uint32_t tt) {
+    const float4* wr[R];
+    tile_rows<R, EPI>(a, tt, wr);
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+#pragma unroll
+      for (int r = 0; r < R; ++r) w0[j][r] = ldw(wr[r] + lane + kWave * j);
+    p0 = residual_prefetch<M, R, EPI>(a, tt, lane);
+  };
+  __syncthreads();  // (1) the attention waves' ring rows have arrived
+  // unconditional (a wave without a tile loads the last one and never uses it)
+  load_tile(t < n_tiles ? t : n_tiles - 1);
+  __syncthreads();  // (2) the attention waves have left the attention row in LDS
+  float4 xr[KB];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) xr[j] = xsh[lane + kWave * j];
+  if (a.x_tap != nullptr && blockIdx.x == 0)
+    for (uint32_t c4 = threadIdx.x; c4 < static_cast<uint32_t>(KB * kWave); c4 += kWgThreads)
+      reinterpret_cast<float4*>(a.x_tap)[c4] = xsh[c4];
+  while (t < n_tiles) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = dot4(w0[j][r], xr[j], acc[r]);
+    gemv_epilogue<M, R, EPI>(a, t, acc, lane, &p0);
+    if ((t += ts) >= n_tiles) break;
+    load_tile(t);
   }
 }
 
@@ -918,10 +1261,16 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_ks(GemvArgs a) {
 // ([mimi] rope_push_src: pr[slot] = pos), and form this position's rope cos/sin in float64
 // ([talker] TalkerGpu::load builds its tables on the CPU; rounding once to float32).
 // ------------------------------------------------------------------------------------------------
+// Legal-slot lists of the step begin are formed from per-wave 64-slot ballots kept in LDS: rings of
+// up to 64 * kBeginMaxChunks slots (larger rings take the scan of compact_legal).
+constexpr uint32_t kBeginMaxChunks = 1024;
+
 __global__ __launch_bounds__(kWgThreads) void k_begin(BeginArgs a) {
+  __shared__ unsigned long long masks[kBeginMaxChunks];
+  __shared__ uint32_t wcount[kWgThreads / kWave];
   __shared__ uint32_t scan[kWgThreads];
   const uint32_t s = blockIdx.x;  // one workgroup per stream, then one for the rope and the state
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const uint32_t slot = a.pos % a.ring;
   if (s == a.m) {  // workgroup-uniform: the float64 trig runs beside the streams' compaction
     const uint32_t half = a.head_dim >> 1;
@@ -938,18 +1287,91 @@ __global__ __launch_bounds__(kWgThreads) void k_begin(BeginArgs a) {
     }
     return;
   }
+  // the caller's row is requested together with the position ring (one round trip)
   const float4* src = reinterpret_cast<const float4*>(a.x_in + static_cast<size_t>(s) * a.d);
   float4* dst = reinterpret_cast<float4*>(a.xres + static_cast<size_t>(s) * a.d);
-  for (uint32_t i = tid; i < (a.d >> 2); i += kWgThreads) dst[i] = src[i];
+  const uint32_t d4 = a.d >> 2;
+  float4 xv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t i = tid + u * kWgThreads;
+    xv[u] = i < d4 ? src[i] : f4zero();
+  }
   uint32_t* P = a.pos_rings + static_cast<size_t>(s) * a.ring;
+  uint32_t* out = a.legal + static_cast<size_t>(s) * a.ring;
+  const uint32_t R = a.ring;
+  const uint32_t nch = (R + kWave - 1) / kWave;  // 64-slot chunks
+  if (nch > kBeginMaxChunks) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = tid + u * kWgThreads;
+      if (i < d4) dst[i] = xv[u];
+    }
+    for (uint32_t i = tid + 4 * kWgThreads; i < d4; i += kWgThreads) dst[i] = src[i];
+    if (a.first) {
+      for (uint32_t i = tid; i < R; i += kWgThreads) P[i] = i == slot ? a.pos : kInvalidPos;
+    } else if (tid == 0) {
+      P[slot] = a.pos;
+    }
+    __syncthreads();
+    compact_legal<kWgThreads, false>(P, R, a.pos, a.window, static_cast<int>(slot), out,
+                                     a.n_legal + s, scan);
+    return;
+  }
+  // Wave w takes chunks [w cpw, (w + 1) cpw); lane l of a chunk c tests slot 64 c + l.  The slot
+  // pushed now is listed first and left out of the ballots, so the stamp below never matters to
+  // them; a fresh stream (first) has no other legal slot.  The ring words of a batch of 8 chunks
+  // are requested together ([mimi] attn_src: legal iff P != INVALID, P <= pos, pos - P < window).
+  const uint32_t cpw = (nch + kWgThreads / kWave - 1) / (kWgThreads / kWave);
+  const uint32_t c0 = min(static_cast<uint32_t>(wave) * cpw, nch), c1 = min(c0 + cpw, nch);
+  uint32_t cnt = 0;
+  if (!a.first) {
+    for (uint32_t cb = c0; cb < c1; cb += 8) {
+      uint32_t pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pv[j] = P[min((cb + j) * kWave + lane, R - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t c = cb + j, sl = c * kWave + lane;
+        const uint32_t p = pv[j];
+        const bool legal = c < c1 && sl < R && sl != slot && p != kInvalidPos && p <= a.pos &&
+                           a.pos - p < a.window;
+        const unsigned long long m = __ballot(legal);
+        if (c < c1 && lane == 0) masks[c] = m;
+        cnt += c < c1 ? static_cast<uint32_t>(__popcll(m)) : 0u;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t i = tid + u * kWgThreads;
+    if (i < d4) dst[i] = xv[u];
+  }
+  for (uint32_t i = tid + 4 * kWgThreads; i < d4; i += kWgThreads) dst[i] = src[i];
   if (a.first) {
-    for (uint32_t i = tid; i < a.ring; i += kWgThreads) P[i] = i == slot ? a.pos : kInvalidPos;
+    for (uint32_t i = tid; i < R; i += kWgThreads) P[i] = i == slot ? a.pos : kInvalidPos;
   } else if (tid == 0) {
     P[slot] = a.pos;
   }
+  if (lane == 0) wcount[wave] = cnt;
   __syncthreads();
-  compact_legal<kWgThreads, false>(P, a.ring, a.pos, a.window, static_cast<int>(slot),
-                                   a.legal + static_cast<size_t>(s) * a.ring, a.n_legal + s, scan);
+  uint32_t o = 1, total = 1;
+  for (int w = 0; w < kWgThreads / kWave; ++w) {
+    o += w < wave ? wcount[w] : 0u;
+    total += wcount[w];
+  }
+  if (!a.first) {
+    const unsigned long long below = lane ? (~0ull >> (kWave - lane)) : 0ull;
+    for (uint32_t c = c0; c < c1; ++c) {
+      const unsigned long long m = masks[c];
+      if ((m >> lane) & 1ull) out[o + __popcll(m & below)] = c * kWave + lane;
+      o += static_cast<uint32_t>(__popcll(m));
+    }
+  }
+  if (tid == 0) {
+    out[0] = slot;
+    a.n_legal[s] = total;
+  }
 }
 
 // Multi-position begin ([talker] TalkerGpu::prefill → forward_rows): the m rows are positions
@@ -1033,52 +1455,95 @@ __global__ __launch_bounds__(kWgThreads) void k_compact_legal(const uint32_t* po
 
 // Step end: the output rows -- the final norm of the residual stream ([talker] build_step_plan's
 // closing RMSNorm) or the residual stream itself ([mimi] transformer_shaped works in place).
+// Rows of up to 4096 floats: the row, the gain and the bias are requested in one round trip and
+// held in registers (16 floats per thread); the statistics meet in LDS.
 __global__ __launch_bounds__(kWgThreads) void k_end(EndArgs a) {
-  __shared__ float red[kWgThreads / kWave];
-  __shared__ float2 st;
+  __shared__ float red[2][kWgThreads / kWave];
   const uint32_t r = blockIdx.x;
   const float* x = a.xres + static_cast<size_t>(r) * a.d;
   float* y = a.x_out + static_cast<size_t>(r) * a.d;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  if (a.norm < 0) {
-    for (uint32_t i = tid; i < a.d; i += blockDim.x) y[i] = x[i];
+  const uint32_t d4 = a.d >> 2;
+  if (a.norm < 0 || d4 > 4 * kWgThreads) {  // a copy, or a row wider than the register tile
+    if (a.norm < 0) {
+      for (uint32_t i = tid; i < a.d; i += blockDim.x) y[i] = x[i];
+      return;
+    }
+    const float df = static_cast<float>(a.d);
+    float s = 0.f;
+    for (uint32_t i = tid; i < a.d; i += blockDim.x) s += x[i];
+    s = wave_sum(s);
+    if (lane == 0) red[0][wave] = s;
+    __syncthreads();
+    const float mean = a.norm == PRO_LN ? ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / df : 0.f;
+    float ss = 0.f;
+    for (uint32_t i = tid; i < a.d; i += blockDim.x) {
+      const float v = x[i] - mean;
+      ss = fmaf(v, v, ss);
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[1][wave] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf(((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / df + a.eps);
+    for (uint32_t i = tid; i < a.d; i += blockDim.x) {
+      if (a.norm == PRO_LN) y[i] = ((x[i] - mean) * inv) * a.w[i] + a.b[i];
+      else y[i] = (x[i] * inv) * a.w[i];
+    }
     return;
+  }
+  static_assert(kWgThreads / kWave == 4, "four partial sums");
+  const float4* x4 = reinterpret_cast<const float4*>(x);
+  const float4* w4 = reinterpret_cast<const float4*>(a.w);
+  const float4* b4 = reinterpret_cast<const float4*>(a.b);
+  float4 xv[4], wv[4], bv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t i = min(tid + u * kWgThreads, d4 - 1);  // clamped; lanes past the row add 0
+    xv[u] = x4[i];
+    wv[u] = w4[i];
+    bv[u] = a.norm == PRO_LN ? b4[i] : f4zero();
   }
   const float df = static_cast<float>(a.d);
   float mean = 0.f;
   if (a.norm == PRO_LN) {
     float s = 0.f;
-    for (uint32_t i = tid; i < a.d; i += blockDim.x) s += x[i];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (tid + u * kWgThreads < d4) s += (xv[u].x + xv[u].y) + (xv[u].z + xv[u].w);
     s = wave_sum(s);
-    if (lane == 0) red[wave] = s;
+    if (lane == 0) red[0][wave] = s;
     __syncthreads();
-    if (tid == 0) {
-      float t = 0.f;
-      for (int w = 0; w < kWgThreads / kWave; ++w) t += red[w];
-      st.x = t / df;
-    }
-    __syncthreads();
-    mean = st.x;
+    mean = ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / df;
   }
   float ss = 0.f;
-  for (uint32_t i = tid; i < a.d; i += blockDim.x) {
-    const float v = x[i] - mean;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (tid + u * kWgThreads < d4) {
+      float4 v = xv[u];
+      v.x -= mean; v.y -= mean; v.z -= mean; v.w -= mean;
+      ss = dot4(v, v, ss);
+    }
   }
   ss = wave_sum(ss);
+  if (lane == 0) red[1][wave] = ss;
   __syncthreads();
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  if (tid == 0) {
-    float t = 0.f;
-    for (int w = 0; w < kWgThreads / kWave; ++w) t += red[w];
-    st.y = 1.0f / sqrtf(t / df + a.eps);
-  }
-  __syncthreads();
-  const float inv = st.y;
-  for (uint32_t i = tid; i < a.d; i += blockDim.x) {
-    if (a.norm == PRO_LN) y[i] = ((x[i] - mean) * inv) * a.w[i] + a.b[i];
-    else y[i] = (x[i] * inv) * a.w[i];
+  const float inv = 1.0f / sqrtf(((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / df + a.eps);
+  float4* y4 = reinterpret_cast<float4*>(y);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t i = tid + u * kWgThreads;
+    if (i < d4) {
+      const float4 v = xv[u], g = wv[u], bb = bv[u];
+      float4 o;
+      if (a.norm == PRO_LN) {
+        o.x = ((v.x - mean) * inv) * g.x + bb.x; o.y = ((v.y - mean) * inv) * g.y + bb.y;
+        o.z = ((v.z - mean) * inv) * g.z + bb.z; o.w = ((v.w - mean) * inv) * g.w + bb.w;
+      } else {
+        o.x = (v.x * inv) * g.x; o.y = (v.y * inv) * g.y;
+        o.z = (v.z * inv) * g.z; o.w = (v.w * inv) * g.w;
+      }
+      y4[i] = o;
+    }
   }
 }
 
@@ -1231,8 +1696,32 @@ GemvKernel gemv_ks(const GemvLaunch& l) {
   return {nullptr, 0};
 }
 
+// The short-context attention + o kernels: (head_dim, group, kv heads per attention wave,
+// attention waves) of the workloads, input row of 256 * kb floats.
+template <int HD, int G, int HPW, int NAW>
+GemvKernel gemv_short_kb(int kb) {
+  switch (kb) {
+    case 2: return {reinterpret_cast<const void*>(&k_attn_short_o<HD, G, HPW, NAW, 2>), 0};
+    case 4: return {reinterpret_cast<const void*>(&k_attn_short_o<HD, G, HPW, NAW, 4>), 0};
+    case 8: return {reinterpret_cast<const void*>(&k_attn_short_o<HD, G, HPW, NAW, 8>), 0};
+    default: return {nullptr, 0};
+  }
+}
+GemvKernel gemv_short(const GemvLaunch& l) {
+  if (l.epilogue != EPI_RESIDUAL || l.rows_per_wave != short_o_rows(l.kb)) return {nullptr, 0};
+  const int naw = l.waves_per_wg - kWgThreads / kWave;
+  if (l.attn_hd == 128 && l.attn_g == 2 && l.attn_hpw == 1 && naw == 8) return gemv_short_kb<128, 2, 1, 8>(l.kb);
+  if (l.attn_hd == 128 && l.attn_g == 2 && l.attn_hpw == 1 && naw == 4) return gemv_short_kb<128, 2, 1, 4>(l.kb);
+  if (l.attn_hd == 64 && l.attn_g == 1 && l.attn_hpw == 1 && naw == 8) return gemv_short_kb<64, 1, 1, 8>(l.kb);
+  return {nullptr, 0};
+}
+
 template <int M>
 GemvKernel gemv_pick_m(const GemvLaunch& l, uint32_t k) {
+  if (l.prologue == PRO_ATTN_SHORT) {
+    if constexpr (M == 1) return gemv_short(l);
+    return {nullptr, 0};
+  }
   if (l.prologue == PRO_ATTN) {
     if constexpr (M == 1) {
       if (l.epilogue != EPI_RESIDUAL) return {nullptr, 0};
@@ -1317,7 +1806,7 @@ static GemvKernel gemv_pick(const GemvLaunch& l, uint32_t k, uint32_t m) {
 }
 
 GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, uint32_t m) {
-  GemvLaunch l;
+  GemvLaunch l{};
   l.prologue = prologue;
   l.epilogue = epilogue;
   const int M = round_m(m);
@@ -1428,6 +1917,34 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
   uint32_t wgs = (tiles + l.waves_per_wg - 1) / l.waves_per_wg;
   if (wgs > max_wgs) wgs = max_wgs;
   l.grid = wgs < 1 ? 1 : wgs;
+  return l;
+}
+
+GemvLaunch plan_attn_short_o(uint32_t n_rows, uint32_t k, uint32_t head_dim, uint32_t n_q_heads,
+                             uint32_t n_kv_heads) {
+  GemvLaunch l{};
+  l.prologue = PRO_ATTN_SHORT;
+  l.epilogue = EPI_RESIDUAL;
+  l.kb = k % 256 == 0 ? static_cast<int>(k / 256) : 0;
+  l.rows_per_wave = short_o_rows(l.kb);
+  // one attention wave per kv head (up to eight)
+  const uint32_t naw = n_kv_heads <= 8 ? n_kv_heads : 0;
+  l.waves_per_wg = static_cast<int>(kWgThreads / kWave + naw);
+  l.attn_hd = static_cast<int>(head_dim);
+  l.attn_g = n_kv_heads ? static_cast<int>(n_q_heads / n_kv_heads) : 0;
+  l.attn_hpw = naw ? static_cast<int>(n_kv_heads / naw) : 0;
+  if (naw == 0 || n_kv_heads % naw != 0 || n_q_heads != static_cast<uint32_t>(l.attn_g) * n_kv_heads ||
+      k != n_q_heads * head_dim) {
+    l.kb = 0;  // no such kernel
+  }
+  const uint32_t tiles = (n_rows + l.rows_per_wave - 1) / l.rows_per_wave;
+  const uint32_t gemv_waves = kWgThreads / kWave;
+  l.grid = (tiles + gemv_waves - 1) / gemv_waves;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (l.grid > static_cast<uint32_t>(cus)) l.grid = static_cast<uint32_t>(cus);
+  if (l.grid < 1) l.grid = 1;
   return l;
 }
 

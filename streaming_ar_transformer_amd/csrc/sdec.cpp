@@ -74,6 +74,10 @@ struct sdec_handle {
   uint64_t ring_layer_stride = 0;   // floats between layers of one stream
 
   std::vector<GemvLaunch> plan_qkv, plan_o, plan_up, plan_down;
+  // one stream, at most kShortSlots legal slots: the attention runs inside the o-projection launch
+  // (no attention launch); a second graph records that plan
+  bool short_ok = false;
+  GemvLaunch plan_o_short{};
   // one stream: the attention launch leaves its chunk partials and the o projection combines them
   bool attn_fused = false;
   // several streams: attention items split each stream's legal slots evenly (n_chunks per kv head)
@@ -81,10 +85,15 @@ struct sdec_handle {
 
   hipStream_t cap_stream = nullptr;
   hipGraphExec_t exec = nullptr;
+  hipGraphExec_t exec_short = nullptr;
   bool graph_ready = false;
 
   bool has_next = false;
   uint32_t next_pos = 0;
+  // first position of the stream's history when known (every legal position lies in
+  // [hist_start, pos]); kNoHistory: set by the next step; hist_known false after an import
+  bool hist_known = true;
+  uint32_t hist_start = 0xFFFFFFFFu;
 };
 
 namespace {
@@ -221,7 +230,7 @@ int hook_post(Hooks* k, hipStream_t s, int kind) {
 
 // The per-token launch sequence of every layer ([talker] build_step_plan; [mimi]
 // Builder::transformer_shaped), on `s`.  Position-dependent values come from h->st.
-int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk) {
+int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk, bool short_attn = false) {
   const sdec_config& c = h->cfg;
   const uint32_t hd = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads;
   const uint32_t qw = hq * hd, kw = hkv * hd, nqkv = qw + 2 * kw;
@@ -238,8 +247,27 @@ int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk) {
     g.norm_w = w.attn_norm_w; g.norm_b = w.attn_norm_b; g.eps = c.norm_eps;
     g.y = h->qkv; g.y_stride = nqkv;
     LAUNCH(hk, s, SDEC_K_QKV, launch_gemv(g, h->plan_qkv[l], s));
-    // ring attention; it also finishes this step's q/k (qk-norm, rope) and pushes k/v
     float* att = taps ? h->attn_out + static_cast<size_t>(l) * c.m * qw : h->attn_out;
+    if (short_attn) {
+      // attention (qk-norm, rope, push, softmax over the few legal slots) inside the o launch
+      GemvArgs o{};
+      o.w[0] = o.w[1] = o.w[2] = w.wo;
+      o.seg_end[0] = o.seg_end[1] = o.seg_end[2] = c.d_model;
+      o.n_rows = c.d_model; o.k = qw; o.m = 1;
+      o.x_tap = taps ? att : nullptr;
+      o.res = h->xres; o.res_stride = c.d_model; o.ls = c.layer_scale ? w.ls1 : nullptr;
+      o.tap = taps ? h->tap_attn_proj + static_cast<size_t>(l) * c.d_model : nullptr;
+      o.tap_stride = c.d_model;
+      ShortAttnArgs& sa = o.sa;
+      sa.qkv = h->qkv;
+      sa.q_norm = c.qk_norm ? w.q_norm : nullptr; sa.k_norm = c.qk_norm ? w.k_norm : nullptr;
+      sa.eps = c.qk_norm_eps; sa.rope_style = c.rope == SDEC_ROPE_HALF ? 0 : 1; sa.cs = h->cs;
+      sa.k_ring = ring_at(h, h->k_rings, 0, l); sa.v_ring = ring_at(h, h->v_rings, 0, l);
+      sa.legal = h->legal; sa.n_legal = h->n_legal; sa.st = h->st;
+      sa.n_q_heads = hq; sa.n_kv_heads = hkv; sa.ring = h->ring;
+      LAUNCH(hk, s, SDEC_K_O, launch_gemv(o, h->plan_o_short, s));
+    } else {
+    // ring attention; it also finishes this step's q/k (qk-norm, rope) and pushes k/v
     AttnArgs aa{};
     aa.qkv = h->qkv; aa.qkv_stride = nqkv;
     aa.q_norm = c.qk_norm ? w.q_norm : nullptr; aa.k_norm = c.qk_norm ? w.k_norm : nullptr;
@@ -269,6 +297,7 @@ int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk) {
     o.tap = taps ? h->tap_attn_proj + static_cast<size_t>(l) * c.m * c.d_model : nullptr;
     o.tap_stride = c.d_model;
     LAUNCH(hk, s, SDEC_K_O, launch_gemv(o, h->plan_o[l], s));
+    }
     // FFN norm + up projection(s) + activation
     GemvArgs u{};
     if (c.ffn == SDEC_FFN_SWIGLU) {
@@ -293,6 +322,21 @@ int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk) {
     LAUNCH(hk, s, SDEC_K_FFN_DOWN, launch_gemv(dn, h->plan_down[l], s));
   }
   return SDEC_OK;
+}
+
+// Whether this step attends at most kShortSlots slots whatever the rings hold: the legal positions
+// are distinct and lie in (pos - window, pos] and in the stream's history [hist_start, pos] when it
+// is known (else [0, pos]).  Also records where the stream's history starts.
+bool short_step(sdec_handle* h, uint32_t pos, uint32_t first) {
+  if (first || (h->hist_known && h->hist_start == 0xFFFFFFFFu)) {
+    h->hist_known = true;
+    h->hist_start = pos;
+  }
+  if (!h->short_ok) return false;
+  const uint64_t span = h->hist_known ? static_cast<uint64_t>(pos) - h->hist_start + 1
+                                      : static_cast<uint64_t>(pos) + 1;
+  const uint64_t bound = span < h->cfg.window ? span : h->cfg.window;
+  return bound <= kShortSlots;
 }
 
 int check_step(sdec_handle* h, const float* x, uint32_t pos, uint32_t first) {
@@ -607,6 +651,11 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
     const char* fe = std::getenv("SDEC_ATTN_COMBINE_IN_O");  // tuning override: "0" = combine in attention
     h->attn_fused = gemv_supported(fused, qw, c.m) && !(fe != nullptr && fe[0] == '0');
   }
+  const char* se = std::getenv("SDEC_SHORT_ATTN");  // tuning override: "0" keeps the attention launch
+  if (c.m == 1 && !(se != nullptr && se[0] == '0')) {
+    h->plan_o_short = plan_attn_short_o(c.d_model, qw, hd, hq, hkv);
+    h->short_ok = gemv_supported(h->plan_o_short, qw, 1);
+  }
   for (uint32_t l = 0; l < c.n_layers; ++l) {
     h->plan_qkv.push_back(plan_gemv(c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN, EPI_STORE,
                                     qw + 2 * kw, c.d_model, c.m));
@@ -632,19 +681,22 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
   if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "init: %s", hipGetErrorString(e)));
 
   if (!(c.flags & SDEC_FLAG_EAGER)) {
-    e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal);
-    if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "begin capture: %s", hipGetErrorString(e)));
-    r = enqueue_layers(h, h->cap_stream, nullptr);
-    hipGraph_t graph = nullptr;
-    e = hipStreamEndCapture(h->cap_stream, &graph);
-    if (r != SDEC_OK) {
-      if (graph) (void)hipGraphDestroy(graph);
-      return bail(r);
+    // record the layer launches once per plan: the general one, and the short-context one
+    for (int pass = 0; pass < (h->short_ok ? 2 : 1); ++pass) {
+      e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal);
+      if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "begin capture: %s", hipGetErrorString(e)));
+      r = enqueue_layers(h, h->cap_stream, nullptr, pass == 1);
+      hipGraph_t graph = nullptr;
+      e = hipStreamEndCapture(h->cap_stream, &graph);
+      if (r != SDEC_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return bail(r);
+      }
+      if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "end capture: %s", hipGetErrorString(e)));
+      e = hipGraphInstantiate(pass == 1 ? &h->exec_short : &h->exec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "graph instantiate: %s", hipGetErrorString(e)));
     }
-    if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "end capture: %s", hipGetErrorString(e)));
-    e = hipGraphInstantiate(&h->exec, graph, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(graph);
-    if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "graph instantiate: %s", hipGetErrorString(e)));
     h->graph_ready = true;
   }
   *out = h;
@@ -657,10 +709,11 @@ int sdec_step(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stre
   hipStream_t s = static_cast<hipStream_t>(stream);
   r = enqueue_begin(h, x, pos, first, s, nullptr);
   if (r != SDEC_OK) return r;
+  const bool use_short = short_step(h, pos, first);
   if (h->graph_ready) {
-    HIP_TRY(hipGraphLaunch(h->exec, s));
+    HIP_TRY(hipGraphLaunch(use_short ? h->exec_short : h->exec, s));
   } else {
-    r = enqueue_layers(h, s, nullptr);
+    r = enqueue_layers(h, s, nullptr, use_short);
     if (r != SDEC_OK) return r;
   }
   r = enqueue_end(h, x, s, nullptr);
@@ -691,6 +744,7 @@ int sdec_prefill(sdec_handle* h, float* x, uint32_t pos, uint32_t t, uint32_t fi
     return fail(SDEC_E_CAPACITY, "positions up to %u exceed the %u-slot ring of an unbounded stack",
                 pos + t - 1, h->ring);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)short_step(h, pos, first);  // records where the stream's history starts
   r = enqueue_prefill(h, x, pos, t, first, s, nullptr);
   if (r != SDEC_OK) return r;
   h->has_next = true;
@@ -710,8 +764,9 @@ int sdec_step_profile(sdec_handle* h, float* x, uint32_t pos, uint32_t first, vo
   for (auto& e : ev) HIP_TRY(hipEventCreate(&e));
   Hooks hk;
   hk.ev = ev.data(); hk.kinds = kinds.data(); hk.cap = cap;
+  const bool use_short = short_step(h, pos, first);
   r = enqueue_begin(h, x, pos, first, s, &hk);
-  if (r == SDEC_OK) r = enqueue_layers(h, s, &hk);
+  if (r == SDEC_OK) r = enqueue_layers(h, s, &hk, use_short);
   if (r == SDEC_OK) r = enqueue_end(h, x, s, &hk);
   hipError_t e = hipStreamSynchronize(s);
   if (r == SDEC_OK && e != hipSuccess) r = fail(SDEC_E_HIP, "sync: %s", hipGetErrorString(e));
@@ -739,6 +794,8 @@ int sdec_reset(sdec_handle* h, void* stream) {
   if (r != SDEC_OK) return r;
   h->has_next = false;
   h->next_pos = 0;
+  h->hist_known = true;
+  h->hist_start = 0xFFFFFFFFu;
   return SDEC_OK;
 }
 
@@ -752,6 +809,7 @@ void sdec_destroy(sdec_handle* h) {
   if (!h) return;
   (void)hipDeviceSynchronize();
   if (h->exec) (void)hipGraphExecDestroy(h->exec);
+  if (h->exec_short) (void)hipGraphExecDestroy(h->exec_short);
   if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
   free_handle_memory(h);
   delete h;
@@ -773,6 +831,7 @@ int sdec_set_next_position(sdec_handle* h, uint32_t next_pos) {
   if (next_pos == kInvalidPos) return fail(SDEC_E_ARG, "bad position");
   h->has_next = true;
   h->next_pos = next_pos;
+  h->hist_known = false;  // the imported history may hold any positions below next_pos
   return SDEC_OK;
 }
 

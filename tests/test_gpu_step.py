@@ -122,8 +122,33 @@ def test_codec_kv_ring_contents_past_wrap(sd):
 
 
 def test_talker_first_positions(sd):
+    # Positions 0..39: up to 31 the attention runs inside the o-projection launch (at most 32
+    # legal slots), from 32 on in its own launch.
     cfg = wl.CONFIGS[4]
-    run_parity(sd, cfg, 24, ring_check=True)
+    run_parity(sd, cfg, 40, ring_check=True)
+
+
+@pytest.mark.parametrize("short", ["1", "0"])
+def test_talker_short_context_over_an_import(sd, short, monkeypatch):
+    # Positions 20..21 over a seeded import of 0..19 (the step cannot know the imported history,
+    # so it bounds the legal slots by pos + 1 = 21): with the attention inside the o launch and,
+    # for comparison, with the attention launch kept.
+    monkeypatch.setenv("SDEC_SHORT_ATTN", short)
+    cfg = wl.CONFIGS[4]
+    layers, final = weights(cfg)
+    dec = make(sd, cfg)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    _import_prefill(sd, dec, orc, cfg, 20, [0])
+    xs = wl.make_inputs(cfg, 22)
+    x = torch.empty((1, cfg.d_model), device="cuda")
+    for q in (20, 21):
+        x.copy_(torch.from_numpy(xs[q]))
+        dec.step(x, q)
+        want = orc.step(xs[q], q)
+        cos, mx = assert_close_rows(x.cpu().numpy(), want, f"talker short={short} pos {q}")
+        np.testing.assert_array_equal(read_pos_ring(sd, dec, 0, cfg.ring), orc.P[0])
+    log(f"talker short={short} over an import: cos {cos:.9f} max|d| {mx:.3e}")
+    dec.close()
 
 
 def _import_prefill(sd, dec, orc, cfg, n_pos, streams):
@@ -330,8 +355,10 @@ def collect(dec, cfg, xs, positions, firsts=()):
 
 @pytest.mark.parametrize("cfg", [SMALL_T, SMALL_C], ids=["T", "C"])
 def test_graph_replay_equals_eager_and_is_deterministic(sd, cfg):
-    xs = wl.make_inputs(cfg, 30)
-    pos = list(range(30))
+    # 40 positions: both recorded plans (attention inside the o launch up to 32 legal slots, in its
+    # own launch after) replay bit for bit like the eager launches
+    xs = wl.make_inputs(cfg, 40)
+    pos = list(range(40))
     g1 = collect(make(sd, cfg), cfg, xs, pos)
     g2 = collect(make(sd, cfg), cfg, xs, pos)
     e1 = collect(make(sd, cfg, eager=True), cfg, xs, pos)
