@@ -44,6 +44,7 @@ struct ShortAttnArgs {
   const uint32_t* n_legal;
   const DevState* st;        // slot of this step's push
   uint32_t n_q_heads, n_kv_heads, ring;
+  int early_rows;            // GEMV tile rows requested before the ring rows are in (tuning)
 };
 
 // y = x . W^T over up to three row segments (q, k, v share one launch).  With EPI_SWIGLU the

@@ -440,17 +440,8 @@ __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, 
     ld8(sa.qkv + static_cast<size_t>(hq + g0 + h) * HD + 8 * sub, k8[h]);
     ld8(sa.qkv + static_cast<size_t>(hq + hkv + g0 + h) * HD + 8 * sub, v8[h]);
   }
-  if (sa.q_norm) { ld8(sa.q_norm + 8 * sub, gq); ld8(sa.k_norm + 8 * sub, gk); }
-  if (sa.rope_style == 0) {  // element d takes frequency d mod hd/2: 8 consecutive ones
-    ld8(sa.cs + (8 * sub) % HALF, cv);
-    ld8(sa.cs + HALF + (8 * sub) % HALF, sv);
-  } else {                   // element d takes frequency d / 2: 4 consecutive ones, twice each
-    const float4 c4 = reinterpret_cast<const float4*>(sa.cs + 4 * sub)[0];
-    const float4 s4 = reinterpret_cast<const float4*>(sa.cs + HALF + 4 * sub)[0];
-    cv[0] = cv[1] = c4.x; cv[2] = cv[3] = c4.y; cv[4] = cv[5] = c4.z; cv[6] = cv[7] = c4.w;
-    sv[0] = sv[1] = s4.x; sv[2] = sv[3] = s4.y; sv[4] = sv[5] = s4.z; sv[6] = sv[7] = s4.w;
-  }
-  // round trip 2 starts as soon as the list is in: every older slot's key and value rows
+  // round trip 2 starts as soon as the list is in: every older slot's key and value rows, then
+  // the norm gains and the rope cos/sin (not needed before the rows arrive)
   float4 K[HPW][SPG][2], V[HPW][SPG][2];
   const size_t row = static_cast<size_t>(hkv) * HD;
 #pragma unroll
@@ -462,6 +453,16 @@ __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, 
       K[h][j][0] = kp[0]; K[h][j][1] = kp[1];
       V[h][j][0] = vp[0]; V[h][j][1] = vp[1];
     }
+  if (sa.q_norm) { ld8(sa.q_norm + 8 * sub, gq); ld8(sa.k_norm + 8 * sub, gk); }
+  if (sa.rope_style == 0) {  // element d takes frequency d mod hd/2: 8 consecutive ones
+    ld8(sa.cs + (8 * sub) % HALF, cv);
+    ld8(sa.cs + HALF + (8 * sub) % HALF, sv);
+  } else {                   // element d takes frequency d / 2: 4 consecutive ones, twice each
+    const float4 c4 = reinterpret_cast<const float4*>(sa.cs + 4 * sub)[0];
+    const float4 s4 = reinterpret_cast<const float4*>(sa.cs + HALF + 4 * sub)[0];
+    cv[0] = cv[1] = c4.x; cv[2] = cv[3] = c4.y; cv[4] = cv[5] = c4.z; cv[6] = cv[7] = c4.w;
+    sv[0] = sv[1] = s4.x; sv[2] = sv[3] = s4.y; sv[4] = sv[5] = s4.z; sv[6] = sv[7] = s4.w;
+  }
   // (1) the ring rows are in: only now do the GEMV waves start their weight stream, so these
   // requests were not queued behind it; the math below overlaps the stream
   __builtin_amdgcn_s_waitcnt(0);
@@ -518,15 +519,6 @@ __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, 
 #pragma unroll
     for (int q = 0; q < G; ++q) rope(q8[h][q]);
     rope(k8[h]);
-    if (blockIdx.x == 0 && grp == 0) {  // workgroup 0 pushes this step's key and value
-      const size_t roff = (static_cast<size_t>(push_slot) * hkv + g) * HD + 8 * sub;
-      float4* kd = reinterpret_cast<float4*>(sa.k_ring + roff);
-      float4* vd = reinterpret_cast<float4*>(sa.v_ring + roff);
-      kd[0] = make_float4(k8[h][0], k8[h][1], k8[h][2], k8[h][3]);
-      kd[1] = make_float4(k8[h][4], k8[h][5], k8[h][6], k8[h][7]);
-      vd[0] = make_float4(v8[h][0], v8[h][1], v8[h][2], v8[h][3]);
-      vd[1] = make_float4(v8[h][4], v8[h][5], v8[h][6], v8[h][7]);
-    }
     // every score of the group first (independent dot products and reductions), then the
     // group's max, the exponentials and the sums: slot 0 is the pushed one (group 0 only)
     float sc[NS][G];
@@ -663,6 +655,21 @@ __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, 
       }
     }
   }
+  // workgroup 0 pushes this step's roped keys and values into ring slot pos mod R, after its
+  // attention row is out (nothing in this launch reads them back)
+  __syncthreads();  // (2) the attention row is in LDS
+  if (blockIdx.x == 0 && grp == 0) {
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      const size_t roff = (static_cast<size_t>(push_slot) * hkv + g0 + h) * HD + 8 * sub;
+      float4* kd = reinterpret_cast<float4*>(sa.k_ring + roff);
+      float4* vd = reinterpret_cast<float4*>(sa.v_ring + roff);
+      kd[0] = make_float4(k8[h][0], k8[h][1], k8[h][2], k8[h][3]);
+      kd[1] = make_float4(k8[h][4], k8[h][5], k8[h][6], k8[h][7]);
+      vd[0] = make_float4(v8[h][0], v8[h][1], v8[h][2], v8[h][3]);
+      vd[1] = make_float4(v8[h][4], v8[h][5], v8[h][6], v8[h][7]);
+    }
+  }
 }
 
 // Rows per GEMV tile of k_attn_short_o for an input row of 256 KB floats (every SIMD of a
@@ -679,26 +686,32 @@ __global__ __launch_bounds__(kWgThreads + NAW * kWave) void k_attn_short_o(GemvA
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (wave >= NGW) {
     short_attention_wave<HD, G, HPW>(a, wave - NGW, reinterpret_cast<float*>(xsh));
-    __syncthreads();  // (2) the attention row is in LDS
-    return;
+    return;  // it has passed barrier (2)
   }
   const uint32_t n_tiles = (a.n_rows + R - 1) / R;
   const uint32_t ts = gridDim.x * NGW;
   uint32_t t = blockIdx.x * NGW + wave;
   float4 w0[KB][R];
   ResPre p0;
-  auto load_tile = [&](uint32_t tt) {
+  // rows [r0, r1) of a tile (then the old residual): the first tile's rows below
+  // sa.early_rows are requested before the attention waves' ring rows are in, the rest after
+  auto load_tile = [&](uint32_t tt, int r0, int r1) {
     const float4* wr[R];
     tile_rows<R, EPI>(a, tt, wr);
 #pragma unroll
-    for (int j = 0; j < KB; ++j)
+    for (int r = 0; r < R; ++r)
+      if (r >= r0 && r < r1) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) w0[j][r] = ldw(wr[r] + lane + kWave * j);
-    p0 = residual_prefetch<M, R, EPI>(a, tt, lane);
+        for (int j = 0; j < KB; ++j) w0[j][r] = ldw(wr[r] + lane + kWave * j);
+      }
+    if (r1 == R) p0 = residual_prefetch<M, R, EPI>(a, tt, lane);
   };
-  __syncthreads();  // (1) the attention waves' ring rows have arrived
   // unconditional (a wave without a tile loads the last one and never uses it)
-  load_tile(t < n_tiles ? t : n_tiles - 1);
+  const uint32_t t0 = t < n_tiles ? t : n_tiles - 1;
+  const int early = a.sa.early_rows < R ? a.sa.early_rows : R;
+  load_tile(t0, 0, early);
+  __syncthreads();  // (1) the attention waves' ring rows have arrived
+  load_tile(t0, early, R);
   __syncthreads();  // (2) the attention waves have left the attention row in LDS
   float4 xr[KB];
 #pragma unroll
@@ -716,7 +729,7 @@ __global__ __launch_bounds__(kWgThreads + NAW * kWave) void k_attn_short_o(GemvA
       for (int r = 0; r < R; ++r) acc[r] = dot4(w0[j][r], xr[j], acc[r]);
     gemv_epilogue<M, R, EPI>(a, t, acc, lane, &p0);
     if ((t += ts) >= n_tiles) break;
-    load_tile(t);
+    load_tile(t, 0, R);
   }
 }
 

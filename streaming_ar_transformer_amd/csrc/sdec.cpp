@@ -78,6 +78,7 @@ struct sdec_handle {
   // (no attention launch); a second graph records that plan
   bool short_ok = false;
   GemvLaunch plan_o_short{};
+  int short_early_rows = 0;  // tuning override SDEC_SHORT_EARLY
   // one stream: the attention launch leaves its chunk partials and the o projection combines them
   bool attn_fused = false;
   // several streams: attention items split each stream's legal slots evenly (n_chunks per kv head)
@@ -265,6 +266,7 @@ int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk, bool short_attn = f
       sa.k_ring = ring_at(h, h->k_rings, 0, l); sa.v_ring = ring_at(h, h->v_rings, 0, l);
       sa.legal = h->legal; sa.n_legal = h->n_legal; sa.st = h->st;
       sa.n_q_heads = hq; sa.n_kv_heads = hkv; sa.ring = h->ring;
+      sa.early_rows = h->short_early_rows;
       LAUNCH(hk, s, SDEC_K_O, launch_gemv(o, h->plan_o_short, s));
     } else {
     // ring attention; it also finishes this step's q/k (qk-norm, rope) and pushes k/v
@@ -655,6 +657,8 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
   if (c.m == 1 && !(se != nullptr && se[0] == '0')) {
     h->plan_o_short = plan_attn_short_o(c.d_model, qw, hd, hq, hkv);
     h->short_ok = gemv_supported(h->plan_o_short, qw, 1);
+    const char* ee = std::getenv("SDEC_SHORT_EARLY");
+    h->short_early_rows = ee && *ee ? atoi(ee) : 0;
   }
   for (uint32_t l = 0; l < c.n_layers; ++l) {
     h->plan_qkv.push_back(plan_gemv(c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN, EPI_STORE,
