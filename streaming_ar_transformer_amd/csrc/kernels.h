@@ -15,6 +15,7 @@ constexpr int kWgThreads = 256;  // four wave64s
 struct DevState {
   uint32_t pos;
   uint32_t slot;
+  float* x_out;  // the caller's output rows of this step
 };
 
 // PRO_ATTN: the input row is this step's attention output, combined in the prologue from the
@@ -142,6 +143,7 @@ uint32_t attention_chunk(uint32_t head_dim);
 
 struct BeginArgs {
   const float* x_in;     // caller rows [m][d]
+  float* x_out;          // where the step's output rows go (recorded in DevState)
   float* xres;           // residual stream [m][d]
   uint32_t d;
   uint32_t* pos_rings;   // [m][R]
@@ -181,7 +183,8 @@ hipError_t launch_push(const PushArgs& a, hipStream_t s);
 
 struct EndArgs {
   const float* xres;     // [m][d]
-  float* x_out;          // [m][d]
+  float* x_out;          // [m][d]; null: the rows DevState::x_out names (set by the step begin)
+  const DevState* st;
   uint32_t m, d;
   int norm;              // -1: copy, PRO_RMS or PRO_LN
   const float* w;

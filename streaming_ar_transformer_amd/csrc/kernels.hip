@@ -1297,6 +1297,7 @@ __global__ __launch_bounds__(kWgThreads) void k_begin(BeginArgs a) {
     if (tid == 0) {
       a.st->pos = a.pos;
       a.st->slot = slot;
+      a.st->x_out = a.x_out;
     }
     return;
   }
@@ -1474,7 +1475,7 @@ __global__ __launch_bounds__(kWgThreads) void k_end(EndArgs a) {
   __shared__ float red[2][kWgThreads / kWave];
   const uint32_t r = blockIdx.x;
   const float* x = a.xres + static_cast<size_t>(r) * a.d;
-  float* y = a.x_out + static_cast<size_t>(r) * a.d;
+  float* y = (a.x_out != nullptr ? a.x_out : a.st->x_out) + static_cast<size_t>(r) * a.d;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const uint32_t d4 = a.d >> 2;
   if (a.norm < 0 || d4 > 4 * kWgThreads) {  // a copy, or a row wider than the register tile

@@ -354,23 +354,25 @@ int check_step(sdec_handle* h, const float* x, uint32_t pos, uint32_t first) {
   return SDEC_OK;
 }
 
-int enqueue_begin(sdec_handle* h, const float* x, uint32_t pos, uint32_t first, hipStream_t s,
+int enqueue_begin(sdec_handle* h, float* x, uint32_t pos, uint32_t first, hipStream_t s,
                   Hooks* hk) {
   const sdec_config& c = h->cfg;
   BeginArgs b{};
   b.x_in = x; b.xres = h->xres; b.d = c.d_model; b.pos_rings = h->pos_rings;
   b.legal = h->legal; b.n_legal = h->n_legal;
   b.m = c.m; b.ring = h->ring; b.window = c.window; b.pos = pos; b.first = first ? 1u : 0u;
-  b.cs = h->cs;
+  b.cs = h->cs; b.x_out = x;
   b.head_dim = c.head_dim; b.theta = c.rope_theta; b.st = h->st;
   LAUNCH(hk, s, SDEC_K_BEGIN, launch_begin(b, s));
   return SDEC_OK;
 }
 
+// x null: the output rows the step begin recorded in the device state (so the launch can sit in
+// the recorded graph)
 int enqueue_end(sdec_handle* h, float* x, hipStream_t s, Hooks* hk) {
   const sdec_config& c = h->cfg;
   EndArgs e{};
-  e.xres = h->xres; e.x_out = x; e.m = c.m; e.d = c.d_model;
+  e.xres = h->xres; e.x_out = x; e.st = h->st; e.m = c.m; e.d = c.d_model;
   e.norm = c.final_norm ? (c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN) : -1;
   e.w = h->fin.norm_w; e.b = h->fin.norm_b; e.eps = c.norm_eps;
   LAUNCH(hk, s, SDEC_K_END, launch_end(e, s));
@@ -690,6 +692,7 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
       e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal);
       if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "begin capture: %s", hipGetErrorString(e)));
       r = enqueue_layers(h, h->cap_stream, nullptr, pass == 1);
+      if (r == SDEC_OK) r = enqueue_end(h, nullptr, h->cap_stream, nullptr);  // the last node
       hipGraph_t graph = nullptr;
       e = hipStreamEndCapture(h->cap_stream, &graph);
       if (r != SDEC_OK) {
@@ -714,14 +717,14 @@ int sdec_step(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stre
   r = enqueue_begin(h, x, pos, first, s, nullptr);
   if (r != SDEC_OK) return r;
   const bool use_short = short_step(h, pos, first);
-  if (h->graph_ready) {
+  if (h->graph_ready) {  // the graph ends with the end launch
     HIP_TRY(hipGraphLaunch(use_short ? h->exec_short : h->exec, s));
   } else {
     r = enqueue_layers(h, s, nullptr, use_short);
     if (r != SDEC_OK) return r;
+    r = enqueue_end(h, x, s, nullptr);
+    if (r != SDEC_OK) return r;
   }
-  r = enqueue_end(h, x, s, nullptr);
-  if (r != SDEC_OK) return r;
   h->has_next = true;
   h->next_pos = pos + 1;
   return SDEC_OK;
