@@ -146,8 +146,12 @@ void sdec_destroy(sdec_handle* h);
 
 /* Which step path the handle runs: 0 = the per-layer launches recorded once as a hipGraph and
  * replayed per step ([talker] StepPlan: the plan is built once and replayed per token), 1 = the
- * same launches enqueued one by one (SDEC_FLAG_EAGER).  path may be NULL. */
-int sdec_status(sdec_handle* h, uint32_t* path);
+ * same launches enqueued one by one (SDEC_FLAG_EAGER).  attention: how the last step's ring
+ * attention ran -- 0 items over chunks of the compacted legal slots, 1 inside the o-projection
+ * launch (at most 21 legal slots), 2 several streams (legal slots dealt to a fixed number of
+ * items).  Every form computes the masked attention of [talker] StepPlan / [mimi] attn_src; they
+ * differ only in how the work is split.  path and attention may be NULL. */
+int sdec_status(sdec_handle* h, uint32_t* path, uint32_t* attention);
 
 /* Message of the last failed call on this thread ("" if none).  Valid until the next call.
  * The pages return errors as a Result carrying the text of the failed check ([talker]

@@ -39,6 +39,20 @@ __device__ __forceinline__ float partner32(float x, int lane) {
   return __uint_as_float((lane & 32) ? p[0] : p[1]);
 }
 
+// The value of lane l ^ OFF (OFF = 8: a DPP row rotation by 8 inside a 16-lane row).
+template <int OFF>
+__device__ __forceinline__ float lane_xor(float x, int lane) {
+  if constexpr (OFF == 32) return partner32(x, lane);
+  else if constexpr (OFF == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((lane & 16) ? p[0] : p[1]);
+  } else if constexpr (OFF == 8) {
+    return dpp_mov<0x128>(x);  // row_ror:8 -- lane i of a 16-lane row reads lane i ^ 8
+  } else {
+    return __shfl_xor(x, OFF);
+  }
+}
+
 // Sum over the whole wave, left in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_mov<kDppXor1>(v);
@@ -488,13 +502,15 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   }
   __syncthreads();  // queries and this step's key are in LDS
 
-  // 4. online softmax over this group's share of the legal slots
+  // 4. online softmax over this group's share of the legal slots.  Scores are kept in log2 units
+  //    (q.k log2(e) / sqrt(hd)), so every exponential is one exp2 instruction; the chunk maxima
+  //    left in the partials are in the same units.
   float q[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[g][e] = qs[g][8 * sub + e];
-  const float scale = 1.0f / sqrtf(static_cast<float>(HD));
+  const float scale = 1.4426950408889634f / sqrtf(static_cast<float>(HD));
   float mrun[G], lrun[G], acc[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -533,13 +549,13 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
       for (int u = 1; u < UNR; ++u) mb = fmaxf(mb, sc[u][g]);
       const float mnew = fmaxf(mrun[g], mb);
       if (mnew != -INFINITY) {
-        const float corr = expf(mrun[g] - mnew);
+        const float corr = __builtin_amdgcn_exp2f(mrun[g] - mnew);  // 0 while mrun is -inf
         lrun[g] *= corr;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] *= corr;
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-          const float p = expf(sc[u][g] - mnew);
+          const float p = __builtin_amdgcn_exp2f(sc[u][g] - mnew);  // 0 for a masked slot
           const float vf[8] = {V[u][0].x, V[u][0].y, V[u][0].z, V[u][0].w,
                                V[u][1].x, V[u][1].y, V[u][1].z, V[u][1].w};
           lrun[g] += p;
@@ -569,27 +585,51 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
     }
   }
 
-  // 5. merge the slot groups of this workgroup into the chunk's (max, sum, output)
+  // 5. merge the slot groups into the chunk's (max, sum, output): first the GPW groups of each
+  //    wave (lanes LPS, 2 LPS, ... apart hold the same elements) with cross-lane moves, then the
+  //    waves through LDS
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    if (sub == 0) {
-      sm_m[grp][g] = mrun[g];
-      sm_l[grp][g] = lrun[g];
-    }
+    float M = mrun[g];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm_acc[grp][g][8 * sub + e] = acc[g][e];
+    for (int off = LPS; off < kWave; off <<= 1) {
+      const float mo = off == 8 ? lane_xor<8>(M, lane) : off == 16 ? lane_xor<16>(M, lane)
+                                                                   : lane_xor<32>(M, lane);
+      M = fmaxf(M, mo);
+    }
+    const float c = mrun[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[g] - M);
+    float v[9];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = acc[g][e] * c;
+    v[8] = lrun[g] * c;
+#pragma unroll
+    for (int off = LPS; off < kWave; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 9; ++e)
+        v[e] += off == 8 ? lane_xor<8>(v[e], lane) : off == 16 ? lane_xor<16>(v[e], lane)
+                                                               : lane_xor<32>(v[e], lane);
+    if (lane < LPS) {  // the wave's first group writes the wave's merge
+      if (sub == 0) {
+        sm_m[wave][g] = M;
+        sm_l[wave][g] = v[8];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_acc[wave][g][8 * sub + e] = v[e];
+    }
   }
   __syncthreads();
   const bool single = n_items == 1;
   for (int t = tid; t < G * HD; t += NT) {
     const int g = t / HD, d = t % HD;
     float M = -INFINITY;
-    for (int k = 0; k < NG; ++k) M = fmaxf(M, sm_m[k][g]);
+#pragma unroll
+    for (int k = 0; k < NWV; ++k) M = fmaxf(M, sm_m[k][g]);
     float L = 0.f, O = 0.f;
-    for (int k = 0; k < NG; ++k) {
+#pragma unroll
+    for (int k = 0; k < NWV; ++k) {
       const float mk = sm_m[k][g];
       if (mk != -INFINITY) {
-        const float w = expf(mk - M);
+        const float w = __builtin_amdgcn_exp2f(mk - M);
         L = fmaf(w, sm_l[k][g], L);
         O = fmaf(w, sm_acc[k][g][d], O);
       }
@@ -684,12 +724,12 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
         float Mb = Mr[i];
         for (uint32_t c = 0; c < nb; ++c) Mb = fmaxf(Mb, sm_m[c][g]);
         if (Mb != -INFINITY) {
-          const float corr = Mr[i] != -INFINITY ? expf(Mr[i] - Mb) : 0.f;
+          const float corr = Mr[i] != -INFINITY ? __builtin_amdgcn_exp2f(Mr[i] - Mb) : 0.f;
           float L = Lr[i] * corr, O = Or[i] * corr;
           for (uint32_t c = 0; c < nb; ++c) {
             const float mc = sm_m[c][g];
             if (mc != -INFINITY) {
-              const float w = expf(mc - Mb);
+              const float w = __builtin_amdgcn_exp2f(mc - Mb);
               L = fmaf(w, sm_l[c][g], L);
               O = fmaf(w, stage[(c * G + g) * HD + d], O);
             }

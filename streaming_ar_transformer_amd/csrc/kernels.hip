@@ -161,14 +161,14 @@ __device__ __forceinline__ void attn_combine(const GemvArgs& a, uint32_t n_items
     float l = 0.f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j)
-      if (sub + 16u * j < n_items && mv[j] != -INFINITY) l = fmaf(expf(mv[j] - mx), lv[j], l);
+      if (sub + 16u * j < n_items && mv[j] != -INFINITY) l = fmaf(__builtin_amdgcn_exp2f(mv[j] - mx), lv[j], l);
     l = group_sum<16>(l);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     if (h < hq) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         const uint32_t i = sub + 16u * j;
-        if (i < n_items) msh[h * n_items + i] = mv[j] != -INFINITY ? expf(mv[j] - mx) * inv : 0.f;
+        if (i < n_items) msh[h * n_items + i] = mv[j] != -INFINITY ? __builtin_amdgcn_exp2f(mv[j] - mx) * inv : 0.f;
       }
     }
   }
@@ -394,19 +394,6 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
 // requests are not queued behind the weight stream; every workgroup computes the whole
 // attention row (its ring rows come from L2), and workgroup 0 pushes this step's key and value.
 // ------------------------------------------------------------------------------------------------
-
-template <int OFF>
-__device__ __forceinline__ float lane_xor(float x, int lane) {
-  if constexpr (OFF == 32) return partner32(x, lane);
-  else if constexpr (OFF == 16) {
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float((lane & 16) ? p[0] : p[1]);
-  } else if constexpr (OFF == 8) {
-    return dpp_mov<0x128>(x);  // row_ror:8 -- lane i of a 16-lane row reads lane i ^ 8
-  } else {
-    return __shfl_xor(x, OFF);
-  }
-}
 
 template <int HD, int G, int HPW>
 __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, float* out) {

@@ -20,6 +20,10 @@ using namespace sdec;
 
 namespace {
 
+// How a step's attention runs (one recorded graph each): items over chunks of the compacted
+// legal slots, or (few legal slots) inside the o-projection launch.
+enum StepForm { FORM_LIST = 0, FORM_SHORT = 1 };
+
 thread_local std::string g_err;
 
 int fail(int code, const char* fmt, ...) {
@@ -85,9 +89,9 @@ struct sdec_handle {
   bool attn_split = false;
 
   hipStream_t cap_stream = nullptr;
-  hipGraphExec_t exec = nullptr;
-  hipGraphExec_t exec_short = nullptr;
+  hipGraphExec_t exec[2] = {nullptr, nullptr};  // one recorded graph per StepForm
   bool graph_ready = false;
+  uint32_t last_form = 0;
 
   bool has_next = false;
   uint32_t next_pos = 0;
@@ -231,7 +235,8 @@ int hook_post(Hooks* k, hipStream_t s, int kind) {
 
 // The per-token launch sequence of every layer ([talker] build_step_plan; [mimi]
 // Builder::transformer_shaped), on `s`.  Position-dependent values come from h->st.
-int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk, bool short_attn = false) {
+int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk, StepForm form = FORM_LIST) {
+  const bool short_attn = form == FORM_SHORT;
   const sdec_config& c = h->cfg;
   const uint32_t hd = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads;
   const uint32_t qw = hq * hd, kw = hkv * hd, nqkv = qw + 2 * kw;
@@ -326,19 +331,21 @@ int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk, bool short_attn = f
   return SDEC_OK;
 }
 
-// Whether this step attends at most kShortSlots slots whatever the rings hold: the legal positions
-// are distinct and lie in (pos - window, pos] and in the stream's history [hist_start, pos] when it
-// is known (else [0, pos]).  Also records where the stream's history starts.
-bool short_step(sdec_handle* h, uint32_t pos, uint32_t first) {
+// The attention form of this step, from a bound on its legal slots: the legal positions are
+// distinct and lie in (pos - window, pos], in the stream's history [hist_start, pos] when it is
+// known (else [0, pos]), and in the R ring slots.  At most kShortSlots: the short form, else the
+// legal-list form.  Also records where the stream's history starts.
+StepForm step_form(sdec_handle* h, uint32_t pos, uint32_t first) {
   if (first || (h->hist_known && h->hist_start == 0xFFFFFFFFu)) {
     h->hist_known = true;
     h->hist_start = pos;
   }
-  if (!h->short_ok) return false;
   const uint64_t span = h->hist_known ? static_cast<uint64_t>(pos) - h->hist_start + 1
                                       : static_cast<uint64_t>(pos) + 1;
-  const uint64_t bound = span < h->cfg.window ? span : h->cfg.window;
-  return bound <= kShortSlots;
+  uint64_t bound = span < h->cfg.window ? span : h->cfg.window;
+  if (bound > h->ring) bound = h->ring;
+  if (h->short_ok && bound <= kShortSlots) return FORM_SHORT;
+  return FORM_LIST;
 }
 
 int check_step(sdec_handle* h, const float* x, uint32_t pos, uint32_t first) {
@@ -662,6 +669,7 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
     const char* ee = std::getenv("SDEC_SHORT_EARLY");
     h->short_early_rows = ee && *ee ? atoi(ee) : 0;
   }
+
   for (uint32_t l = 0; l < c.n_layers; ++l) {
     h->plan_qkv.push_back(plan_gemv(c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN, EPI_STORE,
                                     qw + 2 * kw, c.d_model, c.m));
@@ -687,11 +695,12 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
   if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "init: %s", hipGetErrorString(e)));
 
   if (!(c.flags & SDEC_FLAG_EAGER)) {
-    // record the layer launches once per plan: the general one, and the short-context one
-    for (int pass = 0; pass < (h->short_ok ? 2 : 1); ++pass) {
+    // record the layer launches once per attention form the handle can take
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass == FORM_SHORT && !h->short_ok) continue;
       e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal);
       if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "begin capture: %s", hipGetErrorString(e)));
-      r = enqueue_layers(h, h->cap_stream, nullptr, pass == 1);
+      r = enqueue_layers(h, h->cap_stream, nullptr, static_cast<StepForm>(pass));
       if (r == SDEC_OK) r = enqueue_end(h, nullptr, h->cap_stream, nullptr);  // the last node
       hipGraph_t graph = nullptr;
       e = hipStreamEndCapture(h->cap_stream, &graph);
@@ -700,7 +709,7 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
         return bail(r);
       }
       if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "end capture: %s", hipGetErrorString(e)));
-      e = hipGraphInstantiate(pass == 1 ? &h->exec_short : &h->exec, graph, nullptr, nullptr, 0);
+      e = hipGraphInstantiate(&h->exec[pass], graph, nullptr, nullptr, 0);
       (void)hipGraphDestroy(graph);
       if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "graph instantiate: %s", hipGetErrorString(e)));
     }
@@ -716,17 +725,18 @@ int sdec_step(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stre
   hipStream_t s = static_cast<hipStream_t>(stream);
   r = enqueue_begin(h, x, pos, first, s, nullptr);
   if (r != SDEC_OK) return r;
-  const bool use_short = short_step(h, pos, first);
+  const StepForm form = step_form(h, pos, first);
   if (h->graph_ready) {  // the graph ends with the end launch
-    HIP_TRY(hipGraphLaunch(use_short ? h->exec_short : h->exec, s));
+    HIP_TRY(hipGraphLaunch(h->exec[form], s));
   } else {
-    r = enqueue_layers(h, s, nullptr, use_short);
+    r = enqueue_layers(h, s, nullptr, form);
     if (r != SDEC_OK) return r;
     r = enqueue_end(h, x, s, nullptr);
     if (r != SDEC_OK) return r;
   }
   h->has_next = true;
   h->next_pos = pos + 1;
+  h->last_form = form;
   return SDEC_OK;
 }
 
@@ -751,7 +761,7 @@ int sdec_prefill(sdec_handle* h, float* x, uint32_t pos, uint32_t t, uint32_t fi
     return fail(SDEC_E_CAPACITY, "positions up to %u exceed the %u-slot ring of an unbounded stack",
                 pos + t - 1, h->ring);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)short_step(h, pos, first);  // records where the stream's history starts
+  (void)step_form(h, pos, first);  // records where the stream's history starts
   r = enqueue_prefill(h, x, pos, t, first, s, nullptr);
   if (r != SDEC_OK) return r;
   h->has_next = true;
@@ -771,9 +781,9 @@ int sdec_step_profile(sdec_handle* h, float* x, uint32_t pos, uint32_t first, vo
   for (auto& e : ev) HIP_TRY(hipEventCreate(&e));
   Hooks hk;
   hk.ev = ev.data(); hk.kinds = kinds.data(); hk.cap = cap;
-  const bool use_short = short_step(h, pos, first);
+  const StepForm form = step_form(h, pos, first);
   r = enqueue_begin(h, x, pos, first, s, &hk);
-  if (r == SDEC_OK) r = enqueue_layers(h, s, &hk, use_short);
+  if (r == SDEC_OK) r = enqueue_layers(h, s, &hk, form);
   if (r == SDEC_OK) r = enqueue_end(h, x, s, &hk);
   hipError_t e = hipStreamSynchronize(s);
   if (r == SDEC_OK && e != hipSuccess) r = fail(SDEC_E_HIP, "sync: %s", hipGetErrorString(e));
@@ -790,6 +800,7 @@ int sdec_step_profile(sdec_handle* h, float* x, uint32_t pos, uint32_t first, vo
     }
     h->has_next = true;
     h->next_pos = pos + 1;
+    h->last_form = form;
   }
   for (auto& ev1 : ev) (void)hipEventDestroy(ev1);
   return r;
@@ -806,17 +817,18 @@ int sdec_reset(sdec_handle* h, void* stream) {
   return SDEC_OK;
 }
 
-int sdec_status(sdec_handle* h, uint32_t* path) {
+int sdec_status(sdec_handle* h, uint32_t* path, uint32_t* attention) {
   if (!h) return fail(SDEC_E_ARG, "null handle");
   if (path) *path = h->graph_ready ? 0u : 1u;
+  if (attention) *attention = h->attn_split ? 2u : h->last_form;
   return SDEC_OK;
 }
 
 void sdec_destroy(sdec_handle* h) {
   if (!h) return;
   (void)hipDeviceSynchronize();
-  if (h->exec) (void)hipGraphExecDestroy(h->exec);
-  if (h->exec_short) (void)hipGraphExecDestroy(h->exec_short);
+  for (hipGraphExec_t g : h->exec)
+    if (g) (void)hipGraphExecDestroy(g);
   if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
   free_handle_memory(h);
   delete h;

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libsdec.so")
 OK, E_ARG, E_POS, E_CAPACITY, E_HIP, E_NOMEM = 0, -1, -2, -3, -4, -5
 FLAG_EAGER, FLAG_TAPS = 1, 2
 PATH_GRAPH, PATH_EAGER = 0, 1
+ATTN_LIST, ATTN_SHORT, ATTN_SPLIT = 0, 1, 2
 K_NAMES = ["begin", "qkv", "attention", "o_proj", "ffn_up", "ffn_down", "end"]
 
 # Every symbol include/sdec.h declares.
@@ -104,7 +105,7 @@ def lib():
             "sdec_step_profile": (i32, [vp, vp, u32, u32, vp, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(u32)]),
             "sdec_gemv": (i32, [vp, vp, vp, u32, u32, u32, vp]),
-            "sdec_status": (i32, [vp, ctypes.POINTER(u32)]),
+            "sdec_status": (i32, [vp, ctypes.POINTER(u32), ctypes.POINTER(u32)]),
             "sdec_ring_attention": (i32, [vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, u32, u32,
                                           vp]),
             "sdec_ring_attention_static": (i32, [vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, u32,
@@ -217,8 +218,15 @@ class Decoder:
     def path(self) -> int:
         """The step path in use: PATH_GRAPH or PATH_EAGER."""
         path = ctypes.c_uint32()
-        _check(lib().sdec_status(self.h, ctypes.byref(path)))
+        _check(lib().sdec_status(self.h, ctypes.byref(path), None))
         return path.value
+
+    @property
+    def attention_form(self) -> int:
+        """How the last step's attention ran: ATTN_LIST, ATTN_SHORT or ATTN_SPLIT."""
+        form = ctypes.c_uint32()
+        _check(lib().sdec_status(self.h, None, ctypes.byref(form)))
+        return form.value
 
     def reset(self, stream=None):
         _check(lib().sdec_reset(self.h, _stream(stream)))

@@ -95,6 +95,7 @@ def test_codec2_full_run(sd):
     run_parity(sd, cfg, cfg.steps, ring_check=True)
 
 
+
 def test_codec8_full_run(sd):
     cfg = wl.CONFIGS[3]
     run_parity(sd, cfg, cfg.steps, ring_check=True)
@@ -122,8 +123,8 @@ def test_codec_kv_ring_contents_past_wrap(sd):
 
 
 def test_talker_first_positions(sd):
-    # Positions 0..39: up to 31 the attention runs inside the o-projection launch (at most 32
-    # legal slots), from 32 on in its own launch.
+    # Positions 0..39: up to 20 the attention runs inside the o-projection launch (at most 21
+    # legal slots), from 21 on in its own launch.
     cfg = wl.CONFIGS[4]
     run_parity(sd, cfg, 40, ring_check=True)
 
@@ -146,6 +147,7 @@ def test_talker_short_context_over_an_import(sd, short, monkeypatch):
         dec.step(x, q)
         want = orc.step(xs[q], q)
         cos, mx = assert_close_rows(x.cpu().numpy(), want, f"talker short={short} pos {q}")
+        assert dec.attention_form == (sd.ATTN_SHORT if short == "1" and q == 20 else sd.ATTN_LIST)
         np.testing.assert_array_equal(read_pos_ring(sd, dec, 0, cfg.ring), orc.P[0])
     log(f"talker short={short} over an import: cos {cos:.9f} max|d| {mx:.3e}")
     dec.close()
@@ -179,6 +181,7 @@ def test_talker_last_positions_from_prefill(sd):
         dec.step(x, p)
         want = orc.step(xs[p], p)
         assert_close_rows(x.cpu().numpy(), want, f"talker pos {p}")
+        assert dec.attention_form == sd.ATTN_LIST
     np.testing.assert_array_equal(read_pos_ring(sd, dec, 0, cfg.ring), orc.P[0])
     with pytest.raises(sd.SdecError) as e:  # the unbounded cache refuses position 2048
         dec.step(x, 2048)
@@ -206,6 +209,37 @@ def test_talker_mid_positions_from_prefill(sd, p):
         cos, mx = assert_close_rows(x.cpu().numpy(), want, f"talker pos {q}")
         np.testing.assert_array_equal(read_pos_ring(sd, dec, 0, cfg.ring), orc.P[0])
     log(f"talker pos {p}..{p + 1}: cos {cos:.9f} max|d| {mx:.3e}")
+    dec.close()
+
+
+def test_talker_over_a_gapped_import(sd):
+    # An imported history with holes (positions 0..99 and 180..299 only; the slots of 100..179
+    # keep the empty stamp) and a stamp ahead of the step (position 1900 in slot 1900, which no
+    # step before 1900 may attend): the legal lists must leave out exactly those slots.
+    cfg = wl.CONFIGS[4]
+    layers, final = weights(cfg)
+    dec = make(sd, cfg)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    K, V = wl.make_prefill(cfg, n_pos=300, streams=[0])[0]
+    keep = np.r_[0:100, 180:300]
+    orc.import_kv(0, K[:, keep], V[:, keep], keep)
+    orc.import_kv(0, K[:, :1], V[:, :1], [1900])  # a stamp ahead of every step below
+    orc.next_pos = 300
+    for li in range(cfg.n_layers):
+        kp, vp, pp = dec.kv_view(0, li)
+        sd.copy_to_device(kp, orc.K[0, li])
+        sd.copy_to_device(vp, orc.V[0, li])
+    sd.copy_to_device(pp, orc.P[0])
+    dec.set_next_position(300)
+    xs = wl.make_inputs(cfg, 2)
+    x = torch.empty((1, cfg.d_model), device="cuda")
+    for i, q in enumerate((300, 301)):
+        x.copy_(torch.from_numpy(xs[i]))
+        dec.step(x, q)
+        want = orc.step(xs[i], q)
+        cos, mx = assert_close_rows(x.cpu().numpy(), want, f"talker gapped pos {q}")
+        np.testing.assert_array_equal(read_pos_ring(sd, dec, 0, cfg.ring), orc.P[0])
+    log(f"talker gapped import: cos {cos:.9f} max|d| {mx:.3e}")
     dec.close()
 
 
