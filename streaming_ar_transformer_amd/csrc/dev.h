@@ -53,6 +53,22 @@ __device__ __forceinline__ float lane_xor(float x, int lane) {
   }
 }
 
+// max / sum of a value and the lane l ^ 16 or l ^ 32 one: the swap returns both in some order, so
+// no lane select is needed (as there is for lane_xor).
+template <int OFF>
+__device__ __forceinline__ float pair_max(float x) {
+  static_assert(OFF == 16 || OFF == 32, "row or half swaps");
+  const auto p = OFF == 16
+      ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+      : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+template <int OFF>
+__device__ __forceinline__ float pair_sum(float x) {
+  static_assert(OFF == 16 || OFF == 32, "row or half swaps");
+  return OFF == 16 ? rows16_sum(x, x) : halves_sum(x, x);
+}
+
 // Sum over the whole wave, left in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_mov<kDppXor1>(v);
@@ -592,11 +608,8 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
   for (int g = 0; g < G; ++g) {
     float M = mrun[g];
 #pragma unroll
-    for (int off = LPS; off < kWave; off <<= 1) {
-      const float mo = off == 8 ? lane_xor<8>(M, lane) : off == 16 ? lane_xor<16>(M, lane)
-                                                                   : lane_xor<32>(M, lane);
-      M = fmaxf(M, mo);
-    }
+    for (int off = LPS; off < kWave; off <<= 1)
+      M = off == 8 ? fmaxf(M, lane_xor<8>(M, lane)) : off == 16 ? pair_max<16>(M) : pair_max<32>(M);
     const float c = mrun[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[g] - M);
     float v[9];
 #pragma unroll
@@ -606,8 +619,7 @@ __device__ __forceinline__ void attention_item(const AttnArgs& a, uint32_t chunk
     for (int off = LPS; off < kWave; off <<= 1)
 #pragma unroll
       for (int e = 0; e < 9; ++e)
-        v[e] += off == 8 ? lane_xor<8>(v[e], lane) : off == 16 ? lane_xor<16>(v[e], lane)
-                                                               : lane_xor<32>(v[e], lane);
+        v[e] = off == 8 ? v[e] + lane_xor<8>(v[e], lane) : off == 16 ? pair_sum<16>(v[e]) : pair_sum<32>(v[e]);
     if (lane < LPS) {  // the wave's first group writes the wave's merge
       if (sub == 0) {
         sm_m[wave][g] = M;

@@ -454,16 +454,21 @@ __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, 
   // requests were not queued behind it; the math below overlaps the stream
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // rotate_half pairs element d with d + hd/2 (lower half: x c - x' s) and d - hd/2 (upper half:
+  // x c + x' s): the sign goes into the sine once
+  if (sa.rope_style == 0 && 8 * sub < HALF) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[e] = -sv[e];
+  }
   // qk-RMSNorm over the hd/8 lanes of a group (the G queries and the key of a kv head at once,
   // so their reduction chains interleave), then rope
   auto rope = [&](float (&x)[8]) {
     float r[8];
-    if (sa.rope_style == 0) {  // rotate_half: element d pairs with d +- hd/2, hd/16 lanes away
-      const bool lo = 8 * sub < HALF;
+    if (sa.rope_style == 0) {  // rotate_half: the partner element is hd/16 lanes away
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float pr = lane_xor<HALF / 8>(x[e], lane);
-        r[e] = lo ? x[e] * cv[e] - pr * sv[e] : x[e] * cv[e] + pr * sv[e];
+        r[e] = fmaf(pr, sv[e], x[e] * cv[e]);
       }
     } else {  // interleaved: pairs (2i, 2i + 1) inside the lane
 #pragma unroll
@@ -476,8 +481,10 @@ __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, 
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = r[e];
   };
-  // scores in log2 units: exponentials are single exp2 instructions
+  // scores in log2 units: exponentials are single exp2 instructions; with the qk-norm the scale
+  // rides on the query's normalisation, otherwise it multiplies each score
   const float scale = 1.4426950408889634f / sqrtf(static_cast<float>(HD));
+  const float sscale = sa.q_norm ? 1.0f : scale;
   constexpr int NS = 1 + SPG;  // the pushed slot, then this group's older slots
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
@@ -496,7 +503,7 @@ __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, 
       for (int q = 0; q <= G; ++q) ss[q] = group_sum<LPS>(ss[q]);
 #pragma unroll
       for (int q = 0; q <= G; ++q) {
-        const float inv = rsqrtf(ss[q] / static_cast<float>(HD) + sa.eps);
+        const float inv = rsqrtf(ss[q] / static_cast<float>(HD) + sa.eps) * (q < G ? scale : 1.0f);
         float* x = q < G ? q8[h][q] : k8[h];
         const float* gn = q < G ? gq : gk;
 #pragma unroll
@@ -540,7 +547,7 @@ __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, 
       for (int j = 0; j < NS; ++j) {
         const uint32_t ent = j == 0 ? 0u : 1u + grp + GPW * (j - 1);
         const bool live = j == 0 ? grp == 0 : (ent < nl && ent < kShortSlots);
-        sc[j][q] = live ? sc[j][q] * scale : -INFINITY;
+        sc[j][q] = live ? sc[j][q] * sscale : -INFINITY;
         mx = fmaxf(mx, sc[j][q]);
       }
       m[q] = mx;
@@ -575,11 +582,9 @@ __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, 
     for (int off = LPS; off < kWave; off <<= 1)
 #pragma unroll
       for (int q = 0; q < G; ++q) {
-        float mo;
-        if (off == 8) mo = lane_xor<8>(M[q], lane);
-        else if (off == 16) mo = lane_xor<16>(M[q], lane);
-        else mo = lane_xor<32>(M[q], lane);
-        M[q] = fmaxf(M[q], mo);
+        if (off == 8) M[q] = fmaxf(M[q], lane_xor<8>(M[q], lane));
+        else if (off == 16) M[q] = pair_max<16>(M[q]);
+        else M[q] = pair_max<32>(M[q]);
       }
     float vals[G * 8 + G];  // rescaled output sums, then the rescaled denominators
 #pragma unroll
@@ -594,8 +599,8 @@ __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, 
     for (int q = 0; q < G; ++q) {
       float t = vals[G * 8 + q];
       if constexpr (LPS <= 8) t += lane_xor<8>(t, lane);
-      if constexpr (LPS <= 16) t += lane_xor<16>(t, lane);
-      t += lane_xor<32>(t, lane);
+      if constexpr (LPS <= 16) t = pair_sum<16>(t);
+      t = pair_sum<32>(t);
       vals[G * 8 + q] = t;
     }
     constexpr int NV = G * 8;
@@ -637,7 +642,7 @@ __device__ __forceinline__ void short_attention_wave(const GemvArgs& a, int aw, 
           const int v = base + i;            // value index: query v / 8, element v % 8
           const int q = v / 8, e = v % 8;
           const float den = vals[G * 8 + q];
-          out[static_cast<size_t>(g * G + q) * HD + 8 * sub + e] = r[i] / den;
+          out[static_cast<size_t>(g * G + q) * HD + 8 * sub + e] = r[i] * __builtin_amdgcn_rcpf(den);
         }
       }
     }
