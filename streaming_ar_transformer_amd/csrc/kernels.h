@@ -157,6 +157,15 @@ struct BeginArgs {
   DevState* st;
 };
 hipError_t launch_begin(const BeginArgs& a, hipStream_t s);
+// One stream: the first layer's q/k/v projection (row-stream kernel, x = the caller's row) and the
+// step begin in one launch.
+struct QkvBeginArgs {
+  GemvArgs g;
+  BeginArgs b;
+  uint32_t gemv_wgs;  // the projection's workgroups (the launch plan's grid)
+};
+bool qkv_begin_supported(const GemvLaunch& l);
+hipError_t launch_qkv_begin(const QkvBeginArgs& a, const GemvLaunch& l, hipStream_t s);
 // Multi-position begin ([talker] TalkerGpu::prefill / forward_rows): the m rows are positions
 // pos .. pos+m-1 of ONE stream whose position ring is pos_rings[0..R).  Stamps every row's slot
 // first, then forms row i's legal list (its own slot first) and its rope cos/sin (cs + i*head_dim).

@@ -823,10 +823,10 @@ __global__ __launch_bounds__(kWgThreads) void k_attention_split(AttnArgs a) {
 // wave's gate sums wait in lane k of one register until its up row k arrives.
 // ------------------------------------------------------------------------------------------------
 template <int KB, int PRO, int EPI>
-__global__ __launch_bounds__(kWgThreads) void k_gemv_rows(GemvArgs a) {
+__device__ __forceinline__ void gemv_rows_body(const GemvArgs& a, uint32_t blk, uint32_t nblk) {
   const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t W = gridDim.x * (kWgThreads / kWave);
-  const uint32_t t = blockIdx.x * (kWgThreads / kWave) +
+  const uint32_t W = nblk * (kWgThreads / kWave);
+  const uint32_t t = blk * (kWgThreads / kWave) +
                      __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t n = a.n_rows;
   const uint32_t total = EPI == EPI_SWIGLU ? 2 * n : n;
@@ -938,6 +938,12 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rows(GemvArgs a) {
     if (!more) return;
   }
 }
+
+template <int KB, int PRO, int EPI>
+__global__ __launch_bounds__(kWgThreads) void k_gemv_rows(GemvArgs a) {
+  gemv_rows_body<KB, PRO, EPI>(a, blockIdx.x, gridDim.x);
+}
+
 
 // ------------------------------------------------------------------------------------------------
 // Split-k GEMV for M input rows (m streams, or the rows of a prefill block), k = NW*256*KW: the
@@ -1270,11 +1276,17 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_ks(GemvArgs a) {
 // up to 64 * kBeginMaxChunks slots (larger rings take the scan of compact_legal).
 constexpr uint32_t kBeginMaxChunks = 1024;
 
-__global__ __launch_bounds__(kWgThreads) void k_begin(BeginArgs a) {
-  __shared__ unsigned long long masks[kBeginMaxChunks];
-  __shared__ uint32_t wcount[kWgThreads / kWave];
-  __shared__ uint32_t scan[kWgThreads];
-  const uint32_t s = blockIdx.x;  // one workgroup per stream, then one for the rope and the state
+struct BeginSmem {
+  unsigned long long masks[kBeginMaxChunks];
+  uint32_t wcount[kWgThreads / kWave];
+  uint32_t scan[kWgThreads];
+};
+
+// Workgroup s of the step begin: s < m takes stream s, s == m the rope table and the state.
+__device__ __forceinline__ void begin_body(const BeginArgs& a, uint32_t s, BeginSmem& sm) {
+  unsigned long long* masks = sm.masks;
+  uint32_t* wcount = sm.wcount;
+  uint32_t* scan = sm.scan;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const uint32_t slot = a.pos % a.ring;
   if (s == a.m) {  // workgroup-uniform: the float64 trig runs beside the streams' compaction
@@ -1378,6 +1390,21 @@ __global__ __launch_bounds__(kWgThreads) void k_begin(BeginArgs a) {
     out[0] = slot;
     a.n_legal[s] = total;
   }
+}
+
+__global__ __launch_bounds__(kWgThreads) void k_begin(BeginArgs a) {
+  __shared__ BeginSmem sm;
+  begin_body(a, blockIdx.x, sm);
+}
+
+// The first layer's normed q/k/v projection and the step begin in one launch: workgroups
+// [0, gemv_wgs) stream the q/k/v rows from the caller's row (which the begin workgroups copy into
+// the residual stream for the later layers), the m + 1 after them do the step begin.
+template <int KB, int PRO>
+__global__ __launch_bounds__(kWgThreads) void k_qkv_begin(QkvBeginArgs a) {
+  __shared__ BeginSmem sm;
+  if (blockIdx.x < a.gemv_wgs) gemv_rows_body<KB, PRO, EPI_STORE>(a.g, blockIdx.x, a.gemv_wgs);
+  else begin_body(a.b, blockIdx.x - a.gemv_wgs, sm);
 }
 
 // Multi-position begin ([talker] TalkerGpu::prefill → forward_rows): the m rows are positions
@@ -1977,6 +2004,21 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.head_dim == 128) return launch_attention_hd<128>(a, s);
   if (a.head_dim == 64) return launch_attention_hd<64>(a, s);
   return hipErrorInvalidValue;
+}
+
+bool qkv_begin_supported(const GemvLaunch& l) {
+  return l.stream && l.kb == 8 && l.epilogue == EPI_STORE &&
+         (l.prologue == PRO_RMS || l.prologue == PRO_LN) && l.waves_per_wg * kWave == kWgThreads;
+}
+
+hipError_t launch_qkv_begin(const QkvBeginArgs& a, const GemvLaunch& l, hipStream_t s) {
+  if (!qkv_begin_supported(l) || a.gemv_wgs != l.grid || a.g.m != 1 || a.b.m != 1)
+    return hipErrorInvalidValue;
+  const void* fn = l.prologue == PRO_RMS ? reinterpret_cast<const void*>(&k_qkv_begin<8, PRO_RMS>)
+                                         : reinterpret_cast<const void*>(&k_qkv_begin<8, PRO_LN>);
+  QkvBeginArgs args = a;
+  void* params[] = {&args};
+  return launch_timed(fn, dim3(l.grid + a.b.m + 1), dim3(kWgThreads), params, 0, s);
 }
 
 hipError_t launch_begin(const BeginArgs& a, hipStream_t s) {

@@ -87,6 +87,9 @@ struct sdec_handle {
   bool attn_fused = false;
   // several streams: attention items split each stream's legal slots evenly (n_chunks per kv head)
   bool attn_split = false;
+  // one stream: the step begin runs in layer 0's q/k/v launch (k_qkv_begin), which therefore sits
+  // outside the recorded graphs (tuning override SDEC_BEGIN_IN_QKV)
+  bool begin_in_qkv = false;
 
   hipStream_t cap_stream = nullptr;
   hipGraphExec_t exec[2] = {nullptr, nullptr};  // one recorded graph per StepForm
@@ -235,7 +238,25 @@ int hook_post(Hooks* k, hipStream_t s, int kind) {
 
 // The per-token launch sequence of every layer ([talker] build_step_plan; [mimi]
 // Builder::transformer_shaped), on `s`.  Position-dependent values come from h->st.
-int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk, StepForm form = FORM_LIST) {
+// The normed q/k/v projection of layer l, reading the residual stream.
+GemvArgs qkv_args(sdec_handle* h, uint32_t l) {
+  const sdec_config& c = h->cfg;
+  const sdec_layer_weights& w = h->layers[l];
+  const uint32_t qw = c.n_q_heads * c.head_dim, kw = c.n_kv_heads * c.head_dim;
+  const uint32_t nqkv = qw + 2 * kw;
+  GemvArgs g{};
+  g.w[0] = w.wq; g.w[1] = w.wk; g.w[2] = w.wv;
+  g.seg_end[0] = qw; g.seg_end[1] = qw + kw; g.seg_end[2] = nqkv;
+  g.n_rows = nqkv; g.k = c.d_model; g.m = c.m;
+  g.x = h->xres; g.x_stride = c.d_model;
+  g.norm_w = w.attn_norm_w; g.norm_b = w.attn_norm_b; g.eps = c.norm_eps;
+  g.y = h->qkv; g.y_stride = nqkv;
+  return g;
+}
+
+// first_qkv false: layer 0's q/k/v projection already ran (with the step begin, k_qkv_begin).
+int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk, StepForm form = FORM_LIST,
+                   bool first_qkv = true) {
   const bool short_attn = form == FORM_SHORT;
   const sdec_config& c = h->cfg;
   const uint32_t hd = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads;
@@ -245,14 +266,10 @@ int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk, StepForm form = FOR
   for (uint32_t l = 0; l < c.n_layers; ++l) {
     const sdec_layer_weights& w = h->layers[l];
     // attention norm + q/k/v projections
-    GemvArgs g{};
-    g.w[0] = w.wq; g.w[1] = w.wk; g.w[2] = w.wv;
-    g.seg_end[0] = qw; g.seg_end[1] = qw + kw; g.seg_end[2] = nqkv;
-    g.n_rows = nqkv; g.k = c.d_model; g.m = c.m;
-    g.x = h->xres; g.x_stride = c.d_model;
-    g.norm_w = w.attn_norm_w; g.norm_b = w.attn_norm_b; g.eps = c.norm_eps;
-    g.y = h->qkv; g.y_stride = nqkv;
-    LAUNCH(hk, s, SDEC_K_QKV, launch_gemv(g, h->plan_qkv[l], s));
+    if (l > 0 || first_qkv) {
+      const GemvArgs g = qkv_args(h, l);
+      LAUNCH(hk, s, SDEC_K_QKV, launch_gemv(g, h->plan_qkv[l], s));
+    }
     float* att = taps ? h->attn_out + static_cast<size_t>(l) * c.m * qw : h->attn_out;
     if (short_attn) {
       // attention (qk-norm, rope, push, softmax over the few legal slots) inside the o launch
@@ -372,6 +389,30 @@ int enqueue_begin(sdec_handle* h, float* x, uint32_t pos, uint32_t first, hipStr
   b.head_dim = c.head_dim; b.theta = c.rope_theta; b.st = h->st;
   LAUNCH(hk, s, SDEC_K_BEGIN, launch_begin(b, s));
   return SDEC_OK;
+}
+
+// The step begin together with layer 0's q/k/v projection, which reads the caller's row.
+int enqueue_qkv_begin(sdec_handle* h, float* x, uint32_t pos, uint32_t first, hipStream_t s,
+                      Hooks* hk) {
+  const sdec_config& c = h->cfg;
+  QkvBeginArgs a{};
+  BeginArgs& b = a.b;
+  b.x_in = x; b.xres = h->xres; b.d = c.d_model; b.pos_rings = h->pos_rings;
+  b.legal = h->legal; b.n_legal = h->n_legal;
+  b.m = c.m; b.ring = h->ring; b.window = c.window; b.pos = pos; b.first = first ? 1u : 0u;
+  b.cs = h->cs; b.x_out = x;
+  b.head_dim = c.head_dim; b.theta = c.rope_theta; b.st = h->st;
+  a.g = qkv_args(h, 0);
+  a.g.x = x;
+  a.gemv_wgs = h->plan_qkv[0].grid;
+  LAUNCH(hk, s, SDEC_K_QKV, launch_qkv_begin(a, h->plan_qkv[0], s));
+  return SDEC_OK;
+}
+
+int enqueue_step_begin(sdec_handle* h, float* x, uint32_t pos, uint32_t first, hipStream_t s,
+                       Hooks* hk) {
+  return h->begin_in_qkv ? enqueue_qkv_begin(h, x, pos, first, s, hk)
+                         : enqueue_begin(h, x, pos, first, s, hk);
 }
 
 // x null: the output rows the step begin recorded in the device state (so the launch can sit in
@@ -680,6 +721,12 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
                                    c.d_model, c.m));
     h->plan_down.push_back(plan_gemv(PRO_NONE, EPI_RESIDUAL, c.d_model, c.d_ff, c.m));
   }
+  {
+    const char* bq = std::getenv("SDEC_BEGIN_IN_QKV");  // tuning override: "0" = separate begin
+    h->begin_in_qkv = c.m == 1 && qkv_begin_supported(h->plan_qkv[0]) &&
+                      !(bq != nullptr && bq[0] == '0');
+  }
+
 
   auto bail = [&](int code) {
     if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
@@ -700,7 +747,7 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
       if (pass == FORM_SHORT && !h->short_ok) continue;
       e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal);
       if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "begin capture: %s", hipGetErrorString(e)));
-      r = enqueue_layers(h, h->cap_stream, nullptr, static_cast<StepForm>(pass));
+      r = enqueue_layers(h, h->cap_stream, nullptr, static_cast<StepForm>(pass), !h->begin_in_qkv);
       if (r == SDEC_OK) r = enqueue_end(h, nullptr, h->cap_stream, nullptr);  // the last node
       hipGraph_t graph = nullptr;
       e = hipStreamEndCapture(h->cap_stream, &graph);
@@ -723,13 +770,13 @@ int sdec_step(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stre
   int r = check_step(h, x, pos, first);
   if (r != SDEC_OK) return r;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  r = enqueue_begin(h, x, pos, first, s, nullptr);
+  r = enqueue_step_begin(h, x, pos, first, s, nullptr);
   if (r != SDEC_OK) return r;
   const StepForm form = step_form(h, pos, first);
   if (h->graph_ready) {  // the graph ends with the end launch
     HIP_TRY(hipGraphLaunch(h->exec[form], s));
   } else {
-    r = enqueue_layers(h, s, nullptr, form);
+    r = enqueue_layers(h, s, nullptr, form, !h->begin_in_qkv);
     if (r != SDEC_OK) return r;
     r = enqueue_end(h, x, s, nullptr);
     if (r != SDEC_OK) return r;
@@ -782,8 +829,8 @@ int sdec_step_profile(sdec_handle* h, float* x, uint32_t pos, uint32_t first, vo
   Hooks hk;
   hk.ev = ev.data(); hk.kinds = kinds.data(); hk.cap = cap;
   const StepForm form = step_form(h, pos, first);
-  r = enqueue_begin(h, x, pos, first, s, &hk);
-  if (r == SDEC_OK) r = enqueue_layers(h, s, &hk, form);
+  r = enqueue_step_begin(h, x, pos, first, s, &hk);
+  if (r == SDEC_OK) r = enqueue_layers(h, s, &hk, form, !h->begin_in_qkv);
   if (r == SDEC_OK) r = enqueue_end(h, x, s, &hk);
   hipError_t e = hipStreamSynchronize(s);
   if (r == SDEC_OK && e != hipSuccess) r = fail(SDEC_E_HIP, "sync: %s", hipGetErrorString(e));

@@ -504,3 +504,29 @@ def test_repeated_step_at_one_position_matches_single_steps(sd):
         np.testing.assert_array_equal(read_pos_ring(sd, dec, 0, cfg.ring), orc.P[0])
     log(f"repeated steps at pos {p}: cos {cos:.9f} max|d| {mx:.3e}")
     dec.close()
+
+
+def test_talker_begin_in_qkv_launch_equals_separate_begin(sd, monkeypatch):
+    # The step begin inside layer 0's q/k/v launch (the default at one stream) and as a launch of
+    # its own give bit-identical outputs over positions 0..24 (both forms of the attention).
+    cfg = wl.CONFIGS[4]
+    layers, final = weights(cfg)
+    monkeypatch.setenv("SDEC_BEGIN_IN_QKV", "0")
+    sep = make(sd, cfg)
+    monkeypatch.delenv("SDEC_BEGIN_IN_QKV")
+    fused = make(sd, cfg)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    xs = wl.make_inputs(cfg, 25)
+    a = torch.empty((1, cfg.d_model), device="cuda")
+    b = torch.empty((1, cfg.d_model), device="cuda")
+    for p in range(25):
+        a.copy_(torch.from_numpy(xs[p]))
+        b.copy_(torch.from_numpy(xs[p]))
+        sep.step(a, p, first=(p == 0))
+        fused.step(b, p, first=(p == 0))
+        want = orc.step(xs[p], p, first=(p == 0))
+        torch.testing.assert_close(a, b, rtol=0, atol=0)
+    assert_close_rows(b.cpu().numpy(), want, "talker begin in qkv, pos 24")
+    np.testing.assert_array_equal(read_pos_ring(sd, fused, 0, cfg.ring), orc.P[0])
+    sep.close()
+    fused.close()
