@@ -60,6 +60,8 @@ def run_parity(sd, cfg, steps, check_every=1, taps=False, ring_check=True):
             continue
         got = x.cpu().numpy()
         cos, mx = assert_close_rows(got, want, f"{cfg.name} pos {p}")
+        if p % 256 == 255:
+            log(f"{cfg.name}: {p + 1} positions compared")
         worst = (min(worst[0], cos), max(worst[1], mx))
         if taps:
             for li in range(cfg.n_layers):
@@ -127,6 +129,43 @@ def test_talker_first_positions(sd):
     # legal slots), from 21 on in its own launch.
     cfg = wl.CONFIGS[4]
     run_parity(sd, cfg, 40, ring_check=True)
+
+
+def test_talker_geometry_two_layers_every_position(sd):
+    # The talker's geometry (hidden 2048, 16/8 heads of 128, SwiGLU 6144, qk-norm, rotate_half
+    # rope) with two of its layers, over its whole 2048-position run from a fresh stream, compared
+    # at every position: the short-context form up to position 20, then the attention launch
+    # with 1 to 16 chunks of 128 slots and the o prologue's combine of each count.
+    cfg = wl.CONFIGS[4].replace(name="talker2_h2048_m1", n_layers=2)
+    run_parity(sd, cfg, cfg.steps, ring_check=True)
+
+
+def test_talker_m8_two_layers_every_step(sd):
+    # The eight-stream talker geometry with two layers over the first 64 steps of its run
+    # (positions 4096..4159 after a seeded 4096-position import into every stream), compared at
+    # every step (the oracle takes about a second per step here).
+    cfg = wl.CONFIGS[5].replace(name="talker2_h2048_m8", n_layers=2, steps=64)
+    layers, final = weights(cfg)
+    dec = make(sd, cfg)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    _import_prefill(sd, dec, orc, cfg, cfg.start_pos, list(range(cfg.m)))
+    xs = wl.make_inputs(cfg, cfg.steps)
+    x = torch.empty((cfg.m, cfg.d_model), device="cuda")
+    worst = (1.0, 0.0)
+    for i in range(cfg.steps):
+        q = cfg.start_pos + i
+        x.copy_(torch.from_numpy(xs[i]))
+        dec.step(x, q)
+        want = orc.step(xs[i], q)
+        cos, mx = assert_close_rows(x.cpu().numpy(), want, f"m8 two layers pos {q}")
+        worst = (min(worst[0], cos), max(worst[1], mx))
+        if i % 16 == 15:
+            log(f"m8 two layers: {i + 1} steps compared")
+    for s in range(cfg.m):
+        np.testing.assert_array_equal(read_pos_ring(sd, dec, s, cfg.ring), orc.P[s])
+    assert dec.attention_form == sd.ATTN_SPLIT
+    log(f"m8 two layers, {cfg.steps} steps: worst cos {worst[0]:.9f} max|d| {worst[1]:.3e}")
+    dec.close()
 
 
 @pytest.mark.parametrize("short", ["1", "0"])
