@@ -231,8 +231,9 @@ __device__ __forceinline__ void attn_input(const GemvArgs& a, float4 (&xr)[KB], 
   }
 }
 
+// Workgroup blk of nblk (kWgThreads threads each).
 template <int M, int R, int PRO, int EPI, int KB>
-__global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
+__device__ __forceinline__ void gemv_rx_body(const GemvArgs& a, uint32_t blk, uint32_t nblk) {
   constexpr int V = R * M;
   static_assert(V <= 64, "tile too large for one wave");
   constexpr int RH = EPI == EPI_SWIGLU ? R / 2 : R;
@@ -240,10 +241,10 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
   // Wave w owns tiles w, w + W, w + 2W, ... (W waves in the grid): at any moment the waves stream
   // neighbouring rows, which the DRAM pages serve better than far-apart contiguous ranges.
   const uint32_t n_tiles = (a.n_rows + RH - 1) / RH;
-  const uint32_t ts = gridDim.x * (blockDim.x / kWave);
+  const uint32_t ts = nblk * (kWgThreads / kWave);
   // wave-uniform, and known to be: the row and segment arithmetic stays scalar, so the weight
   // pointer is never fetched by a vector load (whose wait would also cover every tile in flight)
-  uint32_t t = blockIdx.x * (blockDim.x / kWave) +
+  uint32_t t = blk * (kWgThreads / kWave) +
                __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t t_end = n_tiles;
 
@@ -377,6 +378,11 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
       load_tile(t, w0, p0);
     }
   }
+}
+
+template <int M, int R, int PRO, int EPI, int KB>
+__global__ __launch_bounds__(kWgThreads) void k_gemv_rx(GemvArgs a) {
+  gemv_rx_body<M, R, PRO, EPI, KB>(a, blockIdx.x, gridDim.x);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1406,6 +1412,13 @@ __global__ __launch_bounds__(kWgThreads) void k_qkv_begin(QkvBeginArgs a) {
   if (blockIdx.x < a.gemv_wgs) gemv_rows_body<KB, PRO, EPI_STORE>(a.g, blockIdx.x, a.gemv_wgs);
   else begin_body(a.b, blockIdx.x - a.gemv_wgs, sm);
 }
+// The same with the register GEMV (tiles of R rows; the codec and FlowLM widths).
+template <int R, int PRO, int KB>
+__global__ __launch_bounds__(kWgThreads) void k_qkv_begin_rx(QkvBeginArgs a) {
+  __shared__ BeginSmem sm;
+  if (blockIdx.x < a.gemv_wgs) gemv_rx_body<1, R, PRO, EPI_STORE, KB>(a.g, blockIdx.x, a.gemv_wgs);
+  else begin_body(a.b, blockIdx.x - a.gemv_wgs, sm);
+}
 
 // Multi-position begin ([talker] TalkerGpu::prefill → forward_rows): the m rows are positions
 // pos .. pos+m-1 of one stream.  Every row's slot is stamped before any row's legal list is formed;
@@ -2006,16 +2019,34 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-bool qkv_begin_supported(const GemvLaunch& l) {
-  return l.stream && l.kb == 8 && l.epilogue == EPI_STORE &&
-         (l.prologue == PRO_RMS || l.prologue == PRO_LN) && l.waves_per_wg * kWave == kWgThreads;
+namespace {
+const void* qkv_begin_kernel(const GemvLaunch& l) {
+  if (l.epilogue != EPI_STORE || (l.prologue != PRO_RMS && l.prologue != PRO_LN) ||
+      l.waves_per_wg * kWave != kWgThreads || l.ks > 0)
+    return nullptr;
+  const bool rms = l.prologue == PRO_RMS;
+  if (l.stream) {
+    if (l.kb != 8) return nullptr;
+    return rms ? reinterpret_cast<const void*>(&k_qkv_begin<8, PRO_RMS>)
+               : reinterpret_cast<const void*>(&k_qkv_begin<8, PRO_LN>);
+  }
+  // the register shapes of the codec (R 4, k 512) and FlowLM (R 2, k 1024) projections
+  if (l.rows_per_wave == 4 && l.kb == 2)
+    return rms ? reinterpret_cast<const void*>(&k_qkv_begin_rx<4, PRO_RMS, 2>)
+               : reinterpret_cast<const void*>(&k_qkv_begin_rx<4, PRO_LN, 2>);
+  if (l.rows_per_wave == 2 && l.kb == 4)
+    return rms ? reinterpret_cast<const void*>(&k_qkv_begin_rx<2, PRO_RMS, 4>)
+               : reinterpret_cast<const void*>(&k_qkv_begin_rx<2, PRO_LN, 4>);
+  return nullptr;
 }
+}  // namespace
+
+bool qkv_begin_supported(const GemvLaunch& l) { return qkv_begin_kernel(l) != nullptr; }
 
 hipError_t launch_qkv_begin(const QkvBeginArgs& a, const GemvLaunch& l, hipStream_t s) {
-  if (!qkv_begin_supported(l) || a.gemv_wgs != l.grid || a.g.m != 1 || a.b.m != 1)
+  const void* fn = qkv_begin_kernel(l);
+  if (fn == nullptr || a.gemv_wgs != l.grid || a.g.m != 1 || a.b.m != 1)
     return hipErrorInvalidValue;
-  const void* fn = l.prologue == PRO_RMS ? reinterpret_cast<const void*>(&k_qkv_begin<8, PRO_RMS>)
-                                         : reinterpret_cast<const void*>(&k_qkv_begin<8, PRO_LN>);
   QkvBeginArgs args = a;
   void* params[] = {&args};
   return launch_timed(fn, dim3(l.grid + a.b.m + 1), dim3(kWgThreads), params, 0, s);

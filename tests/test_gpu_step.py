@@ -545,10 +545,12 @@ def test_repeated_step_at_one_position_matches_single_steps(sd):
     dec.close()
 
 
-def test_talker_begin_in_qkv_launch_equals_separate_begin(sd, monkeypatch):
-    # The step begin inside layer 0's q/k/v launch (the default at one stream) and as a launch of
-    # its own give bit-identical outputs over positions 0..24 (both forms of the attention).
-    cfg = wl.CONFIGS[4]
+@pytest.mark.parametrize("cid", [4, 2])
+def test_begin_in_qkv_launch_equals_separate_begin(sd, cid, monkeypatch):
+    # The step begin inside layer 0's q/k/v launch (the default at one stream: the talker's
+    # row-stream projection, the codec's register GEMV) and as a launch of its own give
+    # bit-identical outputs over positions 0..24 (both forms of the attention).
+    cfg = wl.CONFIGS[cid]
     layers, final = weights(cfg)
     monkeypatch.setenv("SDEC_BEGIN_IN_QKV", "0")
     sep = make(sd, cfg)
@@ -565,7 +567,7 @@ def test_talker_begin_in_qkv_launch_equals_separate_begin(sd, monkeypatch):
         fused.step(b, p, first=(p == 0))
         want = orc.step(xs[p], p, first=(p == 0))
         torch.testing.assert_close(a, b, rtol=0, atol=0)
-    assert_close_rows(b.cpu().numpy(), want, "talker begin in qkv, pos 24")
+    assert_close_rows(b.cpu().numpy(), want, f"{cfg.name} begin in qkv, pos 24")
     np.testing.assert_array_equal(read_pos_ring(sd, fused, 0, cfg.ring), orc.P[0])
     sep.close()
     fused.close()
