@@ -289,11 +289,12 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, uint32_t t, flo
         put<COH>(a.y + m * a.y_stride + row, gelu_erf(val));
       } else {
         if (a.tap) a.tap[m * a.tap_stride + row] = val;
+        float* dst = a.res_st != nullptr ? a.res_st->x_out : a.res;
         if (pre) {
-          put<COH>(a.res + m * a.res_stride + row, pre->res + (a.ls ? pre->ls * val : val));
+          put<COH>(dst + m * a.res_stride + row, pre->res + (a.ls ? pre->ls * val : val));
         } else {
           const float* src = (a.res_in ? a.res_in : a.res) + m * a.res_stride + row;
-          put<COH>(a.res + m * a.res_stride + row, *src + (a.ls ? a.ls[row] * val : val));
+          put<COH>(dst + m * a.res_stride + row, *src + (a.ls ? a.ls[row] * val : val));
         }
       }
     }

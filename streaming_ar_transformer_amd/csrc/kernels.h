@@ -64,6 +64,8 @@ struct GemvArgs {
   float* y;              // EPI_STORE / EPI_SWIGLU / EPI_GELU output, [m][y_stride]
   uint32_t y_stride;
   float* res;            // EPI_RESIDUAL target, [m][res_stride]
+  const DevState* res_st;  // non-null (register and generic kernels): the target is res_st->x_out,
+                           // the caller's output rows recorded by the step begin
   uint32_t res_stride;
   const float* res_in;   // EPI_RESIDUAL source of the old residual (null: `res`, in place)
   const float* ls;       // LayerScale or null

@@ -90,6 +90,9 @@ struct sdec_handle {
   // one stream: the step begin runs in layer 0's q/k/v launch (k_qkv_begin), which therefore sits
   // outside the recorded graphs (tuning override SDEC_BEGIN_IN_QKV)
   bool begin_in_qkv = false;
+  // no final norm, one stream: the last down projection writes the caller's rows itself (no end
+  // launch; tuning override SDEC_END_IN_DOWN)
+  bool end_in_down = false;
 
   hipStream_t cap_stream = nullptr;
   hipGraphExec_t exec[2] = {nullptr, nullptr};  // one recorded graph per StepForm
@@ -343,6 +346,10 @@ int enqueue_layers(sdec_handle* h, hipStream_t s, Hooks* hk, StepForm form = FOR
     dn.res = h->xres; dn.res_stride = c.d_model; dn.ls = c.layer_scale ? w.ls2 : nullptr;
     dn.tap = taps ? h->tap_ffn_proj + static_cast<size_t>(l) * c.m * c.d_model : nullptr;
     dn.tap_stride = c.d_model;
+    if (h->end_in_down && l + 1 == c.n_layers) {  // no final norm: the caller's rows directly
+      dn.res_in = h->xres;
+      dn.res_st = h->st;
+    }
     LAUNCH(hk, s, SDEC_K_FFN_DOWN, launch_gemv(dn, h->plan_down[l], s));
   }
   return SDEC_OK;
@@ -722,6 +729,12 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
     h->plan_down.push_back(plan_gemv(PRO_NONE, EPI_RESIDUAL, c.d_model, c.d_ff, c.m));
   }
   {
+    const GemvLaunch& ld = h->plan_down.back();
+    const char* ed = std::getenv("SDEC_END_IN_DOWN");
+    h->end_in_down = c.m == 1 && !c.final_norm && !ld.stream && ld.ks == 0 &&
+                     !(ed != nullptr && ed[0] == '0');
+  }
+  {
     const char* bq = std::getenv("SDEC_BEGIN_IN_QKV");  // tuning override: "0" = separate begin
     h->begin_in_qkv = c.m == 1 && qkv_begin_supported(h->plan_qkv[0]) &&
                       !(bq != nullptr && bq[0] == '0');
@@ -748,7 +761,8 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
       e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal);
       if (e != hipSuccess) return bail(fail(SDEC_E_HIP, "begin capture: %s", hipGetErrorString(e)));
       r = enqueue_layers(h, h->cap_stream, nullptr, static_cast<StepForm>(pass), !h->begin_in_qkv);
-      if (r == SDEC_OK) r = enqueue_end(h, nullptr, h->cap_stream, nullptr);  // the last node
+      if (r == SDEC_OK && !h->end_in_down)
+        r = enqueue_end(h, nullptr, h->cap_stream, nullptr);  // the last node
       hipGraph_t graph = nullptr;
       e = hipStreamEndCapture(h->cap_stream, &graph);
       if (r != SDEC_OK) {
@@ -778,7 +792,7 @@ int sdec_step(sdec_handle* h, float* x, uint32_t pos, uint32_t first, void* stre
   } else {
     r = enqueue_layers(h, s, nullptr, form, !h->begin_in_qkv);
     if (r != SDEC_OK) return r;
-    r = enqueue_end(h, x, s, nullptr);
+    if (!h->end_in_down) r = enqueue_end(h, x, s, nullptr);
     if (r != SDEC_OK) return r;
   }
   h->has_next = true;
@@ -831,7 +845,7 @@ int sdec_step_profile(sdec_handle* h, float* x, uint32_t pos, uint32_t first, vo
   const StepForm form = step_form(h, pos, first);
   r = enqueue_step_begin(h, x, pos, first, s, &hk);
   if (r == SDEC_OK) r = enqueue_layers(h, s, &hk, form, !h->begin_in_qkv);
-  if (r == SDEC_OK) r = enqueue_end(h, x, s, &hk);
+  if (r == SDEC_OK && !h->end_in_down) r = enqueue_end(h, x, s, &hk);
   hipError_t e = hipStreamSynchronize(s);
   if (r == SDEC_OK && e != hipSuccess) r = fail(SDEC_E_HIP, "sync: %s", hipGetErrorString(e));
   if (r == SDEC_OK) {

@@ -571,3 +571,28 @@ def test_begin_in_qkv_launch_equals_separate_begin(sd, cid, monkeypatch):
     np.testing.assert_array_equal(read_pos_ring(sd, fused, 0, cfg.ring), orc.P[0])
     sep.close()
     fused.close()
+
+
+def test_codec_end_in_down_equals_end_launch(sd, monkeypatch):
+    # A stack without a final norm: the last down projection writing the caller's rows itself
+    # (the default at one stream) and a separate end launch give bit-identical outputs.
+    cfg = wl.CONFIGS[2]
+    layers, final = weights(cfg)
+    monkeypatch.setenv("SDEC_END_IN_DOWN", "0")
+    sep = make(sd, cfg)
+    monkeypatch.delenv("SDEC_END_IN_DOWN")
+    fused = make(sd, cfg)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    xs = wl.make_inputs(cfg, 30)
+    a = torch.empty((1, cfg.d_model), device="cuda")
+    b = torch.empty((1, cfg.d_model), device="cuda")
+    for p in range(30):
+        a.copy_(torch.from_numpy(xs[p]))
+        b.copy_(torch.from_numpy(xs[p]))
+        sep.step(a, p, first=(p == 0))
+        fused.step(b, p, first=(p == 0))
+        want = orc.step(xs[p], p, first=(p == 0))
+        torch.testing.assert_close(a, b, rtol=0, atol=0)
+        assert_close_rows(b.cpu().numpy(), want, f"codec end in down, pos {p}")
+    sep.close()
+    fused.close()
