@@ -50,6 +50,8 @@ def parse():
                     help="skip the split-RVQ measurement (64 frames, 8 codebooks of 2048 bins)")
     ap.add_argument("--no-seanet", action="store_true",
                     help="skip the streaming SEANet-decoder measurement")
+    ap.add_argument("--no-pocket", action="store_true",
+                    help="skip the Pocket-style codec frame timing")
     ap.add_argument("--fixed-positions", type=int, default=1,
                     help="also time the step at fixed positions 0, R/2 and R-1 (0: skip)")
     ap.add_argument("--no-configs", action="store_true",
@@ -523,6 +525,43 @@ def main():
         print(f"{scfg.name}: {sms * 1e3:.1f} us/frame", file=sys.stderr, flush=True)
         sdec_.close()
 
+    # Pocket-style codec frame: latent -> 1x1 conv -> channel-wise convtr -> transpose -> the
+    # 2-layer transformer over 16 positions (two prefill blocks of 8) -> transpose -> SEANet
+    pocket = None
+    if not args.no_pocket and args.config == 4:
+        from streaming_ar_transformer_amd.pocket import PocketCodecFrame
+        pc = wl.POCKET_CONFIGS[1]
+        pconv, ptr, psw = wl.make_pocket_frame(pc)
+        dconv = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in pconv.items()}
+        dtr, _ = upload_weights(ptr, {})
+        dsw = {k: torch.from_numpy(v).cuda() for k, v in psw.items()}
+        fr = PocketCodecFrame(pc, dconv, dtr, dsw)
+        n = 64  # 1024 positions: the 266-slot ring wraps three times
+        for i in range(4):
+            fr.decode_frame(dconv["latents"][i % pc.frames], first=(i == 0), stream=stream)
+        fr.decode_frame(dconv["latents"][0], first=True, stream=stream)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(1, n + 1):
+            fr.decode_frame(dconv["latents"][i % pc.frames], stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        fms = start.elapsed_time(end) / n
+        pocket = {"workload": pc.name, "frames": n, "positions": f"{pc.up_stride}..{(n + 1) * pc.up_stride - 1}",
+                  "ms_per_frame": round(fms, 4), "frames_per_s": round(1000.0 / fms, 1),
+                  "samples_per_frame": pc.samples_per_frame,
+                  "realtime_factor_24khz": round(1000.0 * pc.samples_per_frame / 24000.0 / fms, 1),
+                  "mode": "eager"}
+        if not args.no_cpu_baseline:
+            import oracle
+            nf = 4
+            t0 = time.perf_counter()
+            oracle.decode_frames(pconv["latents"][:nf], pconv, pc.transformer, ptr,
+                                 wl.seanet_layers(pc.seanet), psw, pc.up_stride)
+            pocket["cpu_oracle_ms_per_frame"] = round(1e3 * (time.perf_counter() - t0) / nf, 2)
+        print(f"{pc.name}: {fms * 1e3:.1f} us/frame", file=sys.stderr, flush=True)
+        fr.close()
+
     configs = None
     if not args.no_configs and args.config == 4:
         configs = bench_configs((1, 2, 3, 5), dl, df, stream,
@@ -546,7 +585,7 @@ def main():
         "bytes_per_step": int(bytes_avg),
         "roofline": roofline, "fixed_positions": fixed, "eager_kernels": kernels,
         "prefill": prefill, "variant": variant,
-        "rvq": rvq, "seanet": seanet, "configs": configs,
+        "rvq": rvq, "seanet": seanet, "pocket_frame": pocket, "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -317,6 +317,14 @@ int sdec_conv_step(sdec_conv* c, const float* x, uint32_t t_in, float* y, uint32
 /* Release the handle's buffers (synchronizes the device first).  NULL is accepted. */
 void sdec_conv_destroy(sdec_conv* c);
 
+/* Layout change between the convolutions' channel-major buffers and the transformer's time-major
+ * rows ([pocket] PocketCodecGpu::new: a channel-major to time-major pass before the codec
+ * transformer and the reverse pass after it).  x is device [rows][cols] float32, y device
+ * [cols][rows]: y[c][r] = x[r][c].  The two buffers must not overlap.  Asynchronous on `stream`.
+ * Errors (nothing is enqueued): SDEC_E_ARG for a null pointer, rows or cols == 0, cols above
+ * 2096640, or overlapping buffers; SDEC_E_HIP for a failed launch. */
+int sdec_transpose(const float* x, uint32_t rows, uint32_t cols, float* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

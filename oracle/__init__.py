@@ -13,3 +13,4 @@ from .rvq import OracleRVQ, emb_sum, nearest, sq_distances  # noqa: F401,E402
 from .conv import (  # noqa: F401,E402
     causal_conv1d, conv_transpose1d_full, elu, streamed_conv_transpose1d,
 )
+from .pocket import decode_frames, seanet_decode  # noqa: F401,E402

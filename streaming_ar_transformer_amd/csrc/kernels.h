@@ -230,8 +230,9 @@ struct RvqEmbArgs {
   float* acc;                  // [frames][2][vq]: first-group sum, rest-group sum
   uint32_t nq, bins, vq;
 };
-hipError_t launch_rvq_transpose(const float* src, float* dst, uint32_t levels, uint32_t bins,
-                                uint32_t vq, hipStream_t s);
+// [levels][bins][vq] -> [levels][vq][bins] (rvq.hip).
+hipError_t launch_transpose(const float* src, float* dst, uint32_t levels, uint32_t bins,
+                            uint32_t vq, hipStream_t s);
 hipError_t launch_rvq_level(const RvqLevelArgs& a, uint32_t frames, hipStream_t s);
 hipError_t launch_rvq_final(const RvqLevelArgs& a, uint32_t frames, hipStream_t s);
 hipError_t launch_rvq_emb_sum(const RvqEmbArgs& a, uint32_t frames, hipStream_t s);

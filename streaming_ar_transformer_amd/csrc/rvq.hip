@@ -36,9 +36,11 @@ __device__ __forceinline__ void rvq_wave_argmin(float& d, uint32_t& i) {
   }
 }
 
-// [levels][bins][vq] -> [levels][vq][bins], 32 x 32 tiles through LDS.
-__global__ __launch_bounds__(256) void k_rvq_transpose(const float* src, float* dst, uint32_t bins,
-                                                       uint32_t vq) {
+// [levels][bins][vq] -> [levels][vq][bins], 32 x 32 tiles through LDS (the 33-float rows keep
+// the column reads free of bank conflicts).  Also the codec frame's channel-major <-> time-major
+// layout change (one level).
+__global__ __launch_bounds__(256) void k_transpose(const float* src, float* dst, uint32_t bins,
+                                                   uint32_t vq) {
   __shared__ float tile[32][33];
   const uint32_t l = blockIdx.z;
   const uint32_t b0 = blockIdx.x * 32, c0 = blockIdx.y * 32;
@@ -152,9 +154,9 @@ __global__ __launch_bounds__(256) void k_rvq_emb_sum(RvqEmbArgs a) {
 
 }  // namespace
 
-hipError_t launch_rvq_transpose(const float* src, float* dst, uint32_t levels, uint32_t bins,
-                                uint32_t vq, hipStream_t s) {
-  hipLaunchKernelGGL(k_rvq_transpose, dim3((bins + 31) / 32, (vq + 31) / 32, levels), dim3(32, 8),
+hipError_t launch_transpose(const float* src, float* dst, uint32_t levels, uint32_t bins,
+                            uint32_t vq, hipStream_t s) {
+  hipLaunchKernelGGL(k_transpose, dim3((bins + 31) / 32, (vq + 31) / 32, levels), dim3(32, 8),
                      0, s, src, dst, bins, vq);
   return hipGetLastError();
 }

@@ -1135,9 +1135,9 @@ int sdec_rvq_create(const sdec_rvq_config* cfg, const sdec_rvq_weights* w, sdec_
     delete q;
     return A.code;
   }
-  hipError_t e = launch_rvq_transpose(w->cb_first, q->cbT, 1, c.bins, c.vq, nullptr);
+  hipError_t e = launch_transpose(w->cb_first, q->cbT, 1, c.bins, c.vq, nullptr);
   if (e == hipSuccess)
-    e = launch_rvq_transpose(w->cb_rest, q->cbT + level_cb, c.nq - 1, c.bins, c.vq, nullptr);
+    e = launch_transpose(w->cb_rest, q->cbT + level_cb, c.nq - 1, c.bins, c.vq, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     rvq_free(q);
@@ -1315,6 +1315,17 @@ int sdec_conv_step(sdec_conv* h, const float* x, uint32_t t_in, float* y, uint32
   }
   h->cur ^= 1;
   h->started = true;
+  return SDEC_OK;
+}
+
+int sdec_transpose(const float* x, uint32_t rows, uint32_t cols, float* y, void* stream) {
+  if (!x || !y) return fail(SDEC_E_ARG, "x and y must be device pointers");
+  if (rows == 0 || cols == 0) return fail(SDEC_E_ARG, "rows=%u cols=%u must be nonzero", rows, cols);
+  if ((cols + 31u) / 32u > 65535u) return fail(SDEC_E_ARG, "cols=%u exceeds the grid's limit", cols);
+  const uintptr_t bytes = static_cast<uintptr_t>(rows) * cols * sizeof(float);
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(y);
+  if (xa < ya + bytes && ya < xa + bytes) return fail(SDEC_E_ARG, "x and y overlap");
+  HIP_TRY(launch_transpose(x, y, 1, rows, cols, static_cast<hipStream_t>(stream)));
   return SDEC_OK;
 }
 

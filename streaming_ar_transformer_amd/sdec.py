@@ -26,7 +26,8 @@ EXPORTS = ["sdec_create", "sdec_step", "sdec_reset", "sdec_destroy", "sdec_last_
            "sdec_kv_view", "sdec_set_next_position", "sdec_tap_view", "sdec_step_profile",
            "sdec_gemv", "sdec_ring_attention", "sdec_ring_attention_static", "sdec_status",
            "sdec_prefill", "sdec_rvq_create", "sdec_rvq_encode", "sdec_rvq_quantise", "sdec_rvq_decode",
-           "sdec_rvq_destroy", "sdec_conv_create", "sdec_conv_step", "sdec_conv_destroy"]
+           "sdec_rvq_destroy", "sdec_conv_create", "sdec_conv_step", "sdec_conv_destroy",
+           "sdec_transpose"]
 
 
 class SdecError(RuntimeError):
@@ -119,6 +120,7 @@ def lib():
             "sdec_conv_create": (i32, [ctypes.POINTER(ConvConfig), vp, vp, ctypes.POINTER(vp)]),
             "sdec_conv_step": (i32, [vp, vp, u32, vp, u32, vp]),
             "sdec_conv_destroy": (None, [vp]),
+            "sdec_transpose": (i32, [vp, u32, u32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -358,6 +360,15 @@ class RVQ:
             self.close()
         except Exception:
             pass
+
+
+def transpose(x, y, stream=None):
+    """``y = x.T`` for a device ``[rows, cols]`` float32 tensor into a ``[cols, rows]`` one
+    (``sdec_transpose``)."""
+    rows, cols = x.shape
+    assert tuple(y.shape) == (cols, rows), "y must be [cols, rows]"
+    _check(lib().sdec_transpose(_ptr(x), rows, cols, _ptr(y), _stream(stream)))
+    return y
 
 
 class StreamConv:

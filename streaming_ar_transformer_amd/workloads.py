@@ -350,3 +350,68 @@ def make_seanet(cfg: SEANetConfig):
     x = _normal([cfg.seed, 5, 999, 0], (cfg.frames, cfg.channels, cfg.frame_cols), 1.0)
     return w, x
 
+
+
+@dataclasses.dataclass(frozen=True)
+class PocketFrameConfig:
+    """A Pocket-style codec decode frame ([pocket] module doc, the decode graph, and
+    ``PocketCodecGpu::new``): one latent column ``[latent_dim, 1]`` -> 1x1 conv to ``dim``
+    channels -> channel-wise transposed conv (kernel ``up_kernel``, stride ``up_stride``) giving
+    ``up_stride`` positions -> time-major -> the codec transformer over those positions (window
+    ``context``, ring ``context + up_stride``) -> channel-major -> SEANet.  The transformer's
+    rope/ring position advances by ``up_stride`` per frame."""
+
+    name: str
+    seed: int
+    latent_dim: int = 32
+    dim: int = 512
+    heads: int = 8
+    ffn: int = 2048
+    tr_layers: int = 2
+    up_kernel: int = 32
+    up_stride: int = 16
+    context: int = 250
+    frames: int = 20
+    seanet: SEANetConfig = SEANET_CONFIGS[1]
+    tr_weight_std: float = 0.02
+    tr_layer_scale: float = 0.01
+
+    def replace(self, **kw) -> "PocketFrameConfig":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def transformer(self) -> StepConfig:
+        """The codec-family stack of the frame (LayerNorm eps 1e-5, interleaved rope, GELU FFN,
+        LayerScale, no final norm), its weights seeded with ``cfg_id = seed``."""
+        return _codec(f"{self.name}_tr", self.seed, self.tr_layers, self.context + self.up_stride,
+                      self.context, self.frames * self.up_stride).replace(
+            d_model=self.dim, n_q_heads=self.heads, n_kv_heads=self.heads,
+            head_dim=self.dim // self.heads, d_ff=self.ffn, weight_std=self.tr_weight_std,
+            layer_scale_init=self.tr_layer_scale)
+
+    @property
+    def samples_per_frame(self) -> int:
+        return self.up_stride * int(np.prod(self.seanet.ratios))
+
+
+POCKET_CONFIGS = {1: PocketFrameConfig("pocket_frame_l32_d512_tr2_r654", 21)}
+
+
+def make_pocket_frame(cfg: PocketFrameConfig):
+    """The frame's parameters and inputs.  Returns ``(conv, tr_layers, seanet_w)``: ``conv`` holds
+    ``quant.w`` ``[dim, latent_dim, 1]`` (std 1/sqrt(latent_dim)), ``up.w`` ``[dim, 1, up_kernel]``
+    (std sqrt(up_stride / up_kernel): each output column sums up_kernel / up_stride taps), their
+    biases N(0, 0.1) and the latents ``[frames, latent_dim, 1]`` N(0, 1), seeded
+    ``[seed, 6, part]``; ``tr_layers`` come from ``make_weights(cfg.transformer)`` and
+    ``seanet_w`` from ``make_seanet(cfg.seanet)``."""
+    s, d = cfg.seed, cfg.dim
+    conv = {
+        "quant.w": _normal([s, 6, 0], (d, cfg.latent_dim, 1), 1.0 / np.sqrt(cfg.latent_dim)),
+        "quant.b": _normal([s, 6, 1], (d,), 0.1),
+        "up.w": _normal([s, 6, 2], (d, 1, cfg.up_kernel), np.sqrt(cfg.up_stride / cfg.up_kernel)),
+        "up.b": _normal([s, 6, 3], (d,), 0.1),
+        "latents": _normal([s, 6, 4], (cfg.frames, cfg.latent_dim, 1), 1.0),
+    }
+    tr_layers, _ = make_weights(cfg.transformer)
+    seanet_w, _ = make_seanet(cfg.seanet)
+    return conv, tr_layers, seanet_w

@@ -105,3 +105,114 @@ class BruteDecoder:
             x = rms(x, self.final["norm_w"], cfg.norm_eps) if rmsn else \
                 lnorm(x, self.final["norm_w"], self.final["norm_b"], cfg.norm_eps)
         return x
+
+
+def _elu(v):
+    return v if v > 0 else math.exp(v) - 1.0
+
+
+class BruteConv:
+    """A causal conv fed one frame at a time: signals are lists of time columns (each a list of
+    channel values); the last ``K - stride`` input columns carry over to the next frame."""
+
+    def __init__(self, w, b, stride, pre_elu=False, groups=1):
+        self.w, self.b = w.tolist(), b.tolist()
+        self.s, self.elu, self.groups = stride, pre_elu, groups
+        c_out, ipg, self.K = w.shape
+        self.c_in = ipg * groups
+        self.prev = [[0.0] * self.c_in for _ in range(self.K - stride)]
+
+    def frame(self, cols):
+        buf = self.prev + [list(c) for c in cols]
+        c_out, ipg = len(self.w), len(self.w[0])
+        opg = c_out // self.groups
+        out = []
+        for t in range(len(cols) // self.s):
+            y = []
+            for o in range(c_out):
+                g = o // opg
+                terms = [self.w[o][i][k] * (_elu(buf[t * self.s + k][g * ipg + i]) if self.elu
+                                            else buf[t * self.s + k][g * ipg + i])
+                         for i in range(ipg) for k in range(self.K)]
+                y.append(self.b[o] + math.fsum(terms))
+            out.append(y)
+        self.prev = buf[len(buf) - (self.K - self.s):] if self.K > self.s else []
+        return out
+
+
+class BruteConvTr:
+    """A transposed conv fed one frame at a time: input column t scatters tap k onto output
+    column t * stride + k; the last ``K - stride`` partial sums (no bias yet) wait for the next
+    frame, and a column gets its bias when it is emitted."""
+
+    def __init__(self, w, b, stride, pre_elu=False, groups=1):
+        self.w, self.b = w.tolist(), b.tolist()
+        self.s, self.elu, self.groups = stride, pre_elu, groups
+        c_in, opg, self.K = w.shape
+        self.c_out = opg * groups
+        self.pending = [[0.0] * self.c_out for _ in range(self.K - stride)]
+
+    def frame(self, cols):
+        n = len(cols) * self.s
+        acc = [list(c) for c in self.pending] + [[0.0] * self.c_out
+                                                 for _ in range(n + self.K - self.s - len(self.pending))]
+        c_in, opg = len(self.w), len(self.w[0])
+        ipg = c_in // self.groups
+        for t, col in enumerate(cols):
+            for i in range(c_in):
+                v = _elu(col[i]) if self.elu else col[i]
+                g = i // ipg
+                for oo in range(opg):
+                    for k in range(self.K):
+                        acc[t * self.s + k][g * opg + oo] += self.w[i][oo][k] * v
+        out = [[acc[t][o] + self.b[o] for o in range(self.c_out)] for t in range(n)]
+        self.pending = acc[n:]
+        return out
+
+
+class BruteSEANet:
+    """The SEANet-style decoder of ``seanet_layers`` streamed frame by frame from the brute
+    pieces above (the first conv reads its input as is, every other layer through ELU)."""
+
+    def __init__(self, layers, w):
+        self.stages = []
+        for i, (name, kind, _, stride) in enumerate(layers):
+            W, B = w[name + ".w"], w[name + ".b"]
+            conv = (BruteConvTr(W, B, stride, pre_elu=True) if kind == "convtr"
+                    else BruteConv(W, B, stride, pre_elu=(i != 0)))
+            self.stages.append((kind, conv))
+
+    def frame(self, cols):
+        h = cols
+        block_in = None
+        for kind, conv in self.stages:
+            if kind == "res0":
+                block_in = h
+            out = conv.frame(h)
+            if kind == "res1":
+                out = [[a + c for a, c in zip(ra, rc)] for ra, rc in zip(block_in, out)]
+            h = out
+        return h
+
+
+class BrutePocketFrame:
+    """The Pocket-style codec frame streamed one latent at a time: 1x1 conv, channel-wise
+    transposed conv, the transformer one position at a time (``BruteDecoder``, positions
+    ``frame * stride + r``), then the SEANet stack; returns each frame's stages."""
+
+    def __init__(self, cfg, conv, tr_layers, seanet_layers, seanet_w):
+        self.quant = BruteConv(conv["quant.w"], conv["quant.b"], 1)
+        self.up = BruteConvTr(conv["up.w"], conv["up.b"], cfg.up_stride, groups=cfg.dim)
+        self.tr = BruteDecoder(cfg.transformer, tr_layers, {}, cfg.context)
+        self.seanet = BruteSEANet(seanet_layers, seanet_w)
+        self.pos = 0
+
+    def frame(self, latent):
+        z = self.quant.frame([list(latent[:, 0])])
+        u = self.up.frame(z)
+        tr = []
+        for col in u:
+            tr.append(self.tr.step(col, self.pos))
+            self.pos += 1
+        pcm = self.seanet.frame(tr)
+        return {"quant": z, "up": u, "tr": tr, "pcm": pcm}

@@ -163,6 +163,16 @@ def test_conv_rejects_bad_config():
     L.sdec_conv_destroy(None)
 
 
+def test_transpose_checks_on_the_host():
+    L = sdec.lib()
+    assert L.sdec_transpose(None, 4, 4, 4096, None) == sdec.E_ARG
+    assert L.sdec_transpose(4096, 0, 4, 8192, None) == sdec.E_ARG
+    # 16 x 512 floats from 0x10000 reach past 0x18000
+    assert L.sdec_transpose(0x10000, 16, 512, 0x18000 - 256, None) == sdec.E_ARG
+    assert "overlap" in L.sdec_last_error().decode()
+    assert L.sdec_transpose(0x10000, 1, 1 << 22, 0x10000000, None) == sdec.E_ARG
+
+
 def test_one_shot_entry_points_reject_bad_arguments():
     L = sdec.lib()
     assert L.sdec_gemv(None, 16, 32, 4, 4, 1, None) == sdec.E_ARG

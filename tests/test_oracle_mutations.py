@@ -68,6 +68,18 @@ MUTATIONS = [
      "r = (r + self.cb_rest[l, code]).astype(F32)", "residual update sign"),
     ("oracle.rvq", "sq_distances", "(cb[:, c] - r[c])", "(cb[:, c] - r[0])", "distance index"),
     ("oracle.rvq", "emb_sum", "cbs[l, int(code)]", "cbs[0, int(code)]", "code vector of level 0"),
+    ("oracle.pocket", "decode_frames", "rows = np.ascontiguousarray(u.T)",
+     "rows = np.ascontiguousarray(u.reshape(-1, u.shape[0]))",
+     "channel-major to time-major as a reshape"),
+    ("oracle.pocket", "decode_frames", "tr = np.ascontiguousarray(out.T)",
+     "tr = np.ascontiguousarray(out.reshape(out.shape[1], -1))",
+     "time-major back to channel-major as a reshape"),
+    ("oracle.pocket", "decode_frames", 'conv["up.b"], stride, groups=dim)',
+     'conv["up.b"], stride, pre_elu=True, groups=dim)', "ELU before the upsample"),
+    ("oracle.pocket", "seanet_decode", "pre_elu=(i != 0)", "pre_elu=True",
+     "ELU on the first conv's input"),
+    ("oracle.pocket", "seanet_decode", "h = (block_in + causal_conv1d(h, W, B, stride, pre_elu=True))",
+     "h = (causal_conv1d(h, W, B, stride, pre_elu=True))", "residual block without its skip"),
 ]
 
 

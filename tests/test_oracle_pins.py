@@ -707,3 +707,36 @@ def test_rvq_first_and_rest_projections_are_not_interchangeable():
     y = q.decode(codes)
     want = np.concatenate([2 * cb_first[0, c0], s[qperm]]).astype(F32)
     np.testing.assert_array_equal(y, want)
+
+
+# ---- the Pocket-style codec frame ([pocket] module doc decode graph; PocketCodecGpu) ----
+
+def _tiny_pocket():
+    from streaming_ar_transformer_amd import workloads as wl
+    sc = wl.SEANetConfig("seanet_tiny", 31, channels=8, ratios=(2,), frame_cols=4)
+    # weights large enough that the transformer moves the signal by O(1)
+    return wl.PocketFrameConfig("pocket_tiny", 32, latent_dim=3, dim=8, heads=2, ffn=16,
+                                tr_layers=2, up_kernel=8, up_stride=4, context=10, frames=6,
+                                seanet=sc, tr_weight_std=0.4, tr_layer_scale=0.7)
+
+
+def test_pocket_frame_offline_equals_brute_stream():
+    # The oracle decodes all frames offline (whole-sequence convs, the ring-buffer stack one
+    # position at a time); the brute force streams one latent at a time with explicit carries,
+    # a history-list transformer and scalar sums.  6 frames of 4 positions pass the 14-slot ring.
+    from streaming_ar_transformer_amd import workloads as wl
+    from tests.brute import BrutePocketFrame
+    cfg = _tiny_pocket()
+    conv, trl, sw = wl.make_pocket_frame(cfg)
+    layers = wl.seanet_layers(cfg.seanet)
+    got = oracle.decode_frames(conv["latents"], conv, cfg.transformer, trl, layers, sw,
+                               cfg.up_stride)
+    bru = BrutePocketFrame(cfg, conv, trl, layers, sw)
+    frames = [bru.frame(conv["latents"][f]) for f in range(cfg.frames)]
+    want = {k: np.array([c for fr in frames for c in fr[k]], np.float64).T
+            for k in ("quant", "up", "tr", "pcm")}
+    assert got["pcm"].shape == (1, cfg.frames * cfg.samples_per_frame) == want["pcm"].shape
+    for k in ("quant", "up", "tr", "pcm"):
+        np.testing.assert_allclose(got[k], want[k], rtol=2e-5, atol=2e-5, err_msg=k)
+    # the transformer does move the signal (a dropped stack would not pass unnoticed)
+    assert np.max(np.abs(want["tr"] - want["up"])) > 0.1
