@@ -65,11 +65,12 @@ __global__ __launch_bounds__(64) void k_sconvtr(SConvTrArgs a) {
   const uint32_t ipg = a.c_in / a.groups, opg = a.c_out / a.groups;
   const uint32_t g = oc / opg, oo = oc % opg;
   float acc = a.b[oc];
-  for (uint32_t k = 0; k < a.k && k <= i; ++k) {
-    const uint32_t d = i - k;
-    if (d % a.stride != 0) continue;
-    const uint32_t ti = d / a.stride;
-    if (ti >= a.t_in) continue;
+  // the input columns whose taps reach column i, tap k = i - ti * stride ascending (ti from the
+  // largest with ti * stride <= i down), one division per thread
+  const uint32_t ti_hi = min(i / a.stride, a.t_in - 1);
+  for (int32_t ti = static_cast<int32_t>(ti_hi); ti >= 0; --ti) {
+    const uint32_t k = i - static_cast<uint32_t>(ti) * a.stride;
+    if (k >= a.k) break;
     for (uint32_t ii = 0; ii < ipg; ++ii) {
       const uint32_t ic = g * ipg + ii;
       float v = a.x[static_cast<size_t>(ic) * a.t_in + ti];

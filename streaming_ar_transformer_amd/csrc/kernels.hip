@@ -1424,7 +1424,90 @@ __global__ __launch_bounds__(kWgThreads) void k_qkv_begin_rx(QkvBeginArgs a) {
 // pos .. pos+m-1 of one stream.  Every row's slot is stamped before any row's legal list is formed;
 // with pos + m <= R or R >= window + m - 1 no stamp removes a position an earlier row of the
 // block may attend, so row r's list is exactly the one a single step at pos + r would form.
-// One workgroup.
+//
+// Workgroup r < m forms row r's list; workgroup m writes every row's rope table and the state.
+// A row's workgroup reads the ring as it stands after the whole block's stamps without waiting for
+// them: a slot of the block holds pos + (its distance from the block's first slot), any other
+// slot is empty after `first` and otherwise unchanged, so the one value the stamps would change
+// is computed, not read.  The list is the lead slot then the other legal slots in ascending
+// order, as the single-workgroup form below builds it.
+__global__ __launch_bounds__(kWgThreads) void k_begin_rows_wg(BeginArgs a) {
+  __shared__ BeginSmem sm;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const uint32_t r = blockIdx.x, rows = a.m, R = a.ring;
+  const uint32_t base = a.pos % R;
+  if (r == rows) {
+    const uint32_t half = a.head_dim >> 1;
+    for (uint32_t i = tid; i < rows * half; i += kWgThreads) {
+      const uint32_t rr = i / half, j = i % half;
+      const double inv_freq = pow(a.theta, -2.0 * static_cast<double>(j) /
+                                               static_cast<double>(a.head_dim));
+      const double ang = static_cast<double>(a.pos + rr) * inv_freq;
+      a.cs[static_cast<size_t>(rr) * a.head_dim + j] = static_cast<float>(cos(ang));
+      a.cs[static_cast<size_t>(rr) * a.head_dim + half + j] = static_cast<float>(sin(ang));
+    }
+    if (tid == 0 && a.st != nullptr) {
+      a.st->pos = a.pos + rows - 1;
+      a.st->slot = (base + rows - 1) % R;
+    }
+    return;
+  }
+  const uint32_t pos_r = a.pos + r, slot_r = (base + r) % R;
+  uint32_t* P = a.pos_rings;
+  // the ring after the block's stamps
+  auto stamped = [&](uint32_t j, uint32_t old) {
+    const uint32_t k = j >= base ? j - base : j + R - base;
+    return k < rows ? a.pos + k : (a.first ? kInvalidPos : old);
+  };
+  const uint32_t nch = (R + kWave - 1) / kWave;
+  const uint32_t cpw = (nch + kWgThreads / kWave - 1) / (kWgThreads / kWave);
+  const uint32_t c0 = min(static_cast<uint32_t>(wave) * cpw, nch), c1 = min(c0 + cpw, nch);
+  uint32_t cnt = 0;
+  for (uint32_t cb = c0; cb < c1; cb += 8) {
+    uint32_t pv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pv[j] = a.first ? kInvalidPos : P[min((cb + j) * kWave + lane, R - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t c = cb + j, sl = c * kWave + lane;
+      const uint32_t p = stamped(min(sl, R - 1), pv[j]);
+      const bool legal = c < c1 && sl < R && sl != slot_r && p != kInvalidPos && p <= pos_r &&
+                         pos_r - p < a.window;
+      const unsigned long long m = __ballot(legal);
+      if (c < c1 && lane == 0) sm.masks[c] = m;
+      cnt += c < c1 ? static_cast<uint32_t>(__popcll(m)) : 0u;
+    }
+  }
+  const float4* src = reinterpret_cast<const float4*>(a.x_in + static_cast<size_t>(r) * a.d);
+  float4* dst = reinterpret_cast<float4*>(a.xres + static_cast<size_t>(r) * a.d);
+  for (uint32_t i = tid; i < (a.d >> 2); i += kWgThreads) dst[i] = src[i];
+  if (a.first) {
+    for (uint32_t j = r * kWgThreads + tid; j < R; j += rows * kWgThreads) P[j] = stamped(j, 0u);
+  } else if (tid == 0) {
+    P[slot_r] = pos_r;
+  }
+  if (lane == 0) sm.wcount[wave] = cnt;
+  __syncthreads();
+  uint32_t o = 1, total = 1;
+  for (int w = 0; w < kWgThreads / kWave; ++w) {
+    o += w < wave ? sm.wcount[w] : 0u;
+    total += sm.wcount[w];
+  }
+  uint32_t* out = a.legal + static_cast<size_t>(r) * R;
+  const unsigned long long below = lane ? (~0ull >> (kWave - lane)) : 0ull;
+  for (uint32_t c = c0; c < c1; ++c) {
+    const unsigned long long m = sm.masks[c];
+    if ((m >> lane) & 1ull) out[o + __popcll(m & below)] = c * kWave + lane;
+    o += static_cast<uint32_t>(__popcll(m));
+  }
+  if (tid == 0) {
+    out[0] = slot_r;
+    a.n_legal[r] = total;
+  }
+}
+
+// The same in one workgroup, rows one after another (rings of more than kBeginMaxChunks * 64
+// slots).
 __global__ __launch_bounds__(kWgThreads) void k_begin_rows(BeginArgs a) {
   __shared__ uint32_t scan[kWgThreads];
   const int tid = threadIdx.x;
@@ -2061,6 +2144,9 @@ hipError_t launch_begin(const BeginArgs& a, hipStream_t s) {
 hipError_t launch_begin_rows(const BeginArgs& a, hipStream_t s) {
   BeginArgs args = a;
   void* params[] = {&args};
+  if ((a.ring + kWave - 1) / kWave <= kBeginMaxChunks)
+    return launch_timed(reinterpret_cast<const void*>(&k_begin_rows_wg), dim3(a.m + 1),
+                        dim3(kWgThreads), params, 0, s);
   return launch_timed(reinterpret_cast<const void*>(&k_begin_rows), dim3(1), dim3(kWgThreads), params, 0, s);
 }
 
