@@ -93,6 +93,8 @@ struct sdec_handle {
   // no final norm, one stream: the last down projection writes the caller's rows itself (no end
   // launch; tuning override SDEC_END_IN_DOWN)
   bool end_in_down = false;
+  // the same for prefill blocks (any block width)
+  bool prefill_end_in_down = false;
 
   hipStream_t cap_stream = nullptr;
   hipGraphExec_t exec[2] = {nullptr, nullptr};  // one recorded graph per StepForm
@@ -520,8 +522,13 @@ int enqueue_prefill(sdec_handle* h, float* x, uint32_t pos, uint32_t t, uint32_t
     dn.seg_end[0] = dn.seg_end[1] = dn.seg_end[2] = c.d_model;
     dn.n_rows = c.d_model; dn.k = c.d_ff; dn.m = t; dn.x = h->act; dn.x_stride = c.d_ff;
     dn.res = h->xres; dn.res_stride = c.d_model; dn.ls = c.layer_scale ? w.ls2 : nullptr;
+    if (h->prefill_end_in_down && l + 1 == c.n_layers) {  // no final norm: the caller's rows
+      dn.res_in = h->xres;
+      dn.res = x;
+    }
     LAUNCH(hk, s, SDEC_K_FFN_DOWN, launch_gemv(dn, p_down, s));
   }
+  if (h->prefill_end_in_down) return SDEC_OK;
   EndArgs e{};
   e.xres = h->xres; e.x_out = x; e.m = t; e.d = c.d_model;
   e.norm = c.final_norm ? (c.norm == SDEC_NORM_RMS ? PRO_RMS : PRO_LN) : -1;
@@ -733,6 +740,7 @@ int sdec_create(const sdec_config* cfg, const sdec_layer_weights* layers,
     const char* ed = std::getenv("SDEC_END_IN_DOWN");
     h->end_in_down = c.m == 1 && !c.final_norm && !ld.stream && ld.ks == 0 &&
                      !(ed != nullptr && ed[0] == '0');
+    h->prefill_end_in_down = !c.final_norm && !(ed != nullptr && ed[0] == '0');
   }
   {
     const char* bq = std::getenv("SDEC_BEGIN_IN_QKV");  // tuning override: "0" = separate begin

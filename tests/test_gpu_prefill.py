@@ -177,3 +177,26 @@ def test_prefill_argument_errors(sd):
         tdec.prefill(torch.zeros((8, tcfg.d_model), device="cuda"), tcfg.ring - 4)
     assert e.value.code == sd.E_CAPACITY
     tdec.close()
+
+
+def test_codec_prefill_end_in_down_equals_end_launch(sd, monkeypatch):
+    # A stack without a final norm: the last down projection writing the caller's rows (the
+    # default) and a separate end launch give bit-identical blocks, ring wraps included.
+    cfg = wl.CONFIGS[2]
+    ring = cfg.window + 7
+    monkeypatch.setenv("SDEC_END_IN_DOWN", "0")
+    sep = make(sd, cfg, ring=ring, max_prefill=8)
+    monkeypatch.delenv("SDEC_END_IN_DOWN")
+    fused = make(sd, cfg, ring=ring, max_prefill=8)
+    xs = wl.make_inputs(cfg, 296)
+    p = 0
+    for t in [8, 3, 8, 5] * 10:
+        a = torch.from_numpy(np.ascontiguousarray(xs[p:p + t, 0])).cuda()
+        b = a.clone()
+        sep.prefill(a, p, first=(p == 0))
+        fused.prefill(b, p, first=(p == 0))
+        torch.testing.assert_close(a, b, rtol=0, atol=0)
+        p += t
+    sep.close()
+    fused.close()
+    log(f"{cfg.name}: {p} positions in blocks, fused and separate end bit-identical")
