@@ -1779,6 +1779,11 @@ template <int M>
 GemvKernel gemv_ksm(const GemvLaunch& l) {
   if (l.waves_per_wg == 4 && l.ks == 2 && l.rows_per_wave == 4) return gemv_ksm_kind<M, 4, 2, 4>(l);
   if (l.waves_per_wg == 8 && l.ks == 3 && l.rows_per_wave == 2) return gemv_ksm_kind<M, 8, 3, 2>(l);
+  // k = 512 and 1024 (the codec and FlowLM widths): one float4 per lane and row in each slice
+  if (l.waves_per_wg == 2 && l.ks == 1 && l.rows_per_wave == 4) return gemv_ksm_kind<M, 2, 1, 4>(l);
+  if (l.waves_per_wg == 2 && l.ks == 1 && l.rows_per_wave == 2) return gemv_ksm_kind<M, 2, 1, 2>(l);
+  if (l.waves_per_wg == 4 && l.ks == 1 && l.rows_per_wave == 4) return gemv_ksm_kind<M, 4, 1, 4>(l);
+  if (l.waves_per_wg == 4 && l.ks == 1 && l.rows_per_wave == 2) return gemv_ksm_kind<M, 4, 1, 2>(l);
   if constexpr (M == 8) {  // taller tiles: every tile of the launch in flight in one round
     if (l.waves_per_wg == 4 && l.ks == 2 && l.rows_per_wave == 8) return gemv_ksm_kind<M, 4, 2, 8>(l);
     if (l.waves_per_wg == 8 && l.ks == 3 && l.rows_per_wave == 4) return gemv_ksm_kind<M, 8, 3, 4>(l);
@@ -1969,13 +1974,16 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
     if (l.grid < 1) l.grid = 1;
     return l;
   }
-  if (M >= 2 && (k == 2048 || k == 6144) && prologue != PRO_ATTN &&
+  const bool narrow_k = (k == 512 || k == 1024) && env_int("SDEC_KSM_NARROW", 1) != 0;
+  if (M >= 2 && (k == 2048 || k == 6144 || narrow_k) && prologue != PRO_ATTN &&
       env_int("SDEC_GEMV_SPLITK", 1) != 0) {
     // the NW waves of a workgroup take the NW slices of k; all M input rows of a slice in registers
-    l.ks = k == 2048 ? 2 : 3;
+    l.ks = k == 2048 ? 2 : k == 6144 ? 3 : 1;
     l.kb = 0;
-    l.waves_per_wg = k == 2048 ? 4 : 8;
-    l.rows_per_wave = k == 2048 ? 4 : 2;
+    l.waves_per_wg = k == 2048 ? 4 : k == 6144 ? 8 : static_cast<int>(k / 256);
+    l.rows_per_wave = k == 2048 ? 4 : k == 6144 ? 2 : 4;
+    // narrow rows: 4-row tiles while they give every CU a workgroup, else 2-row tiles
+    if (narrow_k && n_rows / 4 < static_cast<uint32_t>(cus)) l.rows_per_wave = 2;
     if (M == 8) {
       // taller tiles where measured faster at 8 streams: the q/k/v projection (8 rows per tile,
       // 10.7 vs 12.8 us) and the down projection (4 rows, 12.6 vs 13.1 us); the o and gate/up
