@@ -183,6 +183,16 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, u
   const uint32_t oc = oc0 + ocl, ot = col0 + otl;
   const bool live = oc < a.c_out && ot < t_out;
   float acc = live && !split ? a.b[oc] : 0.f;
+  if (blockIdx.z == 0 && a.pad > 0) {
+    // the next frame's prefix (the last pad columns of this frame's padded stream), spread over
+    // the workgroups of the first split: it depends on the inputs only, so it needs no launch of
+    // its own
+    const uint32_t n_carry = a.c_in * a.pad;
+    const uint32_t step = gridDim.x * gridDim.y * kConvTileThreads;
+    for (uint32_t e = (blockIdx.y * gridDim.x + blockIdx.x) * kConvTileThreads + tid; e < n_carry;
+         e += step)
+      a.prefix_out[e] = sconv_sample(a, e / a.pad, a.t_in + e % a.pad);
+  }
   for (uint32_t ic0 = ic_begin; ic0 < ic_end; ic0 += icb) {
     const uint32_t nb = min(icb, ic_end - ic0);
     __syncthreads();  // the previous block is consumed
@@ -439,6 +449,7 @@ hipError_t launch_sconv(const SConvArgs& a, hipStream_t s) {
     if (le != hipSuccess) return le;
     if (splits > 1 && args.counters == nullptr)
       hipLaunchKernelGGL(k_sconv_sum, dim3((a.c_out * t_out + 255) / 256), dim3(256), 0, s, a, splits);
+    return hipGetLastError();  // the tiled kernel also writes the next prefix
   } else {
     hipLaunchKernelGGL(k_sconv, dim3((t_out + 63) / 64, a.c_out), dim3(64), 0, s, a);
   }
