@@ -199,7 +199,7 @@ __device__ __forceinline__ void norm_rope_pair(float& va, float& vb, int j, cons
   const bool act = j < HALF;
   if (gnorm != nullptr) {
     const float ss = wave_sum(act ? va * va + vb * vb : 0.f);
-    const float inv = 1.0f / sqrtf(ss / static_cast<float>(HD) + eps);
+    const float inv = rsqrtf(ss * (1.0f / static_cast<float>(HD)) + eps);
     if (act) {
       const int ia = style == 0 ? j : 2 * j, ib = style == 0 ? j + HALF : 2 * j + 1;
       va = (va * inv) * gnorm[ia];

@@ -52,21 +52,21 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, float4* xs, uint32_t 
         const float4 t = row[c];
         ss = dot4(t, t, ss);
       }
-      inv = 1.0f / sqrtf(wave_sum(ss) / kf + a.eps);
+      inv = rsqrtf(wave_sum(ss) * (1.0f / kf) + a.eps);
     } else {
       float s = 0.f;
       for (uint32_t c = lane; c < K4; c += kWave) {
         const float4 t = row[c];
         s += (t.x + t.y) + (t.z + t.w);
       }
-      mean = wave_sum(s) / kf;
+      mean = wave_sum(s) * (1.0f / kf);
       float ss = 0.f;
       for (uint32_t c = lane; c < K4; c += kWave) {
         float4 t = row[c];
         t.x -= mean; t.y -= mean; t.z -= mean; t.w -= mean;
         ss = dot4(t, t, ss);
       }
-      inv = 1.0f / sqrtf(wave_sum(ss) / kf + a.eps);
+      inv = rsqrtf(wave_sum(ss) * (1.0f / kf) + a.eps);
     }
     for (uint32_t c = lane; c < K4; c += kWave) {
       float4 t = row[c];
@@ -317,12 +317,12 @@ __device__ __forceinline__ void gemv_rx_body(const GemvArgs& a, uint32_t blk, ui
         float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < KB; ++j) ss = dot4(xr[m][j], xr[m][j], ss);
-        inv = 1.0f / sqrtf(wave_sum(ss) / kf + a.eps);
+        inv = rsqrtf(wave_sum(ss) * (1.0f / kf) + a.eps);
       } else {
         float sm = 0.f;
 #pragma unroll
         for (int j = 0; j < KB; ++j) sm += (xr[m][j].x + xr[m][j].y) + (xr[m][j].z + xr[m][j].w);
-        mean = wave_sum(sm) / kf;
+        mean = wave_sum(sm) * (1.0f / kf);
         float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
@@ -330,7 +330,7 @@ __device__ __forceinline__ void gemv_rx_body(const GemvArgs& a, uint32_t blk, ui
           d.x -= mean; d.y -= mean; d.z -= mean; d.w -= mean;
           ss = dot4(d, d, ss);
         }
-        inv = 1.0f / sqrtf(wave_sum(ss) / kf + a.eps);
+        inv = rsqrtf(wave_sum(ss) * (1.0f / kf) + a.eps);
       }
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
@@ -887,7 +887,7 @@ __device__ __forceinline__ void gemv_rows_body(const GemvArgs& a, uint32_t blk, 
       float sm = 0.f;
 #pragma unroll
       for (int j = 0; j < KB; ++j) sm += (xr[j].x + xr[j].y) + (xr[j].z + xr[j].w);
-      mean = wave_sum(sm) / kf;
+      mean = wave_sum(sm) * (1.0f / kf);
     }
     float ss = 0.f;
 #pragma unroll
@@ -896,7 +896,7 @@ __device__ __forceinline__ void gemv_rows_body(const GemvArgs& a, uint32_t blk, 
       d.x -= mean; d.y -= mean; d.z -= mean; d.w -= mean;
       ss = dot4(d, d, ss);
     }
-    const float inv = 1.0f / sqrtf(wave_sum(ss) / kf + a.eps);
+    const float inv = rsqrtf(wave_sum(ss) * (1.0f / kf) + a.eps);
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       float4 v = xr[j];
@@ -1023,8 +1023,11 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_ksm(GemvArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 
   if (PRO != PRO_NONE) {  // per input row: statistics of the whole row from the NW slices
-    const float kf = static_cast<float>(a.k);
-    float mean[M];
+    // Each phase runs over all M rows before the next (the sums, then the cross-lane reductions,
+    // then one guarded LDS write per row), so the M independent reduction chains interleave
+    // instead of running one after another between exec-mask switches.
+    const float kf = static_cast<float>(a.k), rk = 1.0f / kf;
+    float mean[M], st[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) mean[m] = 0.f;
     if (PRO == PRO_LN) {
@@ -1033,8 +1036,13 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_ksm(GemvArgs a) {
         float sm = 0.f;
 #pragma unroll
         for (int j = 0; j < KW; ++j) sm += (xr[m][j].x + xr[m][j].y) + (xr[m][j].z + xr[m][j].w);
-        sm = wave_sum(sm);
-        if (lane == 0) stat[0][m][wave] = sm;
+        st[m] = sm;
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) st[m] = wave_sum(st[m]);
+      if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) stat[0][m][wave] = st[m];
       }
       __syncthreads();
 #pragma unroll
@@ -1042,7 +1050,7 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_ksm(GemvArgs a) {
         float tot = 0.f;
 #pragma unroll
         for (int q = 0; q < NW; ++q) tot += stat[0][m][q];
-        mean[m] = tot / kf;
+        mean[m] = tot * rk;
       }
     }
 #pragma unroll
@@ -1054,16 +1062,28 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_ksm(GemvArgs a) {
         d.x -= mean[m]; d.y -= mean[m]; d.z -= mean[m]; d.w -= mean[m];
         ss = dot4(d, d, ss);
       }
-      ss = wave_sum(ss);
-      if (lane == 0) stat[1][m][wave] = ss;
+      st[m] = ss;
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) st[m] = wave_sum(st[m]);
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) stat[1][m][wave] = st[m];
     }
     __syncthreads();
+    float invs[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       float tot = 0.f;
 #pragma unroll
       for (int q = 0; q < NW; ++q) tot += stat[1][m][q];
-      const float inv = 1.0f / sqrtf(tot / kf + a.eps);
+      // one reciprocal square root instruction (within 1 ulp of 1 / sqrt) and a product by
+      // 1 / k: 8 rows of correctly rounded divisions and square roots measured 1.5 us per launch
+      invs[m] = rsqrtf(tot * rk + a.eps);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float inv = invs[m];
 #pragma unroll
       for (int j = 0; j < KW; ++j) {
         float4 v = xr[m][j];
@@ -1206,7 +1226,7 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_ks(GemvArgs a) {
       sm = wave_sum(sm);
       if (lane == 0) stat[0][wave] = sm;
       __syncthreads();
-      mean = ((stat[0][0] + stat[0][1]) + (stat[0][2] + stat[0][3])) / kf;
+      mean = ((stat[0][0] + stat[0][1]) + (stat[0][2] + stat[0][3])) * (1.0f / kf);
     }
     float ss = 0.f;
 #pragma unroll
@@ -1218,7 +1238,7 @@ __global__ __launch_bounds__(kWgThreads) void k_gemv_ks(GemvArgs a) {
     ss = wave_sum(ss);
     if (lane == 0) stat[1][wave] = ss;
     __syncthreads();
-    const float inv = 1.0f / sqrtf(((stat[1][0] + stat[1][1]) + (stat[1][2] + stat[1][3])) / kf + a.eps);
+    const float inv = rsqrtf(((stat[1][0] + stat[1][1]) + (stat[1][2] + stat[1][3])) * (1.0f / kf) + a.eps);
 #pragma unroll
     for (int j = 0; j < KW; ++j) {
       float4 v = xr[j];
@@ -1604,7 +1624,7 @@ __global__ __launch_bounds__(kWgThreads) void k_end(EndArgs a) {
     s = wave_sum(s);
     if (lane == 0) red[0][wave] = s;
     __syncthreads();
-    const float mean = a.norm == PRO_LN ? ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / df : 0.f;
+    const float mean = a.norm == PRO_LN ? ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) * (1.0f / df) : 0.f;
     float ss = 0.f;
     for (uint32_t i = tid; i < a.d; i += blockDim.x) {
       const float v = x[i] - mean;
@@ -1613,7 +1633,7 @@ __global__ __launch_bounds__(kWgThreads) void k_end(EndArgs a) {
     ss = wave_sum(ss);
     if (lane == 0) red[1][wave] = ss;
     __syncthreads();
-    const float inv = 1.0f / sqrtf(((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / df + a.eps);
+    const float inv = rsqrtf(((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) * (1.0f / df) + a.eps);
     for (uint32_t i = tid; i < a.d; i += blockDim.x) {
       if (a.norm == PRO_LN) y[i] = ((x[i] - mean) * inv) * a.w[i] + a.b[i];
       else y[i] = (x[i] * inv) * a.w[i];
@@ -1642,7 +1662,7 @@ __global__ __launch_bounds__(kWgThreads) void k_end(EndArgs a) {
     s = wave_sum(s);
     if (lane == 0) red[0][wave] = s;
     __syncthreads();
-    mean = ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / df;
+    mean = ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) * (1.0f / df);
   }
   float ss = 0.f;
 #pragma unroll
@@ -1656,7 +1676,7 @@ __global__ __launch_bounds__(kWgThreads) void k_end(EndArgs a) {
   ss = wave_sum(ss);
   if (lane == 0) red[1][wave] = ss;
   __syncthreads();
-  const float inv = 1.0f / sqrtf(((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / df + a.eps);
+  const float inv = rsqrtf(((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) * (1.0f / df) + a.eps);
   float4* y4 = reinterpret_cast<float4*>(y);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
