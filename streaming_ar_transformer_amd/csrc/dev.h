@@ -182,7 +182,9 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// g / (1 + e^-g) with the reciprocal instruction (within 1 ulp) in place of a correctly rounded
+// division; e^-g overflowing to infinity gives -0 for very negative g, as the division does.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + expf(-g)); }
 __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
 }
