@@ -161,6 +161,39 @@ __device__ __forceinline__ void conv_stage(uint32_t n, Load load, Store store) {
   }
 }
 
+// A block of `rows` rows of rw floats (rw a multiple of 4): row r from global src + r * gs (16-byte
+// aligned) into LDS dst + r * ds (ds a multiple of 4), rows at or past `valid` (1 <= valid) filled
+// with zeros.
+// One 16-byte load per four floats, a batch of four per thread issued before any is stored: a
+// quarter of the load instructions of the element-wise staging, which is what a weight tile's
+// staging time tracked.
+__device__ __forceinline__ void conv_stage_rows4(float* dst, uint32_t ds, const float* src, size_t gs,
+                                                 uint32_t rows, uint32_t valid, uint32_t rw) {
+  constexpr int B = 4;
+  const uint32_t q = rw >> 2, n = rows * q;
+  const FastDiv dq(q);
+  for (uint32_t e0 = threadIdx.x; e0 < n; e0 += B * kConvTileThreads) {
+    float4 v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      uint32_t c;
+      const uint32_t r = dq.div(min(e0 + u * kConvTileThreads, n - 1), c);
+      // rows past `valid` read the last valid row (in bounds) and store zeros
+      v[u] = *reinterpret_cast<const float4*>(src + min(r, valid - 1) * gs + 4 * c);
+      if (r >= valid) v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const uint32_t e = e0 + u * kConvTileThreads;
+      if (e < n) {
+        uint32_t c;
+        const uint32_t r = dq.div(e, c);
+        *reinterpret_cast<float4*>(dst + r * ds + 4 * c) = v[u];
+      }
+    }
+  }
+}
+
 // With gridDim.z > 1 the input channels are split: workgroup z sums channels [z * ics, (z+1) * ics)
 // without the bias into part[z], and k_sconv_sum adds the splits in order.
 // KT: the kernel size when it is one of the unrolled ones (1, 3, 7), else 0 (a.k at run time).
@@ -231,20 +264,29 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, u
             X[(e / n_pre) * xw + e % n_pre] = a.pre_elu ? elu_f(v) : v;
           });
     }
-    // W[o][i][k] for output channel oc0 + o (zero past c_out)
-    const FastDiv dnk(nb * a.k);
-    conv_stage(
-        oc_t * nb * a.k,
-        [&](uint32_t e) {
-          uint32_t r;
-          const uint32_t o = dnk.div(e, r);
-          return a.w[(static_cast<size_t>(min(oc0 + o, a.c_out - 1)) * a.c_in + ic0) * a.k + r];
-        },
-        [&](uint32_t e, float v) {
-          uint32_t r;
-          const uint32_t o = dnk.div(e, r);
-          W[o * icb * a.k + r] = oc0 + o < a.c_out ? v : 0.f;
-        });
+    // W[o][i][k] for output channel oc0 + o (zero past c_out): row o of the tile is nb * k
+    // consecutive floats of the weights
+    if (((nb * a.k) & 3u) == 0 && ((a.c_in * a.k) & 3u) == 0 && ((ic0 * a.k) & 3u) == 0 &&
+        (reinterpret_cast<uintptr_t>(a.w) & 15u) == 0) {
+      const uint32_t valid = a.c_out > oc0 ? min(oc_t, a.c_out - oc0) : 0u;
+      conv_stage_rows4(W, icb * a.k,
+                       a.w + (static_cast<size_t>(min(oc0, a.c_out - 1)) * a.c_in + ic0) * a.k,
+                       static_cast<size_t>(a.c_in) * a.k, valid > 0 ? oc_t : 0u, valid, nb * a.k);
+    } else {
+      const FastDiv dnk(nb * a.k);
+      conv_stage(
+          oc_t * nb * a.k,
+          [&](uint32_t e) {
+            uint32_t r;
+            const uint32_t o = dnk.div(e, r);
+            return a.w[(static_cast<size_t>(min(oc0 + o, a.c_out - 1)) * a.c_in + ic0) * a.k + r];
+          },
+          [&](uint32_t e, float v) {
+            uint32_t r;
+            const uint32_t o = dnk.div(e, r);
+            W[o * icb * a.k + r] = oc0 + o < a.c_out ? v : 0.f;
+          });
+    }
     __syncthreads();
     if (live) {
       const float* wr = W + ocl * icb * a.k;
@@ -343,19 +385,26 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconvtr_tiled(SConvTrArgs 
           const uint32_t c = dxw.div(e, j);
           X[c * xcap + j] = a.pre_elu ? elu_f(v) : v;
         });
-    conv_stage(
-        nb * oc_t * a.k,
-        [&](uint32_t e) {
-          uint32_t r, k;
-          const uint32_t c = dok.div(e, r), o = dk.div(r, k);
-          return a.w[(static_cast<size_t>(ic0 + c) * a.c_out + min(oc0 + o, a.c_out - 1)) * a.k + k];
-        },
-        [&](uint32_t e, float v) {
-          uint32_t r, k;
-          dok.div(e, r);
-          const uint32_t o = dk.div(r, k);
-          W[e] = oc0 + o < a.c_out ? v : 0.f;
-        });
+    if (oc0 + oc_t <= a.c_out && ((oc_t * a.k) & 3u) == 0 && ((a.c_out * a.k) & 3u) == 0 &&
+        (reinterpret_cast<uintptr_t>(a.w) & 15u) == 0) {
+      // W[c][o][k]: row c of the tile is the oc_t * k consecutive floats of input channel ic0 + c
+      conv_stage_rows4(W, oc_t * a.k, a.w + (static_cast<size_t>(ic0) * a.c_out + oc0) * a.k,
+                       static_cast<size_t>(a.c_out) * a.k, nb, nb, oc_t * a.k);
+    } else {
+      conv_stage(
+          nb * oc_t * a.k,
+          [&](uint32_t e) {
+            uint32_t r, k;
+            const uint32_t c = dok.div(e, r), o = dk.div(r, k);
+            return a.w[(static_cast<size_t>(ic0 + c) * a.c_out + min(oc0 + o, a.c_out - 1)) * a.k + k];
+          },
+          [&](uint32_t e, float v) {
+            uint32_t r, k;
+            dok.div(e, r);
+            const uint32_t o = dk.div(r, k);
+            W[e] = oc0 + o < a.c_out ? v : 0.f;
+          });
+    }
     __syncthreads();
     if (live) {
       for (uint32_t k = i % a.stride; k < a.k && k <= i; k += a.stride) {
