@@ -211,6 +211,9 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, u
   const uint32_t xw = t_t * a.stride + a.pad;  // padded-stream columns the tile reads
   float* X = lds;
   float* W = lds + icb * xw;
+  // W rows (one per output channel) padded by 4 floats: the channel groups of a wave (64 / t_t of
+  // them, each reading one row in lockstep) then fall in different LDS banks
+  const uint32_t wst = icb * a.k + 4;
   const uint32_t tid = threadIdx.x;
   const uint32_t ocl = tid / t_t, otl = tid % t_t;
   const uint32_t oc = oc0 + ocl, ot = col0 + otl;
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, u
     if (((nb * a.k) & 3u) == 0 && ((a.c_in * a.k) & 3u) == 0 && ((ic0 * a.k) & 3u) == 0 &&
         (reinterpret_cast<uintptr_t>(a.w) & 15u) == 0) {
       const uint32_t valid = a.c_out > oc0 ? min(oc_t, a.c_out - oc0) : 0u;
-      conv_stage_rows4(W, icb * a.k,
+      conv_stage_rows4(W, wst,
                        a.w + (static_cast<size_t>(min(oc0, a.c_out - 1)) * a.c_in + ic0) * a.k,
                        static_cast<size_t>(a.c_in) * a.k, valid > 0 ? oc_t : 0u, valid, nb * a.k);
     } else {
@@ -284,12 +287,12 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, u
           [&](uint32_t e, float v) {
             uint32_t r;
             const uint32_t o = dnk.div(e, r);
-            W[o * icb * a.k + r] = oc0 + o < a.c_out ? v : 0.f;
+            W[o * wst + r] = oc0 + o < a.c_out ? v : 0.f;
           });
     }
     __syncthreads();
     if (live) {
-      const float* wr = W + ocl * icb * a.k;
+      const float* wr = W + ocl * wst;
       if constexpr (KT > 0) {
 #pragma unroll 4
         for (uint32_t i = 0; i < nb; ++i) {
@@ -479,7 +482,7 @@ hipError_t launch_sconv(const SConvArgs& a, hipStream_t s) {
     uint32_t oc_t, t_t;
     conv_tile(t_out, oc_t, t_t);
     const uint32_t xw = t_t * a.stride + a.pad;
-    const size_t lds = (static_cast<size_t>(kConvIcb) * xw + static_cast<size_t>(oc_t) * kConvIcb * a.k) * sizeof(float);
+    const size_t lds = (static_cast<size_t>(kConvIcb) * xw + static_cast<size_t>(oc_t) * (kConvIcb * a.k + 4)) * sizeof(float);
     if (lds > 64 * 1024) return hipErrorInvalidValue;
     const dim3 g((t_out + t_t - 1) / t_t, (a.c_out + oc_t - 1) / oc_t);
     uint32_t ics = a.c_in;
