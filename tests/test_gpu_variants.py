@@ -57,3 +57,40 @@ def test_flowlm_variant_steps_and_eos_logit(sd):
     dec.close()
     log(f"{cfg.name}: {cfg.ring} steps, worst cos {worst[0]:.9f} max|d| {worst[1]:.3e}, "
         f"EOS logit max|d| {worst_logit:.2e}")
+
+
+def test_flowlm_prefill_blocks_equal_single_steps(sd):
+    # [pocket] PocketBackboneGpu's doc: the prompt may be fed in chunks or one position at a time
+    # with the same hidden states.  Blocks of 8, 5, 8, 3 and 8 rows through sdec_prefill (the
+    # k = 1024 eight-row GEMVs with LayerNorm prologues), then single steps, against the oracle
+    # stepping one position at a time; up to the ring's end, where the unbounded stack refuses.
+    cfg = wl.CONFIGS[6]
+    layers, final = weights(cfg)
+    dl, df = device_weights(cfg)
+    dec = sd.Decoder(cfg, dl, df, max_prefill=8)
+    orc = oracle.OracleDecoder(cfg, layers, final)
+    xs = wl.make_inputs(cfg, cfg.ring)
+    p = 0
+    worst = (1.0, 0.0)
+    for t in [8, 5, 8, 3, 8] * 12 + [8] * 4:
+        xb = torch.from_numpy(np.ascontiguousarray(xs[p:p + t, 0])).cuda()
+        dec.prefill(xb, p, first=(p == 0))
+        got = xb.cpu().numpy()
+        for r in range(t):
+            want = orc.step(xs[p + r], p + r, first=(p + r == 0))
+            cos, mx = assert_close_rows(got[r:r + 1], want, f"{cfg.name} prefill pos {p + r}")
+            worst = (min(worst[0], cos), max(worst[1], mx))
+        p += t
+    x = torch.empty((1, cfg.d_model), device="cuda")
+    for q in range(p, p + 4):
+        x.copy_(torch.from_numpy(xs[q]))
+        dec.step(x, q)
+        assert_close_rows(x.cpu().numpy(), orc.step(xs[q], q), f"{cfg.name} step pos {q}")
+    p += 4
+    xb = torch.zeros((8, cfg.d_model), device="cuda")
+    dec.set_next_position(cfg.ring - 4)
+    with pytest.raises(sd.SdecError) as e:  # a block running past the unbounded ring
+        dec.prefill(xb, cfg.ring - 4)
+    assert e.value.code == sd.E_CAPACITY
+    dec.close()
+    log(f"{cfg.name}: {p} positions in blocks and steps, worst cos {worst[0]:.9f} max|d| {worst[1]:.3e}")
