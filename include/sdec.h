@@ -71,8 +71,10 @@ typedef struct sdec_config {
                            (the talker's cache and the FlowLM ring); requires window == ring */
   uint32_t flags;       /* SDEC_FLAG_* */
   uint32_t max_prefill; /* positions one sdec_prefill call may carry: 0 or 1 = none beyond a
-                           single step, at most 8; above 1 the stack must have m == 1
-                           ([talker] TalkerGpu::load: max_m bounds the prefill block width) */
+                           single step, at most 16; above 1 the stack must have m == 1, and
+                           max_prefill (rounded up to a power of two) * d_model floats must fit
+                           64 KiB ([talker] TalkerGpu::load: max_m bounds the prefill block
+                           width) */
 } sdec_config;
 
 /* One layer's parameters: device pointers, float32, borrowed (the caller keeps them alive and

@@ -8,6 +8,9 @@ namespace sdec {
 
 constexpr uint32_t kInvalidPos = 0xFFFFFFFFu;
 constexpr int kMaxM = 8;
+// Rows of one prefill block (a single stream's consecutive positions); blocks above kMaxM rows
+// take the 16-row GEMV shapes.
+constexpr int kMaxPrefill = 16;
 constexpr int kWgThreads = 256;  // four wave64s
 
 // Per-step device state written by the step-begin kernel and read by the layer kernels, so a

@@ -1797,6 +1797,17 @@ GemvKernel gemv_ksm_kind(const GemvLaunch& l) {
 }
 template <int M>
 GemvKernel gemv_ksm(const GemvLaunch& l) {
+  if constexpr (M == 16) {
+    // sixteen rows (prefill blocks past eight): one float4 per lane and row, k = 256 * waves
+    if (l.ks != 1) return {nullptr, 0};
+    if (l.waves_per_wg == 2 && l.rows_per_wave == 4) return gemv_ksm_kind<M, 2, 1, 4>(l);
+    if (l.waves_per_wg == 2 && l.rows_per_wave == 2) return gemv_ksm_kind<M, 2, 1, 2>(l);
+    if (l.waves_per_wg == 4 && l.rows_per_wave == 4) return gemv_ksm_kind<M, 4, 1, 4>(l);
+    if (l.waves_per_wg == 4 && l.rows_per_wave == 2) return gemv_ksm_kind<M, 4, 1, 2>(l);
+    if (l.waves_per_wg == 8 && l.rows_per_wave == 4) return gemv_ksm_kind<M, 8, 1, 4>(l);
+    if (l.waves_per_wg == 8 && l.rows_per_wave == 2) return gemv_ksm_kind<M, 8, 1, 2>(l);
+    return {nullptr, 0};
+  }
   if (l.waves_per_wg == 4 && l.ks == 2 && l.rows_per_wave == 4) return gemv_ksm_kind<M, 4, 2, 4>(l);
   if (l.waves_per_wg == 8 && l.ks == 3 && l.rows_per_wave == 2) return gemv_ksm_kind<M, 8, 3, 2>(l);
   // k = 512 and 1024 (the codec and FlowLM widths): one float4 per lane and row in each slice
@@ -1943,7 +1954,7 @@ hipError_t launch_attention_hd(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 // Rows m are processed as M = next power of two (unused rows read zeros, write nothing).
-static int round_m(uint32_t m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8; }
+static int round_m(uint32_t m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16; }
 
 static int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
@@ -1955,7 +1966,8 @@ static GemvKernel gemv_pick(const GemvLaunch& l, uint32_t k, uint32_t m) {
     case 1: return gemv_pick_m<1>(l, k);
     case 2: return gemv_pick_m<2>(l, k);
     case 4: return gemv_pick_m<4>(l, k);
-    default: return gemv_pick_m<8>(l, k);
+    case 8: return gemv_pick_m<8>(l, k);
+    default: return gemv_pick_m<16>(l, k);
   }
 }
 
@@ -1994,14 +2006,17 @@ GemvLaunch plan_gemv(int prologue, int epilogue, uint32_t n_rows, uint32_t k, ui
     if (l.grid < 1) l.grid = 1;
     return l;
   }
-  const bool narrow_k = (k == 512 || k == 1024) && env_int("SDEC_KSM_NARROW", 1) != 0;
-  if (M >= 2 && (k == 2048 || k == 6144 || narrow_k) && prologue != PRO_ATTN &&
+  // one float4 per lane and row in each slice: k = 512 and 1024 at any row count, and k = 2048 at
+  // sixteen rows (eight waves), where two float4 per row would not fit the registers
+  const bool narrow_k = ((k == 512 || k == 1024) && env_int("SDEC_KSM_NARROW", 1) != 0) ||
+                        (M == 16 && k == 2048);
+  if (M >= 2 && (((k == 2048 || k == 6144) && M < 16) || narrow_k) && prologue != PRO_ATTN &&
       env_int("SDEC_GEMV_SPLITK", 1) != 0) {
     // the NW waves of a workgroup take the NW slices of k; all M input rows of a slice in registers
-    l.ks = k == 2048 ? 2 : k == 6144 ? 3 : 1;
+    l.ks = narrow_k ? 1 : k == 2048 ? 2 : 3;
     l.kb = 0;
-    l.waves_per_wg = k == 2048 ? 4 : k == 6144 ? 8 : static_cast<int>(k / 256);
-    l.rows_per_wave = k == 2048 ? 4 : k == 6144 ? 2 : 4;
+    l.waves_per_wg = narrow_k ? static_cast<int>(k / 256) : k == 2048 ? 4 : 8;
+    l.rows_per_wave = narrow_k ? 4 : k == 2048 ? 4 : 2;
     // narrow rows: 4-row tiles while they give every CU a workgroup, else 2-row tiles
     if (narrow_k && n_rows / 4 < static_cast<uint32_t>(cus)) l.rows_per_wave = 2;
     if (M == 8) {

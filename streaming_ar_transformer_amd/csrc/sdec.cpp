@@ -149,8 +149,8 @@ int validate_config(const sdec_config* c, uint32_t ring) {
   if (group != 1 && group != 2 && group != 4)
     return fail(SDEC_E_ARG, "GQA group %u unsupported (1, 2 or 4)", group);
   if (c->m < 1 || c->m > kMaxM) return fail(SDEC_E_ARG, "m must be in [1, %d]", kMaxM);
-  if (c->max_prefill > static_cast<uint32_t>(kMaxM))
-    return fail(SDEC_E_ARG, "max_prefill must be in [0, %d]", kMaxM);
+  if (c->max_prefill > static_cast<uint32_t>(kMaxPrefill))
+    return fail(SDEC_E_ARG, "max_prefill must be in [0, %d]", kMaxPrefill);
   if (c->max_prefill > 1 && c->m != 1)
     return fail(SDEC_E_ARG, "a stack with max_prefill > 1 must have one stream (m == 1)");
   if (c->norm > SDEC_NORM_LAYER) return fail(SDEC_E_ARG, "bad norm kind");
@@ -163,7 +163,7 @@ int validate_config(const sdec_config* c, uint32_t ring) {
   if (c->unbounded && c->window != ring)
     return fail(SDEC_E_ARG, "an unbounded stack needs window == ring_slots");
   const uint32_t rows = c->m > c->max_prefill ? c->m : c->max_prefill;
-  const uint32_t mp = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : 8;
+  const uint32_t mp = rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : 16;
   if (static_cast<uint64_t>(mp) * c->d_model * sizeof(float) > 65536)
     return fail(SDEC_E_ARG, "%u rows of d_model=%u exceed the 64 KiB staging tile", rows,
                 c->d_model);

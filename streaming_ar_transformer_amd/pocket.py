@@ -6,7 +6,7 @@ decode graph; ``PocketCodecGpu::new`` and ``decode_frame``):
 
   1x1 conv (``sdec_conv_step``) -> channel-wise transposed conv -> ``sdec_transpose`` to
   time-major rows -> the codec transformer over the frame's ``up_stride`` positions
-  (``sdec_prefill``, blocks of at most 8 rows) -> ``sdec_transpose`` back -> SEANet.
+  (``sdec_prefill``, one block of up to 16 rows) -> ``sdec_transpose`` back -> SEANet.
 
 The transformer's ring holds ``context + up_stride`` slots so that the frame's pushes never evict
 a position its earlier rows still attend ([pocket] ``PocketCodecGpu::new``); its position
@@ -20,7 +20,7 @@ from . import sdec
 from .seanet import SEANetDecoder
 from .workloads import PocketFrameConfig
 
-MAX_BLOCK = 8  # rows per sdec_prefill call (the library's max_prefill bound)
+MAX_BLOCK = 16  # rows per sdec_prefill call (the library's max_prefill bound)
 
 
 class PocketCodecFrame:

@@ -87,7 +87,7 @@ def _create(c, layers, ring, final=None):
     ("window", 0, "window"),
     ("norm", 7, "norm"),
     ("n_layers", 0, "n_layers"),
-    ("max_prefill", 9, "max_prefill"),
+    ("max_prefill", 17, "max_prefill"),
 ])
 def test_create_rejects_bad_config(field, value, msg):
     cfg = wl.CONFIGS[1]
@@ -116,6 +116,14 @@ def test_create_rejects_unbounded_window_and_bad_weights():
     rc, err = _create(c, (sdec.LayerWeights * 1)(_fake_layer(cfg)), 2048,
                       final=sdec.FinalWeights(0, 0))
     assert rc == sdec.E_ARG and "final" in err
+
+
+def test_prefill_block_width_fits_the_staging_tile():
+    # 16 rows of the 2048-wide talker would need 128 KiB of row staging; the codec's 512 fit
+    cfg = wl.CONFIGS[4].replace(n_layers=1)
+    c = sdec.make_config(cfg, max_prefill=16)
+    rc, err = _create(c, (sdec.LayerWeights * 1)(_fake_layer(cfg)), 2048)
+    assert rc == sdec.E_ARG and "staging" in err
 
 
 def test_prefill_needs_one_stream():

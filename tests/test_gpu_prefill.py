@@ -200,3 +200,13 @@ def test_codec_prefill_end_in_down_equals_end_launch(sd, monkeypatch):
     sep.close()
     fused.close()
     log(f"{cfg.name}: {p} positions in blocks, fused and separate end bit-identical")
+
+
+def test_codec_prefill_blocks_of_sixteen(sd):
+    # Blocks of 9..16 rows take the sixteen-row GEMV shapes (k = 512 and 2048, one float4 per lane
+    # and row); ring = window + 15 so every block stays legal after the ring wraps (265, 530).
+    cfg = wl.CONFIGS[2]
+    blocks = [16, 9, 16, 12, 16, 15, 1, 16, 13, 10] * 6
+    while sum(blocks) > 620:
+        blocks.pop()
+    run_blocks(sd, cfg, blocks, decode_after=4, ring=cfg.window + 15, check_kv=True)
