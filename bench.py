@@ -526,7 +526,7 @@ def main():
         sdec_.close()
 
     # Pocket-style codec frame: latent -> 1x1 conv -> channel-wise convtr -> transpose -> the
-    # 2-layer transformer over 16 positions (two prefill blocks of 8) -> transpose -> SEANet
+    # 2-layer transformer over 16 positions (one prefill block of 16) -> transpose -> SEANet
     pocket = None
     if not args.no_pocket and args.config == 4:
         from streaming_ar_transformer_amd.pocket import PocketCodecFrame

@@ -3,7 +3,7 @@ decode graph; PocketCodecGpu::new / decode_frame / reset).
 
 Twenty latents go through ``PocketCodecFrame.decode_frame`` one at a time: 1x1 conv, channel-wise
 transposed conv k32/s16, transpose, the 2-layer d512 transformer over 16 positions per frame
-(two prefill blocks of 8; ring 266, window 250, so the run passes the ring's wrap at position
+(one prefill block of 16; ring 266, window 250, so the run passes the ring's wrap at position
 266), transpose, SEANet.  Every frame's transformer rows and samples must meet the per-row bar
 (cosine >= 0.99999, max|delta| <= 1e-3); a restart with ``first`` must reproduce the first
 frames.
