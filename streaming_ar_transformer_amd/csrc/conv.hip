@@ -144,6 +144,20 @@ __device__ __forceinline__ bool conv_split_arrive(uint32_t* counter, uint32_t sp
   return last != 0;
 }
 
+// acc plus the splits' partial sums of one output, added in split order: every partial is
+// requested before the first is added (a loop of load, wait, add paid one device-coherent round
+// trip per split; the indices are clamped, so the loads need no branch).
+__device__ __forceinline__ float conv_split_sum(float acc, const float* p, size_t plane,
+                                                uint32_t splits) {
+  float v[kConvMaxSplits];
+#pragma unroll
+  for (uint32_t z = 0; z < kConvMaxSplits; ++z) v[z] = dev::ld_dev(p + min(z, splits - 1) * plane);
+#pragma unroll
+  for (uint32_t z = 0; z < kConvMaxSplits; ++z)
+    if (z < splits) acc += v[z];
+  return acc;
+}
+
 // Fills n LDS elements, kConvStageBatch per thread per batch: the batch's global loads are all
 // issued before any result is used (indices clamped into [0, n), so no branch guards a load), so
 // a thread waits about one memory round trip per batch instead of one per element.
@@ -320,7 +334,7 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconv_tiled(SConvArgs a, u
       return;
     if (!live) return;
     acc = a.b[oc];  // the bias, then the splits in order
-    for (uint32_t z = 0; z < gridDim.z; ++z) acc += dev::ld_dev(a.part + z * plane + e);
+    acc = conv_split_sum(acc, a.part + e, plane, gridDim.z);
   }
   if (live) {
     float* y = a.y + static_cast<size_t>(oc) * t_out + ot;
@@ -432,7 +446,7 @@ __global__ __launch_bounds__(kConvTileThreads) void k_sconvtr_tiled(SConvTrArgs 
       return;
     if (!live) return;
     acc = a.b[oc];  // the bias, then the splits in order
-    for (uint32_t z = 0; z < gridDim.z; ++z) acc += dev::ld_dev(a.part + z * plane + e);
+    acc = conv_split_sum(acc, a.part + e, plane, gridDim.z);
   }
   if (!live) return;
   sconvtr_emit(a, oc, i, acc);
