@@ -103,6 +103,8 @@ __global__ __launch_bounds__(kRvqLanes) void k_rvq_level(RvqLevelArgs a) {
   float d = 0.f;
   {
 #pragma clang fp contract(off)
+    // 16 codebook words requested per round trip (the sum itself stays in dimension order)
+#pragma unroll 16
     for (uint32_t c = 0; c < a.vq; ++c) {
       const float df = col[static_cast<size_t>(c) * a.bins] - r[c];
       const float sq = df * df;  // rounded on its own: no fused multiply-add
