@@ -61,18 +61,19 @@ def test_flowlm_variant_steps_and_eos_logit(sd):
 
 def test_flowlm_prefill_blocks_equal_single_steps(sd):
     # [pocket] PocketBackboneGpu's doc: the prompt may be fed in chunks or one position at a time
-    # with the same hidden states.  Blocks of 8, 5, 8, 3 and 8 rows through sdec_prefill (the
-    # k = 1024 eight-row GEMVs with LayerNorm prologues), then single steps, against the oracle
-    # stepping one position at a time; up to the ring's end, where the unbounded stack refuses.
+    # with the same hidden states.  Blocks of 8, 5, 16, 3 and 12 rows through sdec_prefill (the
+    # k = 1024 eight- and sixteen-row GEMVs with LayerNorm prologues, the sixteen-row generic GEMV
+    # for the k = 4096 down projection), then single steps, against the oracle stepping one
+    # position at a time; up to the ring's end, where the unbounded stack refuses.
     cfg = wl.CONFIGS[6]
     layers, final = weights(cfg)
     dl, df = device_weights(cfg)
-    dec = sd.Decoder(cfg, dl, df, max_prefill=8)
+    dec = sd.Decoder(cfg, dl, df, max_prefill=16)
     orc = oracle.OracleDecoder(cfg, layers, final)
     xs = wl.make_inputs(cfg, cfg.ring)
     p = 0
     worst = (1.0, 0.0)
-    for t in [8, 5, 8, 3, 8] * 12 + [8] * 4:
+    for t in [8, 5, 16, 3, 12] * 9 + [8] * 4:
         xb = torch.from_numpy(np.ascontiguousarray(xs[p:p + t, 0])).cuda()
         dec.prefill(xb, p, first=(p == 0))
         got = xb.cpu().numpy()
