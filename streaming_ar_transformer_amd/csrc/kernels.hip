@@ -1078,7 +1078,7 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_ksm(GemvArgs a) {
 #pragma unroll
       for (int q = 0; q < NW; ++q) tot += stat[1][m][q];
       // one reciprocal square root instruction (within 1 ulp of 1 / sqrt) and a product by
-      // 1 / k: 8 rows of correctly rounded divisions and square roots measured 1.5 us per launch
+      // 1 / k: 8 rows of correctly rounded divisions and square roots cost about 1.1 us per launch
       invs[m] = rsqrtf(tot * rk + a.eps);
     }
 #pragma unroll
