@@ -166,7 +166,9 @@ const char* sdec_last_error(void);
  * [n_kv_heads][head_dim] float32 (keys already roped), *pos_ring is [ring_slots] uint32 and is
  * shared by every layer of the stream.  Writing them imports a cache ([pocket] load_voice: the
  * [positions][heads][head_dim] cache layout is the ring's slot-major layout); follow with
- * sdec_set_next_position.  Any output pointer may be NULL. */
+ * sdec_set_next_position.  A position may be stamped in at most one slot (the library's own
+ * pushes use slot pos mod ring_slots): the step sizes its attention work from the number of
+ * distinct positions the window can hold.  Any output pointer may be NULL. */
 int sdec_kv_view(sdec_handle* h, uint32_t stream_idx, uint32_t layer, float** k, float** v,
                  uint32_t** pos_ring);
 
