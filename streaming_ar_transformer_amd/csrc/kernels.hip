@@ -1843,21 +1843,12 @@ GemvKernel gemv_stream(const GemvLaunch& l) {
   return {nullptr, 0};
 }
 
-// The split-k kernels: k = 1024*ks, rows_per_wave = rows per workgroup tile.
-template <int KW, int RB>
-GemvKernel gemv_ks_kind(const GemvLaunch& l) {
-#define SDEC_KS(P, E) \
-  if (l.prologue == P && l.epilogue == E) return {reinterpret_cast<const void*>(&k_gemv_ks<KW, RB, P, E>), 0};
-  SDEC_KS(PRO_NONE, EPI_RESIDUAL)
-  SDEC_KS(PRO_RMS, EPI_STORE)
-  SDEC_KS(PRO_RMS, EPI_SWIGLU)
-#undef SDEC_KS
-  return {nullptr, 0};
-}
+// The split-k kernel the planner picks: the down projection at one stream (k = 6144, four-row
+// tiles, residual epilogue).  Quarter-row split-k for the k = 2048 projections measured slower
+// than the row stream and is not instantiated.
 GemvKernel gemv_ks(const GemvLaunch& l) {
-  if (l.ks == 6 && l.rows_per_wave == 4) return gemv_ks_kind<6, 4>(l);
-  if (l.ks == 2 && l.rows_per_wave == 4) return gemv_ks_kind<2, 4>(l);
-  if (l.ks == 2 && l.rows_per_wave == 8) return gemv_ks_kind<2, 8>(l);
+  if (l.ks == 6 && l.rows_per_wave == 4 && l.prologue == PRO_NONE && l.epilogue == EPI_RESIDUAL)
+    return {reinterpret_cast<const void*>(&k_gemv_ks<6, 4, PRO_NONE, EPI_RESIDUAL>), 0};
   return {nullptr, 0};
 }
 
