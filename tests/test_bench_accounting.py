@@ -76,3 +76,12 @@ def test_codec_steady_state_bytes():
         want = layers * (12_595_200 + 4096 * live + 4096 + F * cfg.ring) + 2 * F * 512
         assert b == want
         assert round(b / 1e6, 2) == pytest.approx(want_mb, abs=0.01)
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU only" in (r.stdout + r.stderr)
+    assert r.stdout.strip() == ""  # no JSON line
