@@ -203,3 +203,12 @@ def test_static_scratch_attention_checks_on_the_host():
     rc = L.sdec_ring_attention_static(256, 512, 768, 1024, 1280, 8, 16, 8, 128, 100000, 100000, 5,
                                       None)
     assert rc == sdec.E_ARG and "static scratch" in L.sdec_last_error().decode()
+
+
+def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
+    # with no built library the binding refuses to run: there is no CPU path behind it
+    from streaming_ar_transformer_amd import sdec
+    monkeypatch.setattr(sdec, "_lib", None)
+    monkeypatch.setattr(sdec, "LIB_PATH", str(tmp_path / "libsdec.so"))
+    with pytest.raises(ImportError, match="is missing"):
+        sdec.lib()
