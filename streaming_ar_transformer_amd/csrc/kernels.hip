@@ -1022,7 +1022,36 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_ksm(GemvArgs a) {
   load(u0);
   __builtin_amdgcn_sched_barrier(0);
 
-  if (PRO != PRO_NONE) {  // per input row: statistics of the whole row from the NW slices
+  // RMSNorm: the products use g * x and the epilogue scales each row's sums by that row's 1/rms,
+  // so no workgroup barrier stands between the input rows' arrival and the first products (the
+  // slices' sums of squares go to LDS here and are read after the first tile's barrier)
+  constexpr bool LATE_RMS = PRO == PRO_RMS;
+  const float rk_late = 1.0f / static_cast<float>(a.k);
+  if constexpr (LATE_RMS) {
+    float st[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < KW; ++j) ss = dot4(xr[m][j], xr[m][j], ss);
+      st[m] = ss;
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) st[m] = wave_sum(st[m]);
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) stat[1][m][wave] = st[m];
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int j = 0; j < KW; ++j) {
+        float4 v = xr[m][j];
+        const float4 g = gr[j];
+        v.x *= g.x; v.y *= g.y; v.z *= g.z; v.w *= g.w;
+        xr[m][j] = v;
+      }
+  } else if (PRO != PRO_NONE) {  // per input row: statistics of the whole row from the NW slices
     // Each phase runs over all M rows before the next (the sums, then the cross-lane reductions,
     // then one guarded LDS write per row), so the M independent reduction chains interleave
     // instead of running one after another between exec-mask switches.
@@ -1129,11 +1158,19 @@ __global__ __launch_bounds__(NW * kWave) void k_gemv_ksm(GemvArgs a) {
         float v = 0.f;
 #pragma unroll
         for (int q = 0; q < NW; ++q) v += part[q][e_u * M + e_m];
+        float rs = 1.f;  // LATE_RMS: 1/rms of input row e_m
+        if constexpr (LATE_RMS) {
+          float tot = 0.f;
+#pragma unroll
+          for (int q = 0; q < NW; ++q) tot += stat[1][e_m][q];
+          rs = rsqrtf(tot * rk_late + a.eps);
+          v *= rs;
+        }
         if (EPI == EPI_SWIGLU) {
           float up = 0.f;
 #pragma unroll
           for (int q = 0; q < NW; ++q) up += part[q][(e_u + U) * M + e_m];
-          a.y[e_m * a.y_stride + u] = silu(v) * up;
+          a.y[e_m * a.y_stride + u] = silu(v) * (up * rs);
         } else if (EPI == EPI_STORE) {
           a.y[e_m * a.y_stride + u] = v;
         } else if (EPI == EPI_GELU) {
