@@ -44,7 +44,7 @@ def read_kv(sd, dec, cfg, stream, layer, ring):
     return sd.copy_from_device(k, n, np.float32, shape), sd.copy_from_device(v, n, np.float32, shape)
 
 
-def run_parity(sd, cfg, steps, check_every=1, taps=False, ring_check=True):
+def run_parity(sd, cfg, steps, check_every=1, taps=False, ring_check=True, log_every=256):
     layers, final = weights(cfg)
     xs = wl.make_inputs(cfg, steps)
     dec = make(sd, cfg, taps=taps)
@@ -60,7 +60,7 @@ def run_parity(sd, cfg, steps, check_every=1, taps=False, ring_check=True):
             continue
         got = x.cpu().numpy()
         cos, mx = assert_close_rows(got, want, f"{cfg.name} pos {p}")
-        if p % 256 == 255:
+        if p % log_every == log_every - 1:
             log(f"{cfg.name}: {p + 1} positions compared")
         worst = (min(worst[0], cos), max(worst[1], mx))
         if taps:
